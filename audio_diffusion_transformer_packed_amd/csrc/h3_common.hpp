@@ -1,0 +1,77 @@
+// Shared device helpers for the gfx950 kernels of the packed DiT hot path.
+// CDNA4: 64-lane wavefronts, bf16 MFMA 32x32x16 with fp32 accumulation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16 bytes viewed as 8 bf16 / 4 words.
+union Chunk16 {
+    uint4 u;
+    bf16x8 b;
+    uint16_t h[8];
+    uint32_t w[4];
+};
+
+union Chunk8 {
+    uint2 u;
+    bf16x4 b;
+    uint16_t h[4];
+    uint32_t w[2];
+};
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = width / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Segment of token t: largest s with cu[s] <= t (cu non-decreasing, cu[0] = 0).
+__device__ __forceinline__ int find_segment(const int32_t* __restrict__ cu, int num_seqs,
+                                            int64_t t) {
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (static_cast<int64_t>(cu[mid]) <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace h3

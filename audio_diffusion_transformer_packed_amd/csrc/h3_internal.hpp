@@ -1,0 +1,56 @@
+// Host-side launch wrappers shared between the kernel translation units and
+// the C ABI. Each returns the hipError_t of its launch; arguments are
+// validated by the caller (h3dit_api.hip) before any of these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace h3 {
+
+// Varlen bookkeeping (bookkeeping.hip)
+size_t bookkeeping_scratch_bytes(int num_seqs);
+hipError_t launch_bookkeeping(const int32_t* cu, int num_seqs, int total_tokens, int num_heads,
+                              int block_m, int32_t* seg_id, int32_t* tile_cu, int32_t* items,
+                              int64_t items_capacity, void* scratch, hipStream_t stream);
+
+// bf16 flash attention over the work list (attn_bf16.hip)
+hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            uint16_t* o, int64_t qs, int64_t ks, int64_t vs, int64_t os,
+                            const int32_t* cu, const int32_t* items, int64_t num_items,
+                            int num_seqs, int total_tokens, int num_heads, int head_dim,
+                            float softmax_scale, hipStream_t stream);
+
+// fp8 quantisation + fp8 attention (attn_fp8.hip)
+bool fp8_attention_available();
+size_t fp8_scratch_bytes(int num_seqs, int total_tokens, int num_heads, int head_dim);
+hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           uint16_t* o, int64_t qs, int64_t ks, int64_t vs, int64_t os,
+                           const int32_t* cu, const int32_t* cu_host, const int32_t* items,
+                           int64_t num_items, int num_seqs, int total_tokens, int num_heads,
+                           int head_dim, float softmax_scale, int skip, float skip_threshold,
+                           int32_t* skip_counts, void* scratch, hipStream_t stream);
+
+// Q/K RMSNorm + 3D RoPE (qk_norm_rope.hip)
+hipError_t launch_qk_norm_rope(uint16_t* q, uint16_t* k, int64_t qs, int64_t ks,
+                               const uint16_t* w_q, const uint16_t* w_k, const int32_t* grid,
+                               int total_tokens, int num_heads, int head_dim,
+                               const int32_t split[3], float theta, float eps,
+                               hipStream_t stream);
+
+// AdaLN: modulation GEMV and RMSNorm + modulate (adaln.hip)
+hipError_t launch_modulation(const uint16_t* cond, const uint16_t* w_mod, float* mod,
+                             int num_seqs, int hidden, hipStream_t stream);
+hipError_t launch_adaln(const uint16_t* x, uint16_t* h, const float* shift, const float* scale,
+                        int64_t mod_stride, const int32_t* cu, int num_seqs, int total_tokens,
+                        int hidden, float eps, hipStream_t stream);
+
+// GEMMs with epilogues (gemm.hip)
+enum GemmEpilogue { kEpiStore = 0, kEpiSwiGLU = 1, kEpiGatedResidual = 2 };
+hipError_t launch_gemm(int epilogue, const uint16_t* a, const uint16_t* w, const uint16_t* w2,
+                       uint16_t* y, int64_t m, int64_t n, int64_t k, const uint16_t* res,
+                       const float* gate, int64_t gate_stride, const int32_t* cu,
+                       int num_seqs, hipStream_t stream);
+
+}  // namespace h3

@@ -1,0 +1,323 @@
+"""Python binding of the HIP library: argument marshalling only.
+
+Each function takes torch tensors (device memory owned by PyTorch), checks
+dtypes and layouts, and calls the C ABI entry point of the same name on the
+current torch stream. Every step of the computation runs in the library's
+HIP kernels; this module computes nothing itself. Workspaces are allocated
+from torch's caching allocator when the caller does not pass one.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from ._lib import AttnOpts, DitDims, DitTaps, DitWeights, check, lib
+
+BF16 = torch.bfloat16
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _host_cu(cu_host) -> np.ndarray:
+    if isinstance(cu_host, torch.Tensor):
+        cu_host = cu_host.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _token_view(t: torch.Tensor, name: str, heads: int, head_dim: int) -> int:
+    """Token stride (elements) of a [N, H, D] view with contiguous heads."""
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != head_dim:
+        raise ValueError(f"{name} must be [N, {heads}, {head_dim}], got {tuple(t.shape)}")
+    if t.stride(2) != 1 or t.stride(1) != head_dim:
+        raise ValueError(f"{name} must have contiguous heads (strides (*, {head_dim}, 1))")
+    return t.stride(0)
+
+
+# --------------------------------------------------------------------------
+# Schedule
+# --------------------------------------------------------------------------
+
+def build_schedule_host(cu_host, num_heads: int, block_m: int = L.H3_ATTN_BLOCK_M) -> np.ndarray:
+    cu = _host_cu(cu_host)
+    count = C.c_int64(0)
+    check(lib().h3_build_schedule_host(cu.ctypes.data_as(C.c_void_p), cu.size - 1, num_heads,
+                                       block_m, None, 0, C.byref(count)))
+    items = np.zeros((count.value, 4), dtype=np.int32)
+    check(lib().h3_build_schedule_host(cu.ctypes.data_as(C.c_void_p), cu.size - 1, num_heads,
+                                       block_m, items.ctypes.data_as(C.c_void_p), count.value,
+                                       C.byref(count)))
+    return items
+
+
+def varlen_bookkeeping(cu_seqlens: torch.Tensor, cu_host, num_heads: int,
+                       block_m: int = L.H3_ATTN_BLOCK_M) -> Tuple[torch.Tensor, ...]:
+    """Device seg_id [N], tile_cu [B+1] and work list [items, 4]."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    cu = _host_cu(cu_host)
+    b, n = cu.size - 1, int(cu[-1])
+    dev = cu_seqlens.device
+    count = C.c_int64(0)
+    check(lib().h3_build_schedule_host(cu.ctypes.data_as(C.c_void_p), b, num_heads, block_m,
+                                       None, 0, C.byref(count)))
+    seg_id = torch.empty(n, dtype=torch.int32, device=dev)
+    tile_cu = torch.empty(b + 1, dtype=torch.int32, device=dev)
+    items = torch.empty((max(count.value, 1), 4), dtype=torch.int32, device=dev)
+    ws = _workspace(lib().h3_varlen_bookkeeping_workspace_size(b), dev, None)
+    check(lib().h3_varlen_bookkeeping(_ptr(cu_seqlens), cu.ctypes.data_as(C.c_void_p), b, n,
+                                      num_heads, block_m, _ptr(seg_id), _ptr(tile_cu),
+                                      _ptr(items), count.value, _ptr(ws), ws.numel(),
+                                      _stream(dev)))
+    return seg_id, tile_cu, items[:count.value]
+
+
+def attn_num_items(cu_host, num_heads: int) -> int:
+    cu = _host_cu(cu_host)
+    count = C.c_int64(0)
+    check(lib().h3_attn_varlen_num_items(cu.ctypes.data_as(C.c_void_p), cu.size - 1, num_heads,
+                                         C.byref(count)))
+    return count.value
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+
+def attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                cu_host, out: Optional[torch.Tensor] = None, precision: str = "bf16",
+                skip_softmax: bool = False, skip_threshold: float = 8.0,
+                softmax_scale: float = 0.0, skip_counts: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Varlen attention over packed segments; q, k, v, out are [N, H, D] bf16."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, BF16, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    n, heads, d = q.shape
+    if out is None:
+        out = torch.empty((n, heads, d), dtype=BF16, device=dev)
+    _need(out, "out", BF16, dev)
+    strides = [_token_view(t, nm, heads, d) for nm, t in (("q", q), ("k", k), ("v", v), ("out", out))]
+    cu = _host_cu(cu_host)
+    prec = {"bf16": L.H3_ATTN_BF16, "fp8": L.H3_ATTN_FP8_E4M3}[precision]
+    if skip_counts is not None:
+        _need(skip_counts, "skip_counts", torch.int32, dev)
+    opts = AttnOpts(prec, int(skip_softmax), float(skip_threshold), float(softmax_scale),
+                    None if skip_counts is None else skip_counts.data_ptr())
+    nbytes = lib().h3_attn_varlen_workspace_size(cu.size - 1, n, heads, d, C.byref(opts))
+    ws = _workspace(nbytes, dev, workspace)
+    check(lib().h3_attn_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), *strides, _ptr(cu_seqlens),
+                               cu.ctypes.data_as(C.c_void_p), cu.size - 1, n, heads, d,
+                               C.byref(opts), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Per-block fused operators
+# --------------------------------------------------------------------------
+
+def qk_rmsnorm_rope(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                    rope_grid: torch.Tensor, rope_split: Sequence[int], theta: float = 10000.0,
+                    eps: float = 1e-6) -> None:
+    """In place on q and k ([N, H, D] bf16 views with contiguous heads)."""
+    dev = q.device
+    _need(q, "q", BF16, dev)
+    _need(k, "k", BF16, dev)
+    _need(w_q, "w_q", BF16, dev)
+    _need(w_k, "w_k", BF16, dev)
+    _need(rope_grid, "rope_grid", torch.int32, dev)
+    n, heads, d = q.shape
+    qs = _token_view(q, "q", heads, d)
+    ks = _token_view(k, "k", heads, d)
+    if not rope_grid.is_contiguous() or tuple(rope_grid.shape) != (n, 3):
+        raise ValueError("rope_grid must be a contiguous [N, 3] int32 tensor")
+    if w_q.numel() != d or w_k.numel() != d:
+        raise ValueError("gains must have head_dim elements")
+    split = (C.c_int32 * 3)(*[int(s) for s in rope_split])
+    check(lib().h3_qk_rmsnorm_rope(_ptr(q), _ptr(k), qs, ks, _ptr(w_q.contiguous()),
+                                   _ptr(w_k.contiguous()), _ptr(rope_grid), n, heads, d, split,
+                                   float(theta), float(eps), _stream(dev)))
+
+
+def modulation(cond: torch.Tensor, w_mod: torch.Tensor) -> torch.Tensor:
+    """fp32 [B, 6C] = cond [B, C] . W_mod^T."""
+    dev = cond.device
+    _need(cond, "cond", BF16, dev)
+    _need(w_mod, "w_mod", BF16, dev)
+    b, c = cond.shape
+    if tuple(w_mod.shape) != (6 * c, c) or not w_mod.is_contiguous() or not cond.is_contiguous():
+        raise ValueError("w_mod must be contiguous [6C, C] and cond contiguous [B, C]")
+    mod = torch.empty((b, 6 * c), dtype=torch.float32, device=dev)
+    check(lib().h3_modulation(_ptr(cond), _ptr(w_mod), _ptr(mod), b, c, _stream(dev)))
+    return mod
+
+
+def adaln_rmsnorm_modulate(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor,
+                           cu_seqlens: torch.Tensor, cu_host, eps: float = 1e-6,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """h = RMSNorm(x) * (1 + scale[seg]) + shift[seg]; shift/scale fp32 [B, C] views
+    whose rows may be strided (e.g. slices of the modulation output)."""
+    dev = x.device
+    _need(x, "x", BF16, dev)
+    _need(shift, "shift", torch.float32, dev)
+    _need(scale, "scale", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    n, c = x.shape
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if shift.stride(1) != 1 or scale.stride(1) != 1 or shift.stride(0) != scale.stride(0):
+        raise ValueError("shift/scale rows must be contiguous with one common row stride")
+    if out is None:
+        out = torch.empty_like(x)
+    cu = _host_cu(cu_host)
+    check(lib().h3_adaln_rmsnorm_modulate(_ptr(x), _ptr(out), _ptr(shift), _ptr(scale),
+                                          shift.stride(0), _ptr(cu_seqlens),
+                                          cu.ctypes.data_as(C.c_void_p), cu.size - 1, n, c,
+                                          float(eps), _stream(dev)))
+    return out
+
+
+def _gemm_args(a, ws, name="w"):
+    dev = a.device
+    _need(a, "a", BF16, dev)
+    for i, w in enumerate(ws):
+        _need(w, f"{name}{i}", BF16, dev)
+        if not w.is_contiguous():
+            raise ValueError("weights must be contiguous")
+    if not a.is_contiguous():
+        raise ValueError("a must be contiguous")
+    return dev
+
+
+def linear(a: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    dev = _gemm_args(a, [w])
+    m, k = a.shape
+    n = w.shape[0]
+    y = torch.empty((m, n), dtype=BF16, device=dev)
+    check(lib().h3_linear_bf16(_ptr(a), _ptr(w), _ptr(y), m, n, k, _stream(dev)))
+    return y
+
+
+def linear_swiglu(a: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:
+    dev = _gemm_args(a, [w_gate, w_up])
+    m, k = a.shape
+    n = w_gate.shape[0]
+    if tuple(w_up.shape) != tuple(w_gate.shape):
+        raise ValueError("w_gate and w_up must have the same shape")
+    y = torch.empty((m, n), dtype=BF16, device=dev)
+    check(lib().h3_linear_swiglu_bf16(_ptr(a), _ptr(w_gate), _ptr(w_up), _ptr(y), m, n, k,
+                                      _stream(dev)))
+    return y
+
+
+def linear_gated_residual(a: torch.Tensor, w: torch.Tensor, res: torch.Tensor,
+                          gate: torch.Tensor, cu_seqlens: torch.Tensor, cu_host,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dev = _gemm_args(a, [w])
+    _need(res, "res", BF16, dev)
+    _need(gate, "gate", torch.float32, dev)
+    m, k = a.shape
+    n = w.shape[0]
+    if gate.stride(1) != 1:
+        raise ValueError("gate rows must be contiguous")
+    y = torch.empty((m, n), dtype=BF16, device=dev) if out is None else out
+    cu = _host_cu(cu_host)
+    check(lib().h3_linear_gated_residual_bf16(_ptr(a), _ptr(w), _ptr(res.contiguous()),
+                                              _ptr(gate), gate.stride(0), _ptr(y), m, n, k,
+                                              _ptr(cu_seqlens), cu.ctypes.data_as(C.c_void_p),
+                                              cu.size - 1, _stream(dev)))
+    return y
+
+
+# --------------------------------------------------------------------------
+# The block
+# --------------------------------------------------------------------------
+
+WEIGHT_NAMES = ("w_mod", "w_qkv", "w_o", "q_norm", "k_norm", "w_gate", "w_up", "w_down")
+TAP_NAMES = ("mod", "h", "qkv", "o", "x1", "h2", "a")
+
+
+class DitBlock:
+    """One block's dims and device weights; forward() calls h3_dit_block_forward."""
+
+    def __init__(self, weights: Dict[str, torch.Tensor], heads: int, head_dim: int,
+                 ffn_dim: int, rope_split: Sequence[int], rope_theta: float = 10000.0,
+                 eps: float = 1e-6):
+        self.weights = weights
+        hidden = heads * head_dim
+        for nm in WEIGHT_NAMES:
+            _need(weights[nm], nm, BF16)
+            if not weights[nm].is_contiguous():
+                raise ValueError(f"{nm} must be contiguous")
+        self.dims = DitDims(hidden, heads, head_dim, ffn_dim, (C.c_int32 * 3)(*rope_split),
+                            float(rope_theta), float(eps))
+        self.c_weights = DitWeights(*[weights[nm].data_ptr() for nm in WEIGHT_NAMES])
+        self.hidden, self.ffn = hidden, ffn_dim
+
+    def workspace_bytes(self, num_seqs: int, total_tokens: int) -> int:
+        return lib().h3_dit_block_workspace_size(C.byref(self.dims), num_seqs, total_tokens)
+
+    def forward(self, x: torch.Tensor, cond: torch.Tensor, cu_seqlens: torch.Tensor, cu_host,
+                rope_grid: torch.Tensor, out: Optional[torch.Tensor] = None,
+                taps: Optional[Dict[str, torch.Tensor]] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        dev = x.device
+        _need(x, "x", BF16, dev)
+        _need(cond, "cond", BF16, dev)
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        _need(rope_grid, "rope_grid", torch.int32, dev)
+        if not (x.is_contiguous() and cond.is_contiguous() and rope_grid.is_contiguous()):
+            raise ValueError("x, cond and rope_grid must be contiguous")
+        cu = _host_cu(cu_host)
+        b, n = cu.size - 1, x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        ws = _workspace(self.workspace_bytes(b, n), dev, workspace)
+        c_taps = None
+        if taps is not None:
+            c_taps = DitTaps(*[None if taps.get(nm) is None else taps[nm].data_ptr()
+                               for nm in TAP_NAMES])
+        check(lib().h3_dit_block_forward(_ptr(x), _ptr(out), _ptr(cond), C.byref(self.c_weights),
+                                         C.byref(self.dims), _ptr(cu_seqlens),
+                                         cu.ctypes.data_as(C.c_void_p), b, n, _ptr(rope_grid),
+                                         None if c_taps is None else C.byref(c_taps), _ptr(ws),
+                                         ws.numel(), _stream(dev)))
+        return out
+
+    def make_taps(self, num_seqs: int, total_tokens: int, device) -> Dict[str, torch.Tensor]:
+        n, c = total_tokens, self.hidden
+        return {"mod": torch.empty((num_seqs, 6 * c), dtype=torch.float32, device=device),
+                "h": torch.empty((n, c), dtype=BF16, device=device),
+                "qkv": torch.empty((n, 3 * c), dtype=BF16, device=device),
+                "o": torch.empty((n, c), dtype=BF16, device=device),
+                "x1": torch.empty((n, c), dtype=BF16, device=device),
+                "h2": torch.empty((n, c), dtype=BF16, device=device),
+                "a": torch.empty((n, self.ffn), dtype=BF16, device=device)}

@@ -1,0 +1,277 @@
+"""Benchmark of the packed joint audio-video DiT hot path on one MI355X.
+
+One step = one full DiT block forward (h3_dit_block_forward: modulation,
+AdaLN, QKV GEMM, Q/K RMSNorm + 3D RoPE, varlen attention, out-projection with
+gated residual, AdaLN, SwiGLU GEMM, down GEMM with gated residual) over the
+57,960-token packed sequence of a 10 s clip, inputs resident in HBM.
+
+Prints ONE JSON line:
+  value       whole-block throughput, algorithmic TFLOP/s (GEMMs + attention
+              over valid tokens only, no padding) = block FLOPs / ms_per_step
+  roofline    the dominant kernel (varlen attention) against bf16 dense MFMA
+              peak, its average launch duration timed with HIP events on the
+              stream it runs on
+  stages      per-kernel timings (events) with TFLOP/s or GB/s
+  cpu_baseline the float64 oracle on the host cores, on a bounded sample
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--no-stages]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "varlen attention TFLOP/s + DiT-block ms at 58k packed tokens; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "audio_diffusion_transformer_packed_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_block_10s_58k_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attention_flops(lengths, heads, head_dim):
+    return float(sum(4.0 * L * L * heads * head_dim for L in lengths))
+
+
+def gemm_flops(n, c, ffn, b):
+    # qkv (3C), out-proj (C), gate+up (2I), down (I), modulation GEMV
+    return 2.0 * n * c * (3 * c + c + 2 * ffn) + 2.0 * n * ffn * c + 2.0 * b * c * 6 * c
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != source_hash(ATTN_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """Average duration of a callable over n launches, with HIP events on the
+    current torch stream (the stream the library enqueues on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, n):
+        t = self.torch
+        start, end = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        start.record()
+        for _ in range(n):
+            fn()
+        end.record()
+        t.cuda.synchronize()
+        return start.elapsed_time(end) / n
+
+
+def cpu_baseline(inp, wl, rows_count=16):
+    """The float64 oracle on a bounded sample of the same block: keys and values
+    of all tokens plus the full block for `rows_count` sampled query rows."""
+    import oracle
+    from oracle import dit_block_rows_ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = os.cpu_count() or 1
+    import h3synth
+    n, c, ffn, heads, d = wl.total_tokens, wl.hidden, wl.ffn, wl.heads, wl.head_dim
+    rows = h3synth.sample_rows(n, rows_count, inp.seed, include_edges=False)
+    weights = {nm: getattr(inp, nm).f32 for nm in inp.weight_names}
+    t0 = time.perf_counter()
+    dit_block_rows_ref(inp.x.f32, inp.cond.f32, weights, inp.cu_seqlens, inp.grid, heads, d,
+                       h3synth.rope_split_for(d), rows)
+    dt = time.perf_counter() - t0
+    r = rows.size
+    L = n   # one segment
+    flops = (2.0 * n * c * 2 * c                         # k, v projections, all tokens
+             + r * (2.0 * c * c + 4.0 * L * c + 2.0 * c * c + 2.0 * c * 2 * ffn + 2.0 * ffn * c)
+             + 2.0 * len(wl.requests) * c * 6 * c)
+    del oracle
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": (f"float64 numpy oracle (dit_block_rows_ref): keys/values of all {n} tokens "
+                       f"+ the whole block for {r} sampled query rows; {flops / 1e12:.3f} "
+                       f"TFLOP algorithmic in {dt:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="block_10s_58k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this hot path runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note, not built)"}))
+        sys.exit(2)
+
+    import torch
+    import h3synth
+    from audio_diffusion_transformer_packed_amd import ops
+
+    dev = torch.device("cuda:0")
+    wl = h3synth.WORKLOADS[args.workload]
+    if wl.kind != "block":
+        raise SystemExit("the bench step is a full block; pick a block workload")
+    log(f"generating {wl.name}: {wl.total_tokens} tokens")
+    inp = h3synth.workload_block_inputs(wl.name)
+    split = h3synth.rope_split_for(wl.head_dim)
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a.bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    weights = {nm: dev_bf16(getattr(inp, nm)) for nm in ops.WEIGHT_NAMES}
+    blk = ops.DitBlock(weights, wl.heads, wl.head_dim, wl.ffn, split)
+    cu = inp.cu_seqlens
+    b, n, c = len(cu) - 1, wl.total_tokens, wl.hidden
+    x = dev_bf16(inp.x)
+    cond = dev_bf16(inp.cond)
+    cu_d = torch.from_numpy(cu).to(dev)
+    grid_d = torch.from_numpy(inp.grid).to(dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(blk.workspace_bytes(b, n), dtype=torch.uint8, device=dev)
+    step = lambda: blk.forward(x, cond, cu_d, cu, grid_d, out=out, workspace=ws)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_wall = time.perf_counter()
+    timer = Timer(torch)
+    ms_step = timer(step, args.steps)
+    t_wall = time.perf_counter() - t_wall
+
+    f_attn = attention_flops(wl.lengths, wl.heads, wl.head_dim)
+    f_gemm = gemm_flops(n, c, wl.ffn, b)
+    block_tflops = (f_attn + f_gemm) / (ms_step * 1e-3) / 1e12
+
+    # attention alone, on the block's own q/k/v (after norm + RoPE), same launch
+    taps = blk.make_taps(b, n, dev)
+    blk.forward(x, cond, cu_d, cu, grid_d, out=out, taps=taps, workspace=ws)
+    qkv = taps["qkv"]
+    hd = wl.heads * wl.head_dim
+    qv = qkv[:, :hd].view(n, wl.heads, wl.head_dim)
+    kv = qkv[:, hd:2 * hd].view(n, wl.heads, wl.head_dim)
+    vv = qkv[:, 2 * hd:].view(n, wl.heads, wl.head_dim)
+    o_att = taps["o"].view(n, wl.heads, wl.head_dim)
+    attn_ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    attn = lambda: ops.attn_varlen(qv, kv, vv, cu_d, cu, out=o_att, workspace=attn_ws)
+    attn()
+    log("timing attention")
+    ms_attn = timer(attn, max(3, args.steps))
+    attn_tflops = f_attn / (ms_attn * 1e-3) / 1e12
+
+    stages = {}
+    if not args.no_stages:
+        log("timing stages")
+        mod = taps["mod"]
+        it = max(3, args.steps)
+        w = weights
+
+        def rec(name, ms, flops=None, nbytes=None):
+            e = {"ms": round(ms, 4)}
+            if flops is not None:
+                e["tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+                e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+            if nbytes is not None:
+                e["gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+                e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+            stages[name] = e
+
+        rec("modulation_gemv", timer(lambda: ops.modulation(cond, w["w_mod"]), it),
+            nbytes=6 * c * c * 2 + b * c * 2 + b * 6 * c * 4)
+        rec("adaln_rmsnorm_modulate",
+            timer(lambda: ops.adaln_rmsnorm_modulate(x, mod[:, 0:c], mod[:, c:2 * c], cu_d, cu,
+                                                     out=taps["h"]), it),
+            nbytes=2 * n * c * 2)
+        rec("qkv_gemm", timer(lambda: ops.linear(taps["h"], w["w_qkv"]), it),
+            flops=2.0 * n * c * 3 * c)
+        qkv2 = qkv.clone()
+        q2 = qkv2[:, :hd].view(n, wl.heads, wl.head_dim)
+        k2 = qkv2[:, hd:2 * hd].view(n, wl.heads, wl.head_dim)
+        rec("qk_rmsnorm_rope",
+            timer(lambda: ops.qk_rmsnorm_rope(q2, k2, w["q_norm"], w["k_norm"], grid_d, split),
+                  it),
+            nbytes=4 * n * c * 2 + 12 * n)
+        del qkv2
+        rec("attention_bf16", ms_attn, flops=f_attn)
+        rec("out_proj_gated_residual",
+            timer(lambda: ops.linear_gated_residual(taps["o"], w["w_o"], x, mod[:, 2 * c:3 * c],
+                                                    cu_d, cu, out=taps["x1"]), it),
+            flops=2.0 * n * c * c)
+        rec("swiglu_gemm", timer(lambda: ops.linear_swiglu(taps["h2"], w["w_gate"], w["w_up"]), it),
+            flops=2.0 * n * c * 2 * wl.ffn)
+        rec("down_gated_residual",
+            timer(lambda: ops.linear_gated_residual(taps["a"], w["w_down"], taps["x1"],
+                                                    mod[:, 5 * c:6 * c], cu_d, cu,
+                                                    out=taps["h2"]), it),
+            flops=2.0 * n * wl.ffn * c)
+
+    traffic = load_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(block_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": n, "segments": b, "hidden": c,
+                   "heads": wl.heads, "head_dim": wl.head_dim, "ffn": wl.ffn,
+                   "seed": inp.seed},
+        "block_ms": round(ms_step, 4),
+        "block_tflop": round((f_attn + f_gemm) / 1e12, 4),
+        "attention_tflops": round(attn_tflops, 2),
+        "attention_ms": round(ms_attn, 4),
+        "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "block_frac_bf16_peak": round(block_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "attn_bf16_kernel<128>", "bound": "mfma",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "stages": stages,
+        "timed_wall_s": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(inp, wl)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

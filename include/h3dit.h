@@ -1,0 +1,290 @@
+/*
+ * h3dit.h - C ABI of the MI355X (gfx950) library for the packed joint
+ * audio-video DiT hot path.
+ *
+ * The library computes one transformer block of a joint audio-video
+ * diffusion transformer over a single packed token sequence: text, audio and
+ * video tokens of each request sit back to back in one row, and only valid
+ * tokens are ever computed (no padding). Sources, cited by page title and
+ * section:
+ *   [FastH3-EN] "MiniMax H3 FastH3 real-time serving with vLLM-Omni",
+ *       section "System-wide optimizations in vLLM-Omni": the bullet on
+ *       long-sequence attention (packed sequence, padding removed) and the
+ *       bullet on fused DiT operators (RMSNorm, RoPE, modulation,
+ *       normalization and SwiGLU fused into fewer launches); section
+ *       "Scaling beyond the FastH3 profile", bullet on sparse & quantized
+ *       attention (FP8 attention, Skip-Softmax).
+ *   [FastH3-ZH] "FastH3 在八卡 B300 上实现完整 MP4 生成快于播放时长",
+ *       sections "长序列注意力与通信优化" (about 58k packed tokens, valid
+ *       tokens only) and "融合 DiT 算子" (Q/K norm merged with RoPE, SwiGLU
+ *       replacing SiLU + multiply, residual connection).
+ * The pages name the operators but not their equations; each entry point
+ * states the definition it implements.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are row-major. "bf16" buffers hold IEEE bfloat16 bit patterns.
+ *    Linear weights use the [out, in] layout (both GEMM operands are
+ *    contiguous along the reduction axis).
+ *  - Pointers named *_dev / device pointers must be device memory of the
+ *    current HIP device; *_host pointers are host memory read synchronously
+ *    during the call. The caller owns every buffer, including workspaces.
+ *    The library never allocates, frees or synchronises: it validates the
+ *    arguments on the host, enqueues kernels on `hip_stream` (a hipStream_t,
+ *    NULL for the default stream) and returns.
+ *  - All argument checks run before the first launch, so a non-OK status
+ *    means nothing was enqueued (except H3_ERR_HIP, reported when a launch
+ *    itself fails; later launches of that call are then not enqueued).
+ *    Faults inside kernels surface at the caller's next synchronisation.
+ *  - cu_seqlens (int32[num_seqs + 1]): cu[0] = 0, non-decreasing,
+ *    cu[num_seqs] = total_tokens. Empty segments are allowed. The host copy
+ *    is validated; the device copy must hold the same values.
+ *  - Thread safety: the only library state is a thread-local error message.
+ */
+#ifndef H3DIT_H
+#define H3DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define H3_API __attribute__((visibility("default")))
+#else
+#define H3_API
+#endif
+
+#define H3_ABI_VERSION 1
+
+/* Largest number of packed segments accepted by one call. */
+#define H3_MAX_SEGMENTS 65536
+/* Query rows per attention work item (the tile of the work list). */
+#define H3_ATTN_BLOCK_M 128
+/* Tokens per fp8 Q/K scale block (aligned to each segment's start). */
+#define H3_FP8_QK_BLOCK 64
+
+typedef enum {
+    H3_OK = 0,
+    H3_ERR_INVALID_ARGUMENT = 1, /* malformed sizes, pointers or cu_seqlens */
+    H3_ERR_UNSUPPORTED = 2,      /* well-formed but not implemented (e.g. head_dim) */
+    H3_ERR_WORKSPACE_TOO_SMALL = 3,
+    H3_ERR_HIP = 4               /* a HIP runtime call or launch failed */
+} h3_status;
+
+typedef enum { H3_ATTN_BF16 = 0, H3_ATTN_FP8_E4M3 = 1 } h3_attn_precision;
+
+/* Status name, e.g. "H3_ERR_UNSUPPORTED". Never NULL. */
+H3_API const char* h3_status_string(h3_status status);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+H3_API const char* h3_last_error_message(void);
+H3_API int32_t h3_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Varlen bookkeeping ([FastH3-EN] long-sequence attention bullet: only the
+ * valid tokens of the packed sequence are scheduled).
+ *
+ * Work list of the attention kernels: one item per (head, segment, query
+ * tile of block_m rows), item = int32[4] {head, segment, first query token
+ * (absolute index), rows in the tile}. Order: segments by descending length
+ * (ties: ascending segment index), then head ascending, then query tile
+ * ascending. Empty segments contribute no item. Count = num_heads *
+ * sum_s ceil(L_s / block_m).
+ * ---------------------------------------------------------------------- */
+
+/* Host builder. items_out may be NULL to query the count only; otherwise it
+ * must hold `capacity` items (4 * capacity int32). count_out (required)
+ * receives the count. block_m must be positive. */
+H3_API h3_status h3_build_schedule_host(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                        int32_t num_heads, int32_t block_m,
+                                        int32_t* items_out, int64_t capacity,
+                                        int64_t* count_out);
+
+/* Device builder, the same list bit for bit, plus:
+ *   seg_id_dev  int32[total_tokens]: segment of each token (may be NULL);
+ *   tile_cu_dev int32[num_seqs + 1]: tile_cu[0] = 0, tile_cu[s + 1] =
+ *               tile_cu[s] + ceil(L_s / block_m) in segment order (may be NULL).
+ * items_dev must hold items_capacity >= count items. Needs a workspace of
+ * h3_varlen_bookkeeping_workspace_size(num_seqs) bytes. */
+H3_API size_t h3_varlen_bookkeeping_workspace_size(int32_t num_seqs);
+H3_API h3_status h3_varlen_bookkeeping(const int32_t* cu_seqlens_dev,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                       int32_t total_tokens, int32_t num_heads,
+                                       int32_t block_m, int32_t* seg_id_dev,
+                                       int32_t* tile_cu_dev, int32_t* items_dev,
+                                       int64_t items_capacity, void* workspace,
+                                       size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Varlen joint attention ([FastH3-EN] long-sequence attention bullet;
+ * [FastH3-ZH] long-sequence attention section).
+ *
+ * For every segment s and head h: O = softmax(Q K^T * scale) V over the
+ * segment's tokens only (non-causal, nothing across segments), fp32
+ * accumulation, softmax as exp(S - rowmax)/sum.
+ * q, k, v, out: bf16, token t / head h / dim d at ptr[t * tok_stride + h *
+ * head_dim + d] (strides in elements; heads contiguous inside a token).
+ * head_dim must be 64 or 128 (H3_ERR_UNSUPPORTED otherwise).
+ *
+ * precision = H3_ATTN_FP8_E4M3 ([FastH3-EN] sparse & quantized attention
+ * bullet; [FastH3-ZH] section "其他加速路径：有损但可控", SAGE and
+ * Skip-Softmax) quantises Q and K to OCP e4m3 with one scale per (head,
+ * 64-token block aligned to the segment start), V with one scale per
+ * (segment, head, channel), runs Q K^T and P V on fp8 MFMA with P encoded
+ * as e4m3(448 * p), and, with skip_softmax set, skips exp and P V for a key
+ * tile of 64 keys when every valid row of a 32-row query group has its tile
+ * maximum more than skip_threshold (natural-log units) below its running
+ * maximum (never the segment's first key tile). fp8 needs head_dim 128.
+ * skip_counts (optional, device int32[items]) receives per work item the
+ * number of skipped (32-row group, key tile) pairs; no atomics are used.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t precision;       /* h3_attn_precision */
+    int32_t skip_softmax;    /* fp8 only; 0 = off */
+    float skip_threshold;    /* natural-log units; <= 0 means 8 */
+    float softmax_scale;     /* 0 means 1 / sqrt(head_dim) */
+    int32_t* skip_counts;    /* optional device int32[work items] */
+} h3_attn_opts;
+
+/* opts may be NULL (bf16, default scale). */
+H3_API size_t h3_attn_varlen_workspace_size(int32_t num_seqs, int32_t total_tokens,
+                                            int32_t num_heads, int32_t head_dim,
+                                            const h3_attn_opts* opts);
+/* Number of work items (the length skip_counts must have). */
+H3_API h3_status h3_attn_varlen_num_items(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                          int32_t num_heads, int64_t* count_out);
+H3_API h3_status h3_attn_varlen(const void* q, const void* k, const void* v, void* out,
+                                int64_t q_tok_stride, int64_t k_tok_stride,
+                                int64_t v_tok_stride, int64_t o_tok_stride,
+                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                int32_t head_dim, const h3_attn_opts* opts, void* workspace,
+                                size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Fused Q/K RMSNorm + 3D RoPE, in place ([FastH3-ZH] "融合 DiT 算子": the
+ * Q/K normalisation is merged with RoPE).
+ *
+ * For every token t and head h, with x = q[t, h, :] (and likewise k):
+ *   x <- RoPE_t(RMSNorm(x) * w),  RMSNorm(x) = x / sqrt(mean(x^2) + eps)
+ * w_q / w_k: bf16 [head_dim] gains shared by all heads. RoPE: the head dim
+ * is split into (d_t, d_h, d_w) = rope_split (even, summing to head_dim);
+ * inside axis a's slice, pair j = dims (2j, 2j+1) is rotated by the angle
+ * pos_a * theta^(-2j / d_a), (u, v) -> (u cos - v sin, u sin + v cos), with
+ * pos = rope_grid[t] (device int32 [total_tokens, 3] = (t, h, w)).
+ * q/k: bf16 with token strides in elements, heads contiguous. Math in fp32,
+ * result rounded to bf16. head_dim 64 or 128.
+ * ---------------------------------------------------------------------- */
+H3_API h3_status h3_qk_rmsnorm_rope(void* q, void* k, int64_t q_tok_stride,
+                                    int64_t k_tok_stride, const void* w_q, const void* w_k,
+                                    const int32_t* rope_grid, int32_t total_tokens,
+                                    int32_t num_heads, int32_t head_dim,
+                                    const int32_t rope_split[3], float theta, float eps,
+                                    void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * AdaLN modulation ([FastH3-EN] fused DiT operators bullet: modulation).
+ *
+ * mod[b, :] = cond[b, :] . W_mod^T (fp32 out, [num_seqs, 6 * hidden]);
+ * cond bf16 [num_seqs, hidden], W_mod bf16 [6 * hidden, hidden]. The six
+ * chunks of `hidden` are, in order: shift1, scale1, gate1, shift2, scale2,
+ * gate2. fp32 accumulation.
+ * ---------------------------------------------------------------------- */
+H3_API h3_status h3_modulation(const void* cond, const void* w_mod, float* mod_out,
+                               int32_t num_seqs, int32_t hidden, void* hip_stream);
+
+/* RMSNorm + modulate ([FastH3-EN] fused DiT operators bullet: modulation and
+ * normalization in one kernel):
+ *   h[t, :] = RMSNorm(x[t, :]) * (1 + scale[seg(t), :]) + shift[seg(t), :]
+ * x, h: bf16 [total_tokens, hidden] (row stride = hidden); shift, scale:
+ * fp32 rows of `mod_row_stride` floats per segment (e.g. pointers into the
+ * h3_modulation output, stride 6 * hidden). hidden must be a multiple of 512
+ * and at most 8192. */
+H3_API h3_status h3_adaln_rmsnorm_modulate(const void* x, void* h_out, const float* shift,
+                                           const float* scale, int64_t mod_row_stride,
+                                           const int32_t* cu_seqlens_dev,
+                                           const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                           int32_t total_tokens, int32_t hidden, float eps,
+                                           void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Linear layers on bf16 MFMA with fused epilogues ([FastH3-ZH] "融合 DiT
+ * 算子": SwiGLU in place of separate SiLU and multiply, the residual
+ * connection; [FastH3-EN] fused DiT operators bullet).
+ *
+ * a: bf16 [m, k] (row stride k); weights bf16 [n, k]; output bf16 [m, n].
+ * fp32 accumulation, one bf16 rounding at the end. m >= 0; n a multiple of
+ * 128 (64 for SwiGLU), k a multiple of 64.
+ *   h3_linear_bf16:              y = a . W^T
+ *   h3_linear_swiglu_bf16:       y = silu(a . W_gate^T) * (a . W_up^T),
+ *                                silu(z) = z / (1 + e^-z)
+ *   h3_linear_gated_residual_bf16:
+ *                                y[t, :] = res[t, :] + gate[seg(t), :] * (a . W^T)[t, :]
+ *                                (res bf16 [m, n], may equal y; gate fp32 rows
+ *                                of gate_row_stride floats per segment)
+ * ---------------------------------------------------------------------- */
+H3_API h3_status h3_linear_bf16(const void* a, const void* w, void* y, int64_t m, int64_t n,
+                                int64_t k, void* hip_stream);
+H3_API h3_status h3_linear_swiglu_bf16(const void* a, const void* w_gate, const void* w_up,
+                                       void* y, int64_t m, int64_t n, int64_t k,
+                                       void* hip_stream);
+H3_API h3_status h3_linear_gated_residual_bf16(const void* a, const void* w, const void* res,
+                                               const float* gate, int64_t gate_row_stride,
+                                               void* y, int64_t m, int64_t n, int64_t k,
+                                               const int32_t* cu_seqlens_dev,
+                                               const int32_t* cu_seqlens_host,
+                                               int32_t num_seqs, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * One DiT block over the packed sequence (all of the above, in order):
+ *   mod = cond W_mod^T                      -> shift1 scale1 gate1 shift2 scale2 gate2
+ *   h   = RMSNorm(x)(1 + scale1) + shift1
+ *   qkv = h W_qkv^T                         (q | k | v, each [H * D], head-major)
+ *   q,k = RoPE(RMSNorm_D(q|k) * gain)       (h3_qk_rmsnorm_rope)
+ *   o   = varlen attention(q, k, v)         (bf16 path)
+ *   x1  = x + gate1 * (o W_o^T)
+ *   h2  = RMSNorm(x1)(1 + scale2) + shift2
+ *   a   = silu(h2 W_gate^T) * (h2 W_up^T)
+ *   x2  = x1 + gate2 * (a W_down^T)        -> x_out
+ * This is a plain reading of the operator list of [FastH3-EN]'s fused DiT
+ * operators bullet and [FastH3-ZH]'s "融合 DiT 算子" section as a
+ * single-stream pre-norm AdaLN-Zero block; cond is one bf16 vector of
+ * `hidden` per segment (request). Every intermediate is stored in bf16
+ * (mod in fp32). x, x_out: bf16 [total_tokens, hidden] (may not alias).
+ * hidden = num_heads * head_dim; ffn_dim a multiple of 128.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t hidden, num_heads, head_dim, ffn_dim;
+    int32_t rope_split[3];
+    float rope_theta, eps;
+} h3_dit_dims;
+
+typedef struct {
+    const void *w_mod, *w_qkv, *w_o, *q_norm, *k_norm, *w_gate, *w_up, *w_down;
+} h3_dit_weights;
+
+/* Optional caller buffers for intermediates; a non-NULL field replaces the
+ * workspace buffer of that intermediate, so the caller can read it after the
+ * call. mod: fp32 [B, 6C]; h, o, x1, h2: bf16 [N, C]; qkv: bf16 [N, 3C];
+ * a: bf16 [N, ffn]. */
+typedef struct {
+    float* mod;
+    void *h, *qkv, *o, *x1, *h2, *a;
+} h3_dit_taps;
+
+H3_API size_t h3_dit_block_workspace_size(const h3_dit_dims* dims, int32_t num_seqs,
+                                          int32_t total_tokens);
+H3_API h3_status h3_dit_block_forward(const void* x, void* x_out, const void* cond,
+                                      const h3_dit_weights* weights, const h3_dit_dims* dims,
+                                      const int32_t* cu_seqlens_dev,
+                                      const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                      int32_t total_tokens, const int32_t* rope_grid,
+                                      const h3_dit_taps* taps, void* workspace,
+                                      size_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3DIT_H */

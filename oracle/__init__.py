@@ -9,12 +9,12 @@ invariants, special cases or brute force):
   segment_ids, tile_offsets, schedule_ref, rmsnorm, rope_3d,
   qk_norm_rope_ref, attn_varlen_ref, modulation_ref, adaln_modulate_ref,
   silu, swiglu_ref, gated_residual_ref, dit_block_ref, dit_block_rows_ref,
-  e4m3_round, fp8_attn_emulated_ref.
+  e4m3_round, fp8_attn_emulated_ref, bf16_round (storage emulation).
 
 Parity unpinned: agreement of the block structure with the real model's
 block (the pages give operator names only, no equations or weights).
 """
-from .h3_oracle import (MOD_CHUNKS, adaln_modulate_ref, attn_varlen_ref, check_cu_seqlens,
+from .h3_oracle import (MOD_CHUNKS, adaln_modulate_ref, bf16_round, attn_varlen_ref, check_cu_seqlens,
                         dit_block_ref, dit_block_rows_ref, gated_residual_ref, modulation_ref,
                         qk_norm_rope_ref, rel_frobenius, rmsnorm, rope_3d, schedule_ref,
                         segment_ids, silu, split_modulation, swiglu_ref, tile_offsets)
@@ -22,7 +22,7 @@ from .fp8_attention import (e4m3_round, fp8_attn_emulated_ref, quantize_qk_block
                             quantize_v_channels)
 
 __all__ = [
-    "MOD_CHUNKS", "adaln_modulate_ref", "attn_varlen_ref", "check_cu_seqlens", "dit_block_ref",
+    "MOD_CHUNKS", "adaln_modulate_ref", "bf16_round", "attn_varlen_ref", "check_cu_seqlens", "dit_block_ref",
     "dit_block_rows_ref", "gated_residual_ref", "modulation_ref", "qk_norm_rope_ref",
     "rel_frobenius", "rmsnorm", "rope_3d", "schedule_ref", "segment_ids", "silu",
     "split_modulation", "swiglu_ref", "tile_offsets", "e4m3_round", "fp8_attn_emulated_ref",

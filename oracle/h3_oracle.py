@@ -49,6 +49,21 @@ def _f64(a) -> np.ndarray:
     return np.asarray(a, dtype=_F)
 
 
+def bf16_round(a) -> np.ndarray:
+    """Nearest bfloat16 value (8 significant bits, ties to even), in float64.
+
+    Used only by the storage emulation of the block (see dit_block_ref); the
+    exact oracle never rounds. Finite inputs within the bf16 range.
+    """
+    a = _f64(a)
+    m, e = np.frexp(a)                  # a = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)   # np.round: ties to even
+
+
+def _identity(a):
+    return a
+
+
 # --------------------------------------------------------------------------
 # Packed-sequence bookkeeping  ([FastH3-EN] long-sequence attention bullet:
 # padding is removed, so every index below refers to valid tokens only)
@@ -253,8 +268,14 @@ def _split_heads(qkv: np.ndarray, heads: int, head_dim: int):
 
 def dit_block_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], grid,
                   heads: int, head_dim: int, rope_split: Sequence[int],
-                  rope_theta: float = 10000.0, eps: float = 1e-6) -> Dict[str, np.ndarray]:
+                  rope_theta: float = 10000.0, eps: float = 1e-6,
+                  emulate_bf16_storage: bool = False) -> Dict[str, np.ndarray]:
     """One block over the whole packed sequence; returns every intermediate.
+
+    With emulate_bf16_storage, every intermediate that the device path stores
+    between kernels is rounded to bf16 (h, qkv, q/k after norm + RoPE, o, x1,
+    h2, a, x2) and mod to float32; all arithmetic in between stays float64.
+    This models the storage precision of the path, not its exact value.
 
     h   = RMSNorm(x)(1+scale1)+shift1
     qkv = h W_qkv^T                   (q | k | v, each head-major [H*D])
@@ -265,21 +286,25 @@ def dit_block_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], gr
     a   = silu(h2 W_gate^T) * (h2 W_up^T)
     x2  = x1 + gate2 * (a W_down^T)
     """
+    st = bf16_round if emulate_bf16_storage else _identity
     x = _f64(x)
     n, c = x.shape
     seg = segment_ids(cu)
     mod = modulation_ref(cond, weights["w_mod"])
+    if emulate_bf16_storage:
+        mod = mod.astype(np.float32).astype(_F)
     m = split_modulation(mod, c)
-    h = adaln_modulate_ref(x, m["shift1"], m["scale1"], seg, eps)
-    qkv = h @ _f64(weights["w_qkv"]).T
+    h = st(adaln_modulate_ref(x, m["shift1"], m["scale1"], seg, eps))
+    qkv = st(h @ _f64(weights["w_qkv"]).T)
     q, k, v = _split_heads(qkv, heads, head_dim)
     qr, kr = qk_norm_rope_ref(q, k, weights["q_norm"], weights["k_norm"], grid, rope_split,
                               rope_theta, eps)
-    o = attn_varlen_ref(qr, kr, v, cu).reshape(n, c)
-    x1 = gated_residual_ref(x, m["gate1"], o @ _f64(weights["w_o"]).T, seg)
-    h2 = adaln_modulate_ref(x1, m["shift2"], m["scale2"], seg, eps)
-    a = swiglu_ref(h2, weights["w_gate"], weights["w_up"])
-    x2 = gated_residual_ref(x1, m["gate2"], a @ _f64(weights["w_down"]).T, seg)
+    qr, kr = st(qr), st(kr)
+    o = st(attn_varlen_ref(qr, kr, v, cu).reshape(n, c))
+    x1 = st(gated_residual_ref(x, m["gate1"], o @ _f64(weights["w_o"]).T, seg))
+    h2 = st(adaln_modulate_ref(x1, m["shift2"], m["scale2"], seg, eps))
+    a = st(swiglu_ref(h2, weights["w_gate"], weights["w_up"]))
+    x2 = st(gated_residual_ref(x1, m["gate2"], a @ _f64(weights["w_down"]).T, seg))
     return {"mod": mod, "h": h, "qkv": qkv, "q": qr.reshape(n, c), "k": kr.reshape(n, c),
             "v": v.reshape(n, c), "o": o, "x1": x1, "h2": h2, "a": a, "x2": x2}
 
@@ -287,14 +312,17 @@ def dit_block_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], gr
 def dit_block_rows_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], grid,
                        heads: int, head_dim: int, rope_split: Sequence[int], rows,
                        rope_theta: float = 10000.0, eps: float = 1e-6,
-                       token_chunk: int = 4096) -> Dict[str, np.ndarray]:
-    """The same block, exact, for the sampled token indices `rows` only.
+                       token_chunk: int = 4096,
+                       emulate_bf16_storage: bool = False) -> Dict[str, np.ndarray]:
+    """The same block for the sampled token indices `rows` only (exact, or
+    with the storage emulation of dit_block_ref).
 
     Keys and values of every token of the segments that hold a sampled row
     are computed (a sampled row attends to its whole segment); everything
     else is computed for the sampled rows alone. Outputs have len(rows)
     leading rows. Memory is bounded by processing tokens in chunks.
     """
+    st = bf16_round if emulate_bf16_storage else _identity
     cu = check_cu_seqlens(cu)
     x32 = np.asarray(x)
     n, c = x32.shape
@@ -302,14 +330,15 @@ def dit_block_rows_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int
     seg = segment_ids(cu)
     grid = np.asarray(grid)
     mod = modulation_ref(cond, weights["w_mod"])
+    if emulate_bf16_storage:
+        mod = mod.astype(np.float32).astype(_F)
     m = split_modulation(mod, c)
     w_qkv = _f64(weights["w_qkv"])
     w_q, w_k, w_v = w_qkv[0:c], w_qkv[c:2 * c], w_qkv[2 * c:3 * c]
     wq_t, wk_t, wv_t = w_q.T.copy(), w_k.T.copy(), w_v.T.copy()
 
     def project(tok):
-        h = adaln_modulate_ref(x32[tok], m["shift1"], m["scale1"], seg[tok], eps)
-        return h
+        return st(adaln_modulate_ref(x32[tok], m["shift1"], m["scale1"], seg[tok], eps))
 
     out_o = np.zeros((rows.size, heads, head_dim), dtype=_F)
     for s in np.unique(seg[rows]) if rows.size else []:
@@ -319,31 +348,31 @@ def dit_block_rows_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int
         for t0 in range(a, b, token_chunk):
             tok = np.arange(t0, min(b, t0 + token_chunk))
             h = project(tok)
-            k_raw = (h @ wk_t).reshape(tok.size, heads, head_dim)
-            vv[t0 - a:t0 - a + tok.size] = (h @ wv_t).reshape(tok.size, heads, head_dim)
+            k_raw = st(h @ wk_t).reshape(tok.size, heads, head_dim)
+            vv[t0 - a:t0 - a + tok.size] = st(h @ wv_t).reshape(tok.size, heads, head_dim)
             kn = rmsnorm(k_raw, eps) * _f64(weights["k_norm"])
-            kk[t0 - a:t0 - a + tok.size] = rope_3d(kn, grid[tok][:, None, :], rope_split,
-                                                    rope_theta)
+            kk[t0 - a:t0 - a + tok.size] = st(rope_3d(kn, grid[tok][:, None, :], rope_split,
+                                                       rope_theta))
         sel = np.nonzero(seg[rows] == s)[0]
         tok = rows[sel]
         h = project(tok)
-        q_raw = (h @ wq_t).reshape(tok.size, heads, head_dim)
+        q_raw = st(h @ wq_t).reshape(tok.size, heads, head_dim)
         qn = rmsnorm(q_raw, eps) * _f64(weights["q_norm"])
-        qq = rope_3d(qn, grid[tok][:, None, :], rope_split, rope_theta)
+        qq = st(rope_3d(qn, grid[tok][:, None, :], rope_split, rope_theta))
         local_cu = [0, b - a]
         # attention of the sampled queries against the whole segment
         q_full = np.zeros((b - a, heads, head_dim), dtype=_F)
         q_full[tok - a] = qq
         out_o[sel] = attn_varlen_ref(q_full, kk, vv, local_cu, rows=tok - a)
 
-    o = out_o.reshape(rows.size, c)
+    o = st(out_o.reshape(rows.size, c))
     segr = seg[rows]
     xr = _f64(x32[rows])
-    h = adaln_modulate_ref(xr, m["shift1"], m["scale1"], segr, eps)
-    x1 = gated_residual_ref(xr, m["gate1"], o @ _f64(weights["w_o"]).T, segr)
-    h2 = adaln_modulate_ref(x1, m["shift2"], m["scale2"], segr, eps)
-    act = swiglu_ref(h2, weights["w_gate"], weights["w_up"])
-    x2 = gated_residual_ref(x1, m["gate2"], act @ _f64(weights["w_down"]).T, segr)
+    h = st(adaln_modulate_ref(xr, m["shift1"], m["scale1"], segr, eps))
+    x1 = st(gated_residual_ref(xr, m["gate1"], o @ _f64(weights["w_o"]).T, segr))
+    h2 = st(adaln_modulate_ref(x1, m["shift2"], m["scale2"], segr, eps))
+    act = st(swiglu_ref(h2, weights["w_gate"], weights["w_up"]))
+    x2 = st(gated_residual_ref(x1, m["gate2"], act @ _f64(weights["w_down"]).T, segr))
     return {"mod": mod, "h": h, "o": o, "x1": x1, "h2": h2, "a": act, "x2": x2}
 
 

@@ -183,3 +183,35 @@ def test_sampled_rows_path_equals_full_path():
     part = dit_block_rows_ref(x, cond, w, cu, grid, H, D, SPLIT, rows, eps=EPS, token_chunk=4)
     for key in ("h", "o", "x1", "h2", "a", "x2"):
         assert np.max(np.abs(part[key] - full[key][rows])) < 1e-12, key
+
+
+def test_bf16_round_ties_and_torch_cast():
+    from oracle import bf16_round
+    assert bf16_round(1.0 + 2.0 ** -8) == 1.0                    # tie -> even
+    assert bf16_round(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6     # tie -> even
+    assert bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+    assert bf16_round(-3.0) == -3.0 and bf16_round(0.0) == 0.0
+    torch = pytest.importorskip("torch")
+    a = np.random.default_rng(9).standard_normal(50000).astype(np.float32)
+    a[:100] *= 1e-30
+    a[100:200] *= 1e30
+    t = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bf16_round(a.astype(np.float64)), t)
+
+
+def test_storage_emulation_rounds_every_boundary_and_stays_close():
+    from oracle import bf16_round
+    cu, x, cond, grid = _case(8, cu=(0, 9, 20))
+    x = bf16_round(x)
+    w = _weights(8, ffn=24)
+    ex = dit_block_ref(x, cond, w, cu, grid, H, D, SPLIT, eps=EPS)
+    em = dit_block_ref(x, cond, w, cu, grid, H, D, SPLIT, eps=EPS, emulate_bf16_storage=True)
+    for key in ("h", "qkv", "q", "k", "o", "x1", "h2", "a", "x2"):
+        assert np.array_equal(bf16_round(em[key]), em[key]), key
+        assert oracle.rel_frobenius(em[key], ex[key]) < 1e-2, key
+    assert np.array_equal(em["mod"].astype(np.float32).astype(np.float64), em["mod"])
+    rows = np.array([0, 5, 19])
+    part = dit_block_rows_ref(x, cond, w, cu, grid, H, D, SPLIT, rows, eps=EPS,
+                              emulate_bf16_storage=True, token_chunk=4)
+    for key in ("h", "o", "x1", "h2", "a", "x2"):
+        assert np.max(np.abs(part[key] - em[key][rows])) < 1e-12, key
