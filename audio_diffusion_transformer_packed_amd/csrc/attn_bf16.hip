@@ -26,7 +26,6 @@
 namespace h3 {
 namespace {
 
-constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;  // four waves
 
@@ -38,6 +37,90 @@ struct Lds {
     static constexpr int vElems = D * vStride;
     static constexpr int bufElems = kElems + vElems;
 };
+
+// One 64-key tile for one wave's 32 query rows: S^T = K Q^T, online softmax
+// (lazy max, exp2 domain), O^T += V^T P^T. With MASK, keys at or past
+// keys_left (the segment end) are excluded.
+template <int D, bool MASK>
+__device__ __forceinline__ void attn_tile(const uint16_t* __restrict__ kl,
+                                          const uint16_t* __restrict__ vl,
+                                          const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
+                                          float& m_run, float& l_run, float scale_log2,
+                                          float lazy_raw, int keys_left, int l32, int g) {
+    using L = Lds<D>;
+    constexpr int KC = D / 16;
+    constexpr int DB = D / 32;
+
+    // S^T = K Q^T for keys [32b, 32b + 32) of the tile
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const u32x4 kf = *reinterpret_cast<const u32x4*>(kl + (32 * b + l32) * L::kStride + 16 * c + 8 * g);
+            sacc[b] = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[c], sacc[b]);
+        }
+    }
+    if (MASK) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (key >= keys_left) sacc[b][r] = -INFINITY;
+            }
+    }
+
+    float mt = sacc[0][0];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(sacc[0][r], sacc[1][r]));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    if (__any(mt > m_run + lazy_raw)) {       // wave-uniform, rare after the first tiles
+        // keeps this block a real branch (not if-converted into 64 multiplies
+        // by a selected alpha on every tile)
+        asm volatile("" ::: "memory");
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float mb = m_run * scale_log2;
+
+    float psum = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * t + e], scale_log2, -mb));
+                psum += p;
+                pf[b][t][e] = static_cast<__bf16>(p);
+            }
+        }
+    }
+    l_run += psum;
+
+    // O^T += V^T P^T; k-step (b, t) covers keys 32b + 16t + [0, 16); lane half
+    // g supplies keys 4g + [0,4) and 8 + 4g + [0,4) of it, the rows the S^T
+    // accumulator gave this lane.
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const uint16_t* vrow = vl + (32 * db + l32) * L::vStride + 4 * g;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 32 * b + 16 * t);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32 * b + 16 * t + 8);
+                const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
+                oacc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, vf), pf[b][t], oacc[db]);
+            }
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
@@ -80,160 +163,110 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                              static_cast<int64_t>(head) * D + 8 * g;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-            Chunk16 ch;
-            ch.u = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * c) : make_uint4(0, 0, 0, 0);
-            qf[c] = ch.b;
+            const u32x4 ch = qvalid ? *reinterpret_cast<const u32x4*>(qp + 16 * c) : u32x4{0, 0, 0, 0};
+            qf[c] = __builtin_bit_cast(bf16x8, ch);
         }
     }
 
-    const uint16_t* kbase = k + static_cast<int64_t>(head) * D;
-    const uint16_t* vbase = v + static_cast<int64_t>(head) * D;
-
     // ---- global -> register staging of one K/V tile ----
-    uint4 kreg[K_PER_T];
-    uint4 vreg[4];
+    // Every load is unconditional: rows past the segment end are clamped to
+    // its last row (finite data of this segment); their scores are masked to
+    // -inf in the last tile, so they contribute exactly zero.
+    constexpr int K_ROWS_PER_PASS = kThreads / (D / 8);
+    const int k_r0 = tid / (D / 8);
+    const int k_c = tid % (D / 8);
     const int vg = tid;                          // V group of this thread
     const int v_key4 = vg % (kBN / 4);
     const int v_dchunk = vg / (kBN / 4);
+    const bool v_active = vg < V_GROUPS;
+    const uint16_t* kthr = k + static_cast<int64_t>(head) * D + 8 * k_c;
+    const uint16_t* vthr = v + static_cast<int64_t>(head) * D + 8 * (v_active ? v_dchunk : 0);
+    const int64_t k_pass_stride = static_cast<int64_t>(K_ROWS_PER_PASS) * ks;
 
-    auto load_tile = [&](int tile) {
-        const int key0 = kv0 + tile * kBN;
-#pragma unroll
-        for (int i = 0; i < K_PER_T; ++i) {
-            const int ci = tid + i * kThreads;
-            const int r = ci / (D / 8);
-            const int c = ci % (D / 8);
-            const int key = key0 + r;
-            kreg[i] = key < kv1 ? *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(key) * ks + 8 * c)
-                                : make_uint4(0, 0, 0, 0);
-        }
-        if (vg < V_GROUPS) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = key0 + 4 * v_key4 + r;
-                vreg[r] = key < kv1 ? *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(key) * vs + 8 * v_dchunk)
-                                    : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-
-    auto store_tile = [&](int buf) {
-        uint16_t* kl = lds + buf * L::bufElems;
-        uint16_t* vl = kl + L::kElems;
-#pragma unroll
-        for (int i = 0; i < K_PER_T; ++i) {
-            const int ci = tid + i * kThreads;
-            const int r = ci / (D / 8);
-            const int c = ci % (D / 8);
-            *reinterpret_cast<uint4*>(kl + r * L::kStride + 8 * c) = kreg[i];
-        }
-        if (vg < V_GROUPS) {
-            Chunk16 c0, c1, c2, c3;
-            c0.u = vreg[0]; c1.u = vreg[1]; c2.u = vreg[2]; c3.u = vreg[3];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                Chunk8 t;
-                t.h[0] = c0.h[e]; t.h[1] = c1.h[e]; t.h[2] = c2.h[e]; t.h[3] = c3.h[e];
-                *reinterpret_cast<uint2*>(vl + (8 * v_dchunk + e) * L::vStride + 4 * v_key4) = t.u;
-            }
-        }
-    };
+    u32x4 kreg[K_PER_T];
+    u32x4 vreg[4];
 
     f32x16 oacc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
-    float m_run = -INFINITY;   // running max of raw scores for this lane's query row
+    // Reference max of this lane's query row (raw score units). It only moves
+    // when a tile's max exceeds it by more than kLazy / scale_log2, i.e. when
+    // exp2 of a score relative to it would pass 2^kLazy; in between, p <= 2^kLazy
+    // and O needs no rescale. The final O / l is the same softmax.
+    constexpr float kLazy = 8.0f;
+    const float lazy_raw = kLazy / scale_log2;
+    float m_run = -INFINITY;
     float l_run = 0.f;         // partial row sum over this lane's keys
 
-    load_tile(0);
-    store_tile(0);
+    // Loads of key tile `tile` into kreg / vreg (unconditional; see above).
+#define H3_ATTN_LOAD_TILE(tile)                                                              \
+    {                                                                                        \
+        const int key0 = kv0 + (tile) * kBN;                                                 \
+        if (key0 + kBN <= kv1) {                                                             \
+            const uint16_t* kp = kthr + static_cast<int64_t>(key0 + k_r0) * ks;              \
+            _Pragma("unroll") for (int i = 0; i < K_PER_T; ++i)                              \
+                kreg[i] = *reinterpret_cast<const u32x4*>(kp + i * k_pass_stride);           \
+            const uint16_t* vp = vthr + static_cast<int64_t>(key0 + 4 * v_key4) * vs;        \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r)                                    \
+                vreg[r] = *reinterpret_cast<const u32x4*>(vp + r * vs);                      \
+        } else {                                                                             \
+            _Pragma("unroll") for (int i = 0; i < K_PER_T; ++i) {                            \
+                const int key = min(key0 + k_r0 + i * K_ROWS_PER_PASS, kv1 - 1);             \
+                kreg[i] = *reinterpret_cast<const u32x4*>(kthr + static_cast<int64_t>(key) * ks); \
+            }                                                                                \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                  \
+                const int key = min(key0 + 4 * v_key4 + r, kv1 - 1);                         \
+                vreg[r] = *reinterpret_cast<const u32x4*>(vthr + static_cast<int64_t>(key) * vs); \
+            }                                                                                \
+        }                                                                                    \
+    }
+
+    // K rows as they are; V transposed to V^T[d][key] (4 keys x 8 dims per
+    // thread: v_perm_b32 gathers the same dim of 4 keys into 8 bytes).
+#define H3_ATTN_STORE_TILE(buf)                                                              \
+    {                                                                                        \
+        uint16_t* kl_ = lds + (buf) * L::bufElems;                                           \
+        uint16_t* vl_ = kl_ + L::kElems;                                                     \
+        _Pragma("unroll") for (int i = 0; i < K_PER_T; ++i)                                  \
+            *reinterpret_cast<u32x4*>(kl_ + (k_r0 + i * K_ROWS_PER_PASS) * L::kStride + 8 * k_c) = kreg[i]; \
+        if (v_active) {                                                                      \
+            _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                  \
+                _Pragma("unroll") for (int hs = 0; hs < 2; ++hs) {                           \
+                    const uint32_t sel = hs ? 0x07060302u : 0x05040100u;                     \
+                    u32x2 t_;                                                                \
+                    t_.x = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);               \
+                    t_.y = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);               \
+                    *reinterpret_cast<u32x2*>(vl_ + (8 * v_dchunk + 2 * w + hs) * L::vStride + 4 * v_key4) = t_; \
+                }                                                                            \
+            }                                                                                \
+        }                                                                                    \
+    }
+
+    H3_ATTN_LOAD_TILE(0)
+    H3_ATTN_STORE_TILE(0)
     __syncthreads();
 
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
-        const bool has_next = tile + 1 < ntiles;
-        if (has_next) load_tile(tile + 1);
-
-        const uint16_t* kl = lds + buf * L::bufElems;
-        const uint16_t* vl = kl + L::kElems;
-
-        // S^T = K Q^T for keys [32b, 32b + 32) of the tile
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                Chunk16 kf;
-                kf.u = *reinterpret_cast<const uint4*>(kl + (32 * b + l32) * L::kStride + 16 * c + 8 * g);
-                sacc[b] = mfma32x32x16(kf.b, qf[c], sacc[b]);
-            }
-        }
-
-        // mask keys past the segment end (last tile only)
-        const int keys_left = len - tile * kBN;
-        if (keys_left < kBN) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= keys_left) sacc[b][r] = -INFINITY;
-                }
-        }
-
-        // online softmax (exp2 domain)
-        float mt = sacc[0][0];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[b][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = exp2f((m_run - m_new) * scale_log2);
-        const float mb = m_new * scale_log2;
-        m_run = m_new;
-
-        float psum = 0.f;
-        bf16x8 pf[2][2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = exp2f(fmaf(sacc[b][8 * t + e], scale_log2, -mb));
-                    psum += p[e];
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pf[b][t][e] = static_cast<__bf16>(p[e]);
-            }
-        }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-
-        // O^T += V^T P^T; k-step (b, t) covers keys 32b + 16t + [0, 16);
-        // lane half g supplies keys 4g + [0,4) and 8 + 4g + [0,4) of it,
-        // matching the rows the S^T accumulator gave this lane.
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const uint16_t* vrow = vl + (32 * db + l32) * L::vStride + 4 * g;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    Chunk16 vf;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 32 * b + 16 * t);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 32 * b + 16 * t + 8);
-                    vf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    oacc[db] = mfma32x32x16(vf.b, pf[b][t], oacc[db]);
-                }
-        }
-
-        if (has_next) store_tile(buf ^ 1);
+    for (int tile = 0; tile + 1 < ntiles; ++tile) {
+        H3_ATTN_LOAD_TILE(tile + 1)
+        const uint16_t* kl = lds + (tile & 1) * L::bufElems;
+        attn_tile<D, false>(kl, kl + L::kElems, qf, oacc, m_run, l_run, scale_log2, lazy_raw,
+                            kBN, l32, g);
+        H3_ATTN_STORE_TILE((tile & 1) ^ 1)
         __syncthreads();
     }
+    {
+        const int tile = ntiles - 1;
+        const uint16_t* kl = lds + (tile & 1) * L::bufElems;
+        const int keys_left = len - tile * kBN;
+        if (keys_left < kBN)
+            attn_tile<D, true>(kl, kl + L::kElems, qf, oacc, m_run, l_run, scale_log2, lazy_raw,
+                               keys_left, l32, g);
+        else
+            attn_tile<D, false>(kl, kl + L::kElems, qf, oacc, m_run, l_run, scale_log2, lazy_raw,
+                                kBN, l32, g);
+    }
+#undef H3_ATTN_LOAD_TILE
+#undef H3_ATTN_STORE_TILE
 
     // ---- normalise and store ----
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -159,6 +159,15 @@ def main():
     ws = torch.empty(blk.workspace_bytes(b, n), dtype=torch.uint8, device=dev)
     step = lambda: blk.forward(x, cond, cu_d, cu, grid_d, out=out, workspace=ws)
 
+    # Reference kernel for the HBM traffic counters: a plain 512 MiB device
+    # copy reads and writes exactly 512 MiB; the FETCH_SIZE / WRITE_SIZE it
+    # shows under rocprofv3 calibrates the counters of the attention kernel.
+    copy_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+    copy_src.fill_(1)
+    copy_dst.copy_(copy_src)
+    del copy_src, copy_dst
+
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
