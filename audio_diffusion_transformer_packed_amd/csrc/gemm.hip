@@ -11,146 +11,202 @@
 // so both operands are contiguous along K). fp32 accumulation; the epilogue
 // works on the fp32 accumulator and rounds once to bf16.
 //
-// Tiling (CDNA4): 128 x 128 x 64 workgroup tile, four waves in a 2 x 2
-// arrangement, each wave 64 x 64 = 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.
-// A and W tiles are staged in LDS (rows padded to 72 elements), double
-// buffered, with the next K-step's global loads in flight during the
-// current step. For SwiGLU the W tile interleaves 32-row blocks of Wg and Wu
-// so that each wave holds the gate and up accumulators of the same outputs.
+// Design (CDNA4):
+//  * 256 x 256 output tile per workgroup, K step 64, four waves of 128 x 128
+//    (4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 accumulators per lane);
+//  * the MFMA computes C^T = W a^T: the W tile is the A operand, the
+//    activation tile the B operand, so each lane ends up owning one output
+//    row and four consecutive output columns per register group (8-byte
+//    stores, no LDS round trip in the epilogue);
+//  * tiles move global -> LDS with global_load_lds_dwordx4 (no staging
+//    registers), double buffered; each wave instruction fills 1 KB = 8 rows
+//    of 64 bf16, with the 16-byte chunks of row r stored at chunk ^ (r % 8) so
+//    the fragment reads (32 rows x one chunk) spread over all LDS banks;
+//  * SwiGLU: the W tile interleaves 32-row blocks of Wg and Wu, so the gate
+//    and up accumulators of one output sit in the same lane;
+//  * workgroup ids are remapped so each XCD (ids are dealt round-robin over
+//    the 8 XCDs) gets a contiguous run of tiles, grouped 4 row-panels at a
+//    time, so concurrently running tiles share A and W panels in that XCD's L2.
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
 namespace h3 {
 namespace {
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;      // rows of the W tile
+constexpr int kBM = 256;          // activation rows per tile
+constexpr int kBN = 256;          // W rows per tile (output columns, or gate+up pairs)
 constexpr int kBK = 64;
-constexpr int kStride = kBK + 8;
 constexpr int kThreads = 256;
-constexpr int kTileElems = (kBM + kBN) * kStride;
+constexpr int kTileBytes = kBM * kBK * 2;      // 32 KB per operand tile
+constexpr int kStageBytes = 2 * kTileBytes;    // W tile then activation tile
+constexpr int kGroupM = 4;
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                              reinterpret_cast<uintptr_t>(lds_dst)),
+                                     16, 0, 0);
+}
+
+// Tile id -> (row panel, column panel), XCD-aware and grouped.
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int mt, int nt, int& tm, int& tn) {
+    // contiguous run per XCD (block b runs on XCD b % 8); XCD x owns
+    // per + (x < rem) consecutive tiles starting at x * per + min(x, rem)
+    const int per = nblocks / kXcds, rem = nblocks % kXcds;
+    const int xcd = bid % kXcds;
+    const int t = xcd * per + min(xcd, rem) + bid / kXcds;
+    const int group = t / (kGroupM * nt);
+    const int first_m = group * kGroupM;
+    const int gm = min(kGroupM, mt - first_m);
+    const int w = t - group * kGroupM * nt;
+    tm = first_m + w % gm;
+    tn = w / gm;
+}
 
 template <int EPI>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ W2, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     const uint16_t* __restrict__ res, const float* __restrict__ gate, int64_t gate_stride,
-    const int32_t* __restrict__ cu, int num_seqs) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kTileElems];
+    const int32_t* __restrict__ cu, int num_seqs, int mtiles, int ntiles) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
-    const int wm = wave & 1;
-    const int wn = wave >> 1;
+    const int wn = wave >> 1;     // W rows 128 wn .. (output columns)
+    const int wm = wave & 1;      // activation rows 128 wm ..
 
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, mtiles, ntiles, tm, tn);
+    const int64_t m0 = static_cast<int64_t>(tm) * kBM;
     constexpr int OUT_N = EPI == kEpiSwiGLU ? kBN / 2 : kBN;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * OUT_N;
+    const int64_t n0 = static_cast<int64_t>(tn) * OUT_N;
 
-    // Global source row of each staged tile row handled by this thread.
-    // Chunk ci = tid + 256 i covers tile row ci / 8, 16-byte column ci % 8.
-    const uint16_t* a_src[4];
-    const uint16_t* w_src[4];
-    bool a_ok[4];
+    // ---- per-lane DMA sources: wave w fills tile rows 64 w + 8 i + lane/8 ----
+    const int rl = lane >> 3;
+    const int chunk = (lane & 7) ^ rl;            // row % 8 == rl for these rows
+    const uint16_t* asrc[8];
+    const uint16_t* wsrc[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ci = tid + i * kThreads;
-        const int r = ci >> 3;
-        const int c = ci & 7;
-        const int64_t am = m0 + r;
-        a_ok[i] = am < M;
-        a_src[i] = A + (a_ok[i] ? am : 0) * K + 8 * c;
+    for (int i = 0; i < 8; ++i) {
+        const int r = 64 * wave + 8 * i + rl;     // tile row
+        int64_t am = m0 + r;
+        if (am >= M) am = M - 1;                  // clamped rows are computed, never stored
+        asrc[i] = A + am * K + 8 * chunk;
+        // W rows past N are clamped the same way (their columns are not stored)
         if (EPI == kEpiSwiGLU) {
-            const int part = (r & 63) >> 5;         // 0: gate rows, 1: up rows
-            const int64_t wrow = n0 + 32 * (r >> 6) + (r & 31);
-            w_src[i] = (part ? W2 : W) + wrow * K + 8 * c;
+            // W rows: [128 wn' + 32 bj + j]: bj even -> gate, odd -> up, for output
+            // column n0 + 64 wn' + 32 (bj / 2) + j
+            const int wnp = r >> 7, bj = (r >> 5) & 3, j = r & 31;
+            const int64_t col = min(n0 + 64 * wnp + 32 * (bj >> 1) + j, N - 1);
+            wsrc[i] = ((bj & 1) ? W2 : W) + col * K + 8 * chunk;
         } else {
-            w_src[i] = W + (n0 + r) * K + 8 * c;
+            wsrc[i] = W + min(n0 + r, N - 1) * K + 8 * chunk;
         }
     }
 
-    uint4 areg[4], wreg[4];
-    auto load = [&](int64_t k0) {
+    auto issue = [&](int stage, int64_t k0) __attribute__((always_inline)) {
+        char* base = smem + stage * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            areg[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-            wreg[i] = *reinterpret_cast<const uint4*>(w_src[i] + k0);
-        }
-    };
-    auto store = [&](int buf) {
-        uint16_t* al = lds + buf * kTileElems;
-        uint16_t* wl = al + kBM * kStride;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ci = tid + i * kThreads;
-            const int r = ci >> 3;
-            const int c = ci & 7;
-            *reinterpret_cast<uint4*>(al + r * kStride + 8 * c) = areg[i];
-            *reinterpret_cast<uint4*>(wl + r * kStride + 8 * c) = wreg[i];
+        for (int i = 0; i < 8; ++i) {
+            lds_dma16(wsrc[i] + k0, base + (8 * wave + i) * 1024);
+            lds_dma16(asrc[i] + k0, base + kTileBytes + (8 * wave + i) * 1024);
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+    // fragment read offsets: row R (tile row), chunk c -> R * 128 + 16 * (c ^ (R % 8))
+    // rows used by this lane: 128 w* + 32 b + l32, so R % 8 == l32 % 8
+    const int rsw = l32 & 7;
+    const int wrow0 = (128 * wn + l32) * 128;
+    const int arow0 = (128 * wm + l32) * 128;
 
     const int64_t ksteps = K / kBK;
-    load(0);
-    store(0);
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int64_t kt = 0; kt < ksteps; ++kt) {
-        const int buf = static_cast<int>(kt & 1);
-        const bool has_next = kt + 1 < ksteps;
-        if (has_next) load((kt + 1) * kBK);
-        const uint16_t* al = lds + buf * kTileElems;
-        const uint16_t* wl = al + kBM * kStride;
+        const int stage = static_cast<int>(kt & 1);
+        if (kt + 1 < ksteps) issue(stage ^ 1, (kt + 1) * kBK);
+        const char* wt = smem + stage * kStageBytes;
+        const char* at = wt + kTileBytes;
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
-            Chunk16 af[2], bf[2];
+            const int off = 16 * ((2 * ks + g) ^ rsw);
+            bf16x8 wf[4], af[4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i].u = *reinterpret_cast<const uint4*>(al + (64 * wm + 32 * i + l32) * kStride + 16 * ks + 8 * g);
-                bf[i].u = *reinterpret_cast<const uint4*>(wl + (64 * wn + 32 * i + l32) * kStride + 16 * ks + 8 * g);
+            for (int b = 0; b < 4; ++b) {
+                wf[b] = *reinterpret_cast<const bf16x8*>(wt + wrow0 + b * 32 * 128 + off);
+                af[b] = *reinterpret_cast<const bf16x8*>(at + arow0 + b * 32 * 128 + off);
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[i].b, bf[j].b, acc[i][j]);
+                for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mfma32x32x16(wf[bi], af[bj], acc[bi][bj]);
         }
-        if (has_next) store(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    // Epilogue. acc[i][j] register r holds row 64wm + 32i + 8(r/4) + 4g + r%4,
-    // column (of the W tile) 64wn + 32j + l32.
+    // ---- epilogue: acc[bi][bj] register 4 q + e holds output row
+    // m = m0 + 128 wm + 32 bj + l32, W-tile row 128 wn + 32 bi + 8 q + 4 g + e ----
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int bj = 0; bj < 4; ++bj) {
+        const int64_t m = m0 + 128 * wm + 32 * bj + l32;
+        if (m >= M) continue;
+        int seg = 0;
+        if (EPI == kEpiGatedResidual && num_seqs > 1) seg = find_segment(cu, num_seqs, m);
+        if (EPI == kEpiSwiGLU) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (m >= M) continue;
-            if (EPI == kEpiSwiGLU) {
-                const int64_t n = n0 + 32 * wn + l32;
-                const float gv = acc[i][0][r];
-                const float uv = acc[i][1][r];
-                const float s = gv / (1.0f + __expf(-gv));
-                Y[m * N + n] = f2bf(s * uv);
-            } else {
+            for (int pb = 0; pb < 2; ++pb) {           // (gate, up) block pairs
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int64_t n = n0 + 64 * wn + 32 * j + l32;
-                    if (EPI == kEpiStore) {
-                        Y[m * N + n] = f2bf(acc[i][j][r]);
-                    } else {
-                        const int seg = num_seqs == 1 ? 0 : find_segment(cu, num_seqs, m);
-                        const float gt = gate[static_cast<int64_t>(seg) * gate_stride + n];
-                        Y[m * N + n] = f2bf(fmaf(gt, acc[i][j][r], bf2f(res[m * N + n])));
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = n0 + 64 * wn + 32 * pb + 8 * q + 4 * g;
+                    if (n >= N) continue;                // N % 4 == 0: groups are all in or out
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float gv = acc[2 * pb][bj][4 * q + e];
+                        const float uv = acc[2 * pb + 1][bj][4 * q + e];
+                        o[e] = gv / (1.0f + __expf(-gv)) * uv;
                     }
+                    u32x2 w;
+                    w.x = pack_bf16x2(o[0], o[1]);
+                    w.y = pack_bf16x2(o[2], o[3]);
+                    *reinterpret_cast<u32x2*>(Y + m * N + n) = w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int bi = 0; bi < 4; ++bi) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = n0 + 128 * wn + 32 * bi + 8 * q + 4 * g;
+                    if (n >= N) continue;
+                    float o[4];
+                    if (EPI == kEpiStore) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[e] = acc[bi][bj][4 * q + e];
+                    } else {
+                        const u32x2 rv = *reinterpret_cast<const u32x2*>(res + m * N + n);
+                        const f32x4 gt = *reinterpret_cast<const f32x4*>(gate + seg * gate_stride + n);
+                        const float rr[4] = {__uint_as_float(rv.x << 16), __uint_as_float(rv.x & 0xffff0000u),
+                                             __uint_as_float(rv.y << 16), __uint_as_float(rv.y & 0xffff0000u)};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[e] = fmaf(gt[e], acc[bi][bj][4 * q + e], rr[e]);
+                    }
+                    u32x2 w;
+                    w.x = pack_bf16x2(o[0], o[1]);
+                    w.y = pack_bf16x2(o[2], o[3]);
+                    *reinterpret_cast<u32x2*>(Y + m * N + n) = w;
                 }
             }
         }
@@ -165,19 +221,21 @@ hipError_t launch_gemm(int epilogue, const uint16_t* a, const uint16_t* w, const
                        int num_seqs, hipStream_t stream) {
     if (m == 0) return hipSuccess;
     const int out_n = epilogue == kEpiSwiGLU ? kBN / 2 : kBN;
-    const dim3 grid(static_cast<unsigned>(n / out_n), static_cast<unsigned>((m + kBM - 1) / kBM));
+    const int mt = static_cast<int>((m + kBM - 1) / kBM);
+    const int nt = static_cast<int>((n + out_n - 1) / out_n);
+    const dim3 grid(static_cast<unsigned>(mt * nt));
     switch (epilogue) {
         case kEpiStore:
             hipLaunchKernelGGL(gemm_kernel<kEpiStore>, grid, dim3(kThreads), 0, stream, a, w, w2,
-                               y, m, n, k, res, gate, gate_stride, cu, num_seqs);
+                               y, m, n, k, res, gate, gate_stride, cu, num_seqs, mt, nt);
             break;
         case kEpiSwiGLU:
             hipLaunchKernelGGL(gemm_kernel<kEpiSwiGLU>, grid, dim3(kThreads), 0, stream, a, w, w2,
-                               y, m, n, k, res, gate, gate_stride, cu, num_seqs);
+                               y, m, n, k, res, gate, gate_stride, cu, num_seqs, mt, nt);
             break;
         default:
             hipLaunchKernelGGL(gemm_kernel<kEpiGatedResidual>, grid, dim3(kThreads), 0, stream, a,
-                               w, w2, y, m, n, k, res, gate, gate_stride, cu, num_seqs);
+                               w, w2, y, m, n, k, res, gate, gate_stride, cu, num_seqs, mt, nt);
             break;
     }
     return hipGetLastError();

@@ -158,7 +158,8 @@ h3_status check_gemm_shape(int64_t m, int64_t n, int64_t k, int64_t n_mult) {
                                                (long long)m, (long long)n, (long long)k);
     if (n % n_mult) return fail(H3_ERR_UNSUPPORTED, "n=%lld must be a multiple of %lld", (long long)n, (long long)n_mult);
     if (k % 64) return fail(H3_ERR_UNSUPPORTED, "k=%lld must be a multiple of 64", (long long)k);
-    if ((m + 127) / 128 > 65535) return fail(H3_ERR_UNSUPPORTED, "m=%lld too large", (long long)m);
+    if (((m + 255) / 256) * ((n + 127) / 128) > INT32_MAX / 2)
+        return fail(H3_ERR_UNSUPPORTED, "m=%lld, n=%lld: too many tiles", (long long)m, (long long)n);
     return ok();
 }
 
@@ -382,12 +383,13 @@ H3_API h3_status h3_adaln_rmsnorm_modulate(const void* x, void* h_out, const flo
 
 H3_API h3_status h3_linear_bf16(const void* a, const void* w, void* y, int64_t m, int64_t n,
                                 int64_t k, void* hip_stream) {
-    h3_status st = check_gemm_shape(m, n, k, 128);
+    h3_status st = check_gemm_shape(m, n, k, 8);
     if (st != H3_OK) return st;
     if (m == 0) return ok();
     if (!a || !w || !y) return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
-    if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) & 15)
-        return fail(H3_ERR_UNSUPPORTED, "a/w must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) & 15 ||
+        reinterpret_cast<uintptr_t>(y) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "a/w must be 16-byte and y 8-byte aligned");
     hipError_t e = h3::launch_gemm(h3::kEpiStore, static_cast<const uint16_t*>(a),
                                    static_cast<const uint16_t*>(w), nullptr,
                                    static_cast<uint16_t*>(y), m, n, k, nullptr, nullptr, 0,
@@ -399,13 +401,13 @@ H3_API h3_status h3_linear_bf16(const void* a, const void* w, void* y, int64_t m
 H3_API h3_status h3_linear_swiglu_bf16(const void* a, const void* w_gate, const void* w_up,
                                        void* y, int64_t m, int64_t n, int64_t k,
                                        void* hip_stream) {
-    h3_status st = check_gemm_shape(m, n, k, 64);
+    h3_status st = check_gemm_shape(m, n, k, 8);
     if (st != H3_OK) return st;
     if (m == 0) return ok();
     if (!a || !w_gate || !w_up || !y) return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
     if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w_gate) |
-         reinterpret_cast<uintptr_t>(w_up)) & 15)
-        return fail(H3_ERR_UNSUPPORTED, "a/w_gate/w_up must be 16-byte aligned");
+         reinterpret_cast<uintptr_t>(w_up)) & 15 || reinterpret_cast<uintptr_t>(y) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "a/w_gate/w_up must be 16-byte and y 8-byte aligned");
     hipError_t e = h3::launch_gemm(h3::kEpiSwiGLU, static_cast<const uint16_t*>(a),
                                    static_cast<const uint16_t*>(w_gate),
                                    static_cast<const uint16_t*>(w_up), static_cast<uint16_t*>(y),
@@ -421,7 +423,7 @@ H3_API h3_status h3_linear_gated_residual_bf16(const void* a, const void* w, con
                                                const int32_t* cu_seqlens_dev,
                                                const int32_t* cu_seqlens_host,
                                                int32_t num_seqs, void* hip_stream) {
-    h3_status st = check_gemm_shape(m, n, k, 128);
+    h3_status st = check_gemm_shape(m, n, k, 8);
     if (st != H3_OK) return st;
     if (m > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "m too large");
     st = check_cu(cu_seqlens_host, num_seqs, static_cast<int32_t>(m));
@@ -430,8 +432,11 @@ H3_API h3_status h3_linear_gated_residual_bf16(const void* a, const void* w, con
     if (!a || !w || !res || !gate || !y || !cu_seqlens_dev)
         return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
     if (gate_row_stride < n) return fail(H3_ERR_INVALID_ARGUMENT, "gate_row_stride < n");
-    if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) & 15)
-        return fail(H3_ERR_UNSUPPORTED, "a/w must be 16-byte aligned");
+    if (gate_row_stride & 3) return fail(H3_ERR_UNSUPPORTED, "gate_row_stride must be a multiple of 4");
+    if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w) |
+         reinterpret_cast<uintptr_t>(gate)) & 15 ||
+        (reinterpret_cast<uintptr_t>(res) | reinterpret_cast<uintptr_t>(y)) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "a/w/gate must be 16-byte and res/y 8-byte aligned");
     hipError_t e = h3::launch_gemm(h3::kEpiGatedResidual, static_cast<const uint16_t*>(a),
                                    static_cast<const uint16_t*>(w), nullptr,
                                    static_cast<uint16_t*>(y), m, n, k,
@@ -474,7 +479,7 @@ h3_status check_dims(const h3_dit_dims* d) {
                     d->num_heads * d->head_dim);
     if (d->hidden % 512 || d->hidden > 8192)
         return fail(H3_ERR_UNSUPPORTED, "hidden=%d must be a multiple of 512 up to 8192", d->hidden);
-    if (d->ffn_dim % 128) return fail(H3_ERR_UNSUPPORTED, "ffn_dim=%d must be a multiple of 128", d->ffn_dim);
+    if (d->ffn_dim % 64) return fail(H3_ERR_UNSUPPORTED, "ffn_dim=%d must be a multiple of 64", d->ffn_dim);
     h3_status st = check_split(d->rope_split, d->head_dim);
     if (st != H3_OK) return st;
     if (!(d->rope_theta > 0.f) || isinf(d->rope_theta))

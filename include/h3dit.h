@@ -215,7 +215,8 @@ H3_API h3_status h3_adaln_rmsnorm_modulate(const void* x, void* h_out, const flo
  *
  * a: bf16 [m, k] (row stride k); weights bf16 [n, k]; output bf16 [m, n].
  * fp32 accumulation, one bf16 rounding at the end. m >= 0; n a multiple of
- * 128 (64 for SwiGLU), k a multiple of 64.
+ * 8, k a multiple of 64. a and the weights 16-byte aligned, y and res 8-byte
+ * aligned, gate 16-byte aligned with gate_row_stride a multiple of 4.
  *   h3_linear_bf16:              y = a . W^T
  *   h3_linear_swiglu_bf16:       y = silu(a . W_gate^T) * (a . W_up^T),
  *                                silu(z) = z / (1 + e^-z)
@@ -252,7 +253,7 @@ H3_API h3_status h3_linear_gated_residual_bf16(const void* a, const void* w, con
  * single-stream pre-norm AdaLN-Zero block; cond is one bf16 vector of
  * `hidden` per segment (request). Every intermediate is stored in bf16
  * (mod in fp32). x, x_out: bf16 [total_tokens, hidden] (may not alias).
- * hidden = num_heads * head_dim; ffn_dim a multiple of 128.
+ * hidden = num_heads * head_dim; ffn_dim a multiple of 64.
  * ---------------------------------------------------------------------- */
 typedef struct {
     int32_t hidden, num_heads, head_dim, ffn_dim;

@@ -92,18 +92,20 @@ def test_adaln_multi_segment(dev, ops, c):
     compare(to_np(h), ref, f"adaln C={c}")
 
 
-@pytest.mark.parametrize("m", [1, 300, 1000])
-def test_linear_store(dev, ops, m):
-    announce(f"linear store m={m}")
-    n, k = 384, 512
+@pytest.mark.parametrize("m,n", [(1, 384), (300, 384), (1000, 384), (513, 264), (257, 8)])
+def test_linear_store(dev, ops, m, n):
+    """Ragged in both tile dimensions (256 x 256 tiles)."""
+    announce(f"linear store m={m} n={n}")
+    k = 512
     a, w = _bf((m, k), 50), _bf((n, k), 51, 0.05)
     y = ops.linear(to_dev_bf16(a, dev), to_dev_bf16(w, dev))
-    compare(to_np(y), a.f32.astype(np.float64) @ w.f32.astype(np.float64).T, f"linear m={m}")
+    compare(to_np(y), a.f32.astype(np.float64) @ w.f32.astype(np.float64).T, f"linear m={m} n={n}")
 
 
-def test_linear_swiglu(dev, ops):
-    announce("linear swiglu")
-    m, n, k = 333, 256, 640
+@pytest.mark.parametrize("m,n", [(333, 256), (600, 200)])
+def test_linear_swiglu(dev, ops, m, n):
+    announce(f"linear swiglu m={m} n={n}")
+    k = 640
     a = _bf((m, k), 52)
     wg, wu = _bf((n, k), 53, 0.05), _bf((n, k), 54, 0.05)
     y = ops.linear_swiglu(to_dev_bf16(a, dev), to_dev_bf16(wg, dev), to_dev_bf16(wu, dev))
@@ -113,11 +115,11 @@ def test_linear_swiglu(dev, ops):
 def test_linear_gated_residual_multi_segment(dev, ops):
     import torch
     announce("linear gated residual, 3 segments")
-    lens = [100, 0, 157]
+    lens = [100, 0, 157, 300]
     cu = h3synth.cu_from_lengths(lens)
-    m, n, k = int(cu[-1]), 256, 384
+    m, n, k = int(cu[-1]), 392, 384
     a, w, res = _bf((m, k), 55), _bf((n, k), 56, 0.05), _bf((m, n), 57)
-    gate = np.random.default_rng(58).standard_normal((3, 6 * n)).astype(np.float32)
+    gate = np.random.default_rng(58).standard_normal((4, 6 * n)).astype(np.float32)
     gate_t = torch.from_numpy(gate).to(dev)
     y = ops.linear_gated_residual(to_dev_bf16(a, dev), to_dev_bf16(w, dev), to_dev_bf16(res, dev),
                                   gate_t[:, 2 * n:3 * n], to_dev_i32(cu, dev), cu)

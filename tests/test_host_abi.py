@@ -149,7 +149,7 @@ def test_op_argument_errors(lib):
     assert lib.h3_linear_bf16(X, X, X, 10, 128, 60, None) == L.H3_ERR_UNSUPPORTED
     assert lib.h3_linear_bf16(X, X, X, -1, 128, 64, None) == L.H3_ERR_INVALID_ARGUMENT
     assert lib.h3_linear_bf16(X, X, X, 0, 128, 64, None) == L.H3_OK
-    assert lib.h3_linear_swiglu_bf16(X, X, X, X, 10, 96, 64, None) == L.H3_ERR_UNSUPPORTED
+    assert lib.h3_linear_swiglu_bf16(X, X, X, X, 10, 90, 64, None) == L.H3_ERR_UNSUPPORTED
     assert lib.h3_linear_gated_residual_bf16(X, X, X, X, 128, X, 11, 128, 64, X, p, 1, None) == L.H3_ERR_INVALID_ARGUMENT
     assert lib.h3_linear_gated_residual_bf16(X, X, X, X, 64, X, 10, 128, 64, X, p, 1, None) == L.H3_ERR_INVALID_ARGUMENT
 
