@@ -10,16 +10,24 @@
 //  * one workgroup per work item (head, segment, 128-row query tile), four
 //    waves of 32 query rows each; the work list comes from the bookkeeping
 //    kernel, so no padded token is ever loaded or computed;
-//  * the scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: each lane then owns one query row (lane % 32)
-//    and 16 of every 32 keys, so the row max and row sum are lane-local
-//    apart from one exchange with the lane 32 away;
-//  * O^T = V^T P^T: P stays in registers (converted to bf16 in the MFMA B
-//    layout), V^T is read from LDS;
-//  * K and V^T tiles of 64 keys are staged in LDS, double buffered, with the
-//    next tile's global loads in flight during the current tile's math; one
-//    barrier per key tile;
-//  * online softmax in the exp2 domain, fp32 accumulation.
+//  * scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: each lane owns one query row (lane % 32) and
+//    16 of every 32 keys, so row statistics are lane-local plus one exchange
+//    with the lane 32 away;
+//  * O^T = V^T P^T: P stays in registers, converted to bf16 directly in the
+//    MFMA operand layout; V^T fragments come from row-major V in LDS through
+//    ds_read_b64_tr_b16 (transposing 16-lane read);
+//  * K and V tiles of 64 keys move global -> LDS with global_load_lds_dwordx4
+//    (no staging registers), double buffered, with XOR-swizzled 16-byte
+//    chunks so both fragment reads are free of bank conflicts;
+//  * each key tile: S^T MFMAs, softmax, P V MFMAs, while the next tile's K
+//    and V stream into the other LDS stage; two waves per SIMD (two
+//    workgroups per CU) overlap one wave's softmax with the other's MFMAs;
+//  * softmax in the exp2 domain with a reference max that only moves when a
+//    lane's partial sum of exp2 values exceeds 2^16 (or is infinite):
+//    then the tile's true max is taken, O and l are rescaled and the tile's
+//    p recomputed. Between such events p <= 2^16 and O is never touched; the
+//    final O / l is the same softmax.
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -30,96 +38,36 @@ constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;  // four waves
 
 template <int D>
-struct Lds {
-    static constexpr int kStride = D + 8;        // K row: D dims + pad (bf16 elements)
-    static constexpr int vStride = kBN + 8;      // V^T row: 64 keys + pad
-    static constexpr int kElems = kBN * kStride;
-    static constexpr int vElems = D * vStride;
-    static constexpr int bufElems = kElems + vElems;
+struct Cfg {
+    static constexpr int RB = D * 2;               // bytes per K / V row in LDS
+    static constexpr int CPR = D / 8;              // 16-byte chunks per row
+    static constexpr int RPI = 1024 / RB;          // rows per 1 KB DMA instruction
+    static constexpr int NI = kBN / RPI / 4;       // DMA instructions per wave per operand
+    static constexpr int TILE = kBN * RB;          // bytes per K or V tile
+    static constexpr int KC = D / 16;              // MFMA k-steps over the head dim
+    static constexpr int DB = D / 32;              // 32-wide output blocks
 };
 
-// One 64-key tile for one wave's 32 query rows: S^T = K Q^T, online softmax
-// (lazy max, exp2 domain), O^T += V^T P^T. With MASK, keys at or past
-// keys_left (the segment end) are excluded.
-template <int D, bool MASK>
-__device__ __forceinline__ void attn_tile(const uint16_t* __restrict__ kl,
-                                          const uint16_t* __restrict__ vl,
-                                          const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
-                                          float& m_run, float& l_run, float scale_log2,
-                                          float lazy_raw, int keys_left, int l32, int g) {
-    using L = Lds<D>;
-    constexpr int KC = D / 16;
-    constexpr int DB = D / 32;
+// Chunk swizzles (physical chunk = logical chunk ^ swizzle(row)).
+// K: fragment reads take one chunk of 32 consecutive rows; row % CPR spreads them.
+// V: a transposing read takes 4 chunks (64 B) of 8 consecutive rows; the
+// swizzle moves neighbouring rows to different 64-byte quarters.
+template <int D> __device__ __forceinline__ int kswz(int r) { return r % (D / 8); }
+template <int D> __device__ __forceinline__ int vswz(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
-    // S^T = K Q^T for keys [32b, 32b + 32) of the tile
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(kl + (32 * b + l32) * L::kStride + 16 * c + 8 * g);
-            sacc[b] = mfma32x32x16(__builtin_bit_cast(bf16x8, kf), qf[c], sacc[b]);
-        }
-    }
-    if (MASK) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (key >= keys_left) sacc[b][r] = -INFINITY;
-            }
-    }
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                              reinterpret_cast<uintptr_t>(lds_dst)),
+                                     16, 0, 0);
+}
 
-    float mt = sacc[0][0];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(sacc[0][r], sacc[1][r]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    if (__any(mt > m_run + lazy_raw)) {       // wave-uniform, rare after the first tiles
-        // keeps this block a real branch (not if-converted into 64 multiplies
-        // by a selected alpha on every tile)
-        asm volatile("" ::: "memory");
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    }
-    const float mb = m_run * scale_log2;
-
-    float psum = 0.f;
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][8 * t + e], scale_log2, -mb));
-                psum += p;
-                pf[b][t][e] = static_cast<__bf16>(p);
-            }
-        }
-    }
-    l_run += psum;
-
-    // O^T += V^T P^T; k-step (b, t) covers keys 32b + 16t + [0, 16); lane half
-    // g supplies keys 4g + [0,4) and 8 + 4g + [0,4) of it, the rows the S^T
-    // accumulator gave this lane.
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        const uint16_t* vrow = vl + (32 * db + l32) * L::vStride + 4 * g;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 32 * b + 16 * t);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32 * b + 16 * t + 8);
-                const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
-                oacc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, vf), pf[b][t], oacc[db]);
-            }
-    }
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(reinterpret_cast<uintptr_t>(p)));
+    return __builtin_bit_cast(u32x2, v);
 }
 
 template <int D>
@@ -128,16 +76,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int64_t qs, int64_t ks,
     int64_t vs, int64_t os, const int32_t* __restrict__ cu, const int4* __restrict__ items,
     int num_seqs, int total_tokens, int num_heads, float scale_log2) {
-    using L = Lds<D>;
-    constexpr int KC = D / 16;                   // MFMA k-steps over the head dim
-    constexpr int DB = D / 32;                   // 32-wide output blocks over the head dim
-    constexpr int K_CHUNKS = kBN * D / 8;        // 16-byte chunks per K tile
-    constexpr int K_PER_T = K_CHUNKS / kThreads; // per thread
-    constexpr int V_GROUPS = (kBN / 4) * (D / 8);// (4 keys x 8 dims) groups per V tile
-    static_assert(K_CHUNKS % kThreads == 0, "K tile split");
-    static_assert(V_GROUPS <= kThreads, "V tile split");
+    using C = Cfg<D>;
+    constexpr int KC = C::KC, DB = C::DB, RB = C::RB, CPR = C::CPR;
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::bufElems];
+    // K stage 0, K stage 1, V stage 0, V stage 1
+    __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
 
     const int4 it = items[blockIdx.x];
     const int head = it.x, seg = it.y, q0 = it.z, qlen = it.w;
@@ -149,7 +92,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const int ntiles = (len + kBN - 1) / kBN;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
@@ -168,107 +111,205 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         }
     }
 
-    // ---- global -> register staging of one K/V tile ----
-    // Every load is unconditional: rows past the segment end are clamped to
-    // its last row (finite data of this segment); their scores are masked to
-    // -inf in the last tile, so they contribute exactly zero.
-    constexpr int K_ROWS_PER_PASS = kThreads / (D / 8);
-    const int k_r0 = tid / (D / 8);
-    const int k_c = tid % (D / 8);
-    const int vg = tid;                          // V group of this thread
-    const int v_key4 = vg % (kBN / 4);
-    const int v_dchunk = vg / (kBN / 4);
-    const bool v_active = vg < V_GROUPS;
-    const uint16_t* kthr = k + static_cast<int64_t>(head) * D + 8 * k_c;
-    const uint16_t* vthr = v + static_cast<int64_t>(head) * D + 8 * (v_active ? v_dchunk : 0);
-    const int64_t k_pass_stride = static_cast<int64_t>(K_ROWS_PER_PASS) * ks;
+    // ---- DMA sources: instruction i of a tile fills rows RPI*i .. RPI*i+RPI-1;
+    // this wave issues i = NI*wave + j; lane -> row RPI*i + lane/CPR, physical
+    // chunk lane % CPR, which holds logical chunk (lane % CPR) ^ swizzle(row).
+    // Rows past the segment end are clamped to its last row (finite data of
+    // this segment); their scores are masked to -inf in the last tile.
+    const uint16_t* kbase = k + static_cast<int64_t>(head) * D;
+    const uint16_t* vbase = v + static_cast<int64_t>(head) * D;
+    int drow[C::NI];
+    uint32_t koffb[C::NI], voffb[C::NI];      // byte offsets from the tile's first row
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) {
+        drow[j] = C::RPI * (C::NI * wave + j) + lane / CPR;
+        koffb[j] = static_cast<uint32_t>((drow[j] * ks + 8 * ((lane % CPR) ^ kswz<D>(drow[j]))) * 2);
+        voffb[j] = static_cast<uint32_t>((drow[j] * vs + 8 * ((lane % CPR) ^ vswz<D>(drow[j]))) * 2);
+    }
+    // Full tiles: wave-uniform row base (scalar) + per-lane 32-bit offset.
+    // The last, partial tile clamps rows past the segment end to its last row.
+    auto dma = [&](const uint16_t* base, int64_t stride, const uint32_t (&offb)[C::NI], int tile,
+                   char* dst) __attribute__((always_inline)) {
+        const int key0 = kv0 + tile * kBN;
+        if (key0 + kBN <= kv1) {
+            const char* rb = reinterpret_cast<const char*>(base + static_cast<int64_t>(key0) * stride);
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j) lds_dma16(rb + offb[j], dst + (C::NI * wave + j) * 1024);
+        } else {
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j) {
+                const int key = min(key0 + drow[j], kv1 - 1);
+                const uint32_t col = offb[j] - static_cast<uint32_t>(drow[j] * stride * 2);
+                lds_dma16(reinterpret_cast<const char*>(base + static_cast<int64_t>(key) * stride) + col,
+                          dst + (C::NI * wave + j) * 1024);
+            }
+        }
+    };
+    auto dma_k = [&](int tile, int stage) __attribute__((always_inline)) {
+        dma(kbase, ks, koffb, tile, smem + stage * C::TILE);
+    };
+    auto dma_v = [&](int tile, int stage) __attribute__((always_inline)) {
+        dma(vbase, vs, voffb, tile, smem + (2 + stage) * C::TILE);
+    };
 
-    u32x4 kreg[K_PER_T];
-    u32x4 vreg[4];
+    // ---- LDS read offsets ----
+    // K fragment (A operand of S^T): rows 32b + l32, logical chunk 2c + g.
+    const int ksw = kswz<D>(l32);
+    int koff[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) koff[c] = l32 * RB + 16 * ((2 * c + g) ^ ksw);
+    // V^T fragment by transposing read: in each 16-lane group, lane 4e + qq
+    // addresses V[row0 + e][dbase + 4 qq] with row0 = 32b + 16t + 8 half + 4g
+    // and dbase = 32 db + 16 h16; lane j of the group then receives
+    // V[row0 + e][dbase + j] for e = 0..3.
+    const int e4 = (lane & 15) >> 2;
+    const int qq = lane & 3;
+    const int h16 = (lane >> 4) & 1;
+    const int vsw = vswz<D>(4 * g + e4);
+    int voff[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        voff[db] = (4 * g + e4) * RB + 16 * ((4 * db + 2 * h16 + (qq >> 1)) ^ vsw) + 8 * (qq & 1);
 
     f32x16 oacc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
-    // Reference max of this lane's query row (raw score units). It only moves
-    // when a tile's max exceeds it by more than kLazy / scale_log2, i.e. when
-    // exp2 of a score relative to it would pass 2^kLazy; in between, p <= 2^kLazy
-    // and O needs no rescale. The final O / l is the same softmax.
-    constexpr float kLazy = 8.0f;
-    const float lazy_raw = kLazy / scale_log2;
-    float m_run = -INFINITY;
+    // reference max (raw score units) of this lane's row; a large finite start
+    // value makes the first tile trigger through an infinite sum, never NaN
+    float m_run = -1e30f;
     float l_run = 0.f;         // partial row sum over this lane's keys
+    constexpr float kTrig = 65536.0f;
 
-    // Loads of key tile `tile` into kreg / vreg (unconditional; see above).
-#define H3_ATTN_LOAD_TILE(tile)                                                              \
-    {                                                                                        \
-        const int key0 = kv0 + (tile) * kBN;                                                 \
-        if (key0 + kBN <= kv1) {                                                             \
-            const uint16_t* kp = kthr + static_cast<int64_t>(key0 + k_r0) * ks;              \
-            _Pragma("unroll") for (int i = 0; i < K_PER_T; ++i)                              \
-                kreg[i] = *reinterpret_cast<const u32x4*>(kp + i * k_pass_stride);           \
-            const uint16_t* vp = vthr + static_cast<int64_t>(key0 + 4 * v_key4) * vs;        \
-            _Pragma("unroll") for (int r = 0; r < 4; ++r)                                    \
-                vreg[r] = *reinterpret_cast<const u32x4*>(vp + r * vs);                      \
-        } else {                                                                             \
-            _Pragma("unroll") for (int i = 0; i < K_PER_T; ++i) {                            \
-                const int key = min(key0 + k_r0 + i * K_ROWS_PER_PASS, kv1 - 1);             \
-                kreg[i] = *reinterpret_cast<const u32x4*>(kthr + static_cast<int64_t>(key) * ks); \
-            }                                                                                \
-            _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                  \
-                const int key = min(key0 + 4 * v_key4 + r, kv1 - 1);                         \
-                vreg[r] = *reinterpret_cast<const u32x4*>(vthr + static_cast<int64_t>(key) * vs); \
-            }                                                                                \
-        }                                                                                    \
-    }
+    // S^T(tile) from K stage `stage`; each K fragment is read one MFMA ahead
+    auto qk = [&](int stage, f32x16 (&sc)[2]) __attribute__((always_inline)) {
+        const char* kl = smem + stage * C::TILE;
+        sc[0] = f32x16{};
+        sc[1] = f32x16{};
+        bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + koff[0]);
+#pragma unroll
+        for (int i = 0; i < 2 * KC; ++i) {
+            bf16x8 kn;
+            if (i + 1 < 2 * KC)
+                kn = *reinterpret_cast<const bf16x8*>(kl + 32 * ((i + 1) & 1) * RB + koff[(i + 1) >> 1]);
+            sc[i & 1] = mfma32x32x16(kf, qf[i >> 1], sc[i & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < 2 * KC) kf = kn;
+        }
+    };
 
-    // K rows as they are; V transposed to V^T[d][key] (4 keys x 8 dims per
-    // thread: v_perm_b32 gathers the same dim of 4 keys into 8 bytes).
-#define H3_ATTN_STORE_TILE(buf)                                                              \
-    {                                                                                        \
-        uint16_t* kl_ = lds + (buf) * L::bufElems;                                           \
-        uint16_t* vl_ = kl_ + L::kElems;                                                     \
-        _Pragma("unroll") for (int i = 0; i < K_PER_T; ++i)                                  \
-            *reinterpret_cast<u32x4*>(kl_ + (k_r0 + i * K_ROWS_PER_PASS) * L::kStride + 8 * k_c) = kreg[i]; \
-        if (v_active) {                                                                      \
-            _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                  \
-                _Pragma("unroll") for (int hs = 0; hs < 2; ++hs) {                           \
-                    const uint32_t sel = hs ? 0x07060302u : 0x05040100u;                     \
-                    u32x2 t_;                                                                \
-                    t_.x = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);               \
-                    t_.y = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);               \
-                    *reinterpret_cast<u32x2*>(vl_ + (8 * v_dchunk + 2 * w + hs) * L::vStride + 4 * v_key4) = t_; \
-                }                                                                            \
-            }                                                                                \
-        }                                                                                    \
-    }
+    // exp2 of score r of a tile against the current reference max
+    auto pexp = [&](const f32x16 (&s)[2], int r, float mb) __attribute__((always_inline)) {
+        return __builtin_amdgcn_exp2f(fmaf(s[r >> 4][r & 15], scale_log2, -mb));
+    };
+    // bf16 P in the B-operand layout: pf[b][t][e] = p of score 16 b + 8 t + e;
+    // the row sum accumulates the rounded pair (v_dot2_f32_bf16 against 1, 1),
+    // so l normalises exactly the weights that enter P V
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    auto put = [&](bf16x8 (&pf)[2][2], int r, float v0, float v1, float& sum) __attribute__((always_inline)) {
+        const bf16x2 pr = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
+        pf[r >> 4][(r >> 3) & 1][r & 7] = pr[0];
+        pf[r >> 4][(r >> 3) & 1][(r & 7) + 1] = pr[1];
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
+    };
 
-    H3_ATTN_LOAD_TILE(0)
-    H3_ATTN_STORE_TILE(0)
+    // plain exp / sum / bf16 of one tile's scores
+    auto softmax_exp = [&](const f32x16 (&s)[2], bf16x8 (&pf)[2][2], float& psum) __attribute__((always_inline)) {
+        const float mb = m_run * scale_log2;
+        psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; r += 2) {
+            put(pf, r, pexp(s, r, mb), pexp(s, r + 1, mb), psum);
+        }
+    };
+
+    // If any lane's sum exceeded 2^16 (a new max far above the reference, or
+    // the first tile), move the reference to the true max, rescale O and l,
+    // and redo the tile's p. Then accumulate l.
+    auto softmax_fix = [&](const f32x16 (&s)[2], bf16x8 (&pf)[2][2], float psum) __attribute__((always_inline)) {
+        if (__any(!(psum <= kTrig))) {            // wave-uniform
+            asm volatile("" ::: "memory");
+            float mt = s[0][0];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(s[0][r], s[1][r]));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            softmax_exp(s, pf, psum);
+        }
+        l_run += psum;
+    };
+
+    // O^T += V^T P^T from V stage `stage`; k-step (b, t) covers keys
+    // 32b + 16t + [0, 16): lane half g holds keys 4g + [0,4) and 8 + 4g + [0,4)
+    // of it (the S^T accumulator rows), the transposing reads fetch the same.
+    auto pv = [&](int stage, const bf16x8 (&pf)[2][2]) __attribute__((always_inline)) {
+        const char* vl = smem + (2 + stage) * C::TILE;
+        // MFMA i: db = i / 4, (b, t) = (i / 2 % 2, i % 2); fragments read one ahead
+        auto frag = [&](int i) __attribute__((always_inline)) {
+            const int db = i >> 2, b = (i >> 1) & 1, t = i & 1;
+            const char* base = vl + (32 * b + 16 * t) * RB + voff[db];
+            const u32x2 lo = lds_read_tr16(base);
+            const u32x2 hi = lds_read_tr16(base + 8 * RB);
+            const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
+            return __builtin_bit_cast(bf16x8, vf);
+        };
+        constexpr int NM = 4 * DB;
+        bf16x8 f0 = frag(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            bf16x8 f1;
+            if (i + 1 < NM) f1 = frag(i + 1);
+            oacc[i >> 2] = mfma32x32x16(f0, pf[(i >> 1) & 1][i & 1], oacc[i >> 2]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < NM) f0 = f1;
+        }
+    };
+
+    auto mask_tail = [&](f32x16 (&s)[2], int keys_left) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (key >= keys_left) s[b][r] = -INFINITY;
+            }
+    };
+
+    f32x16 sc[2];
+    bf16x8 pf[2][2];
+    float psum;
+
+    // Tile t sits in K / V stage t % 2. Iteration t: DMA tile t+1 into the
+    // other stage, then S^T(t), softmax(t), P V(t) from this stage, then wait
+    // for the DMA and a barrier (one per tile).
+    dma_k(0, 0);
+    dma_v(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    for (int tile = 0; tile + 1 < ntiles; ++tile) {
-        H3_ATTN_LOAD_TILE(tile + 1)
-        const uint16_t* kl = lds + (tile & 1) * L::bufElems;
-        attn_tile<D, false>(kl, kl + L::kElems, qf, oacc, m_run, l_run, scale_log2, lazy_raw,
-                            kBN, l32, g);
-        H3_ATTN_STORE_TILE((tile & 1) ^ 1)
-        __syncthreads();
+    const int keys_left = len - (ntiles - 1) * kBN;
+    for (int t = 0; t < ntiles; ++t) {
+        const int stage = t & 1;
+        const bool last = t + 1 == ntiles;
+        if (!last) {
+            dma_k(t + 1, stage ^ 1);
+            dma_v(t + 1, stage ^ 1);
+        }
+        qk(stage, sc);
+        if (last && keys_left < kBN) mask_tail(sc, keys_left);
+        softmax_exp(sc, pf, psum);
+        softmax_fix(sc, pf, psum);
+        pv(stage, pf);
+        if (!last) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
     }
-    {
-        const int tile = ntiles - 1;
-        const uint16_t* kl = lds + (tile & 1) * L::bufElems;
-        const int keys_left = len - tile * kBN;
-        if (keys_left < kBN)
-            attn_tile<D, true>(kl, kl + L::kElems, qf, oacc, m_run, l_run, scale_log2, lazy_raw,
-                               keys_left, l32, g);
-        else
-            attn_tile<D, false>(kl, kl + L::kElems, qf, oacc, m_run, l_run, scale_log2, lazy_raw,
-                                kBN, l32, g);
-    }
-#undef H3_ATTN_LOAD_TILE
-#undef H3_ATTN_STORE_TILE
 
-    // ---- normalise and store ----
+    // ---- normalise and store: lane holds dims 32 db + 8 r4 + 4 g + [0, 4) ----
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = 1.f / l_tot;
     if (qvalid) {
@@ -278,10 +319,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int d = 32 * db + 8 * r4 + 4 * g;
-                uint2 w;
+                u32x2 w;
                 w.x = pack_bf16x2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
                 w.y = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-                *reinterpret_cast<uint2*>(op + d) = w;
+                *reinterpret_cast<u32x2*>(op + d) = w;
             }
     }
 }
