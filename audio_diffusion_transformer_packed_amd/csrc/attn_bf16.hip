@@ -180,20 +180,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     float l_run = 0.f;         // partial row sum over this lane's keys
     constexpr float kTrig = 65536.0f;
 
-    // S^T(tile) from K stage `stage`; each K fragment is read one MFMA ahead
+    // S^T(tile) from K stage `stage`; K fragments are read PK MFMAs ahead
     auto qk = [&](int stage, f32x16 (&sc)[2]) __attribute__((always_inline)) {
         const char* kl = smem + stage * C::TILE;
+        constexpr int NM = 2 * KC, PK = 3;
+        auto kfrag = [&](int i) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8*>(kl + 32 * (i & 1) * RB + koff[i >> 1]);
+        };
         sc[0] = f32x16{};
         sc[1] = f32x16{};
-        bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + koff[0]);
+        bf16x8 kq[PK];
 #pragma unroll
-        for (int i = 0; i < 2 * KC; ++i) {
+        for (int i = 0; i < PK; ++i) kq[i] = kfrag(i);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
             bf16x8 kn;
-            if (i + 1 < 2 * KC)
-                kn = *reinterpret_cast<const bf16x8*>(kl + 32 * ((i + 1) & 1) * RB + koff[(i + 1) >> 1]);
-            sc[i & 1] = mfma32x32x16(kf, qf[i >> 1], sc[i & 1]);
+            if (i + PK < NM) kn = kfrag(i + PK);
+            sc[i & 1] = mfma32x32x16(kq[i % PK], qf[i >> 1], sc[i & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            if (i + 1 < 2 * KC) kf = kn;
+            if (i + PK < NM) kq[i % PK] = kn;
         }
     };
 
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     // of it (the S^T accumulator rows), the transposing reads fetch the same.
     auto pv = [&](int stage, const bf16x8 (&pf)[2][2]) __attribute__((always_inline)) {
         const char* vl = smem + (2 + stage) * C::TILE;
-        // MFMA i: db = i / 4, (b, t) = (i / 2 % 2, i % 2); fragments read one ahead
+        // MFMA i: db = i / 4, (b, t) = (i / 2 % 2, i % 2); fragments read ahead
         auto frag = [&](int i) __attribute__((always_inline)) {
             const int db = i >> 2, b = (i >> 1) & 1, t = i & 1;
             const char* base = vl + (32 * b + 16 * t) * RB + voff[db];
@@ -257,15 +262,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
             const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
             return __builtin_bit_cast(bf16x8, vf);
         };
-        constexpr int NM = 4 * DB;
-        bf16x8 f0 = frag(0);
+        constexpr int NM = 4 * DB, PV_AHEAD = 2;
+        bf16x8 vq[PV_AHEAD];
+#pragma unroll
+        for (int i = 0; i < PV_AHEAD; ++i) vq[i] = frag(i);
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
-            bf16x8 f1;
-            if (i + 1 < NM) f1 = frag(i + 1);
-            oacc[i >> 2] = mfma32x32x16(f0, pf[(i >> 1) & 1][i & 1], oacc[i >> 2]);
+            bf16x8 vn;
+            if (i + PV_AHEAD < NM) vn = frag(i + PV_AHEAD);
+            oacc[i >> 2] = mfma32x32x16(vq[i % PV_AHEAD], pf[(i >> 1) & 1][i & 1], oacc[i >> 2]);
             __builtin_amdgcn_sched_barrier(0);
-            if (i + 1 < NM) f0 = f1;
+            if (i + PV_AHEAD < NM) vq[i % PV_AHEAD] = vn;
         }
     };
 
