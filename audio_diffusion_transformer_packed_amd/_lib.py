@@ -18,7 +18,7 @@ H3_ERR_HIP = 4
 
 H3_ATTN_BF16 = 0
 H3_ATTN_FP8_E4M3 = 1
-H3_ATTN_BLOCK_M = 128
+H3_ATTN_BLOCK_M = 256
 
 # Every exported symbol, in header order.
 EXPORTS = (

@@ -7,9 +7,11 @@
 // section "长序列注意力与通信优化").
 //
 // Design (CDNA4, 64-lane waves):
-//  * one workgroup per work item (head, segment, 128-row query tile), four
-//    waves of 32 query rows each; the work list comes from the bookkeeping
-//    kernel, so no padded token is ever loaded or computed;
+//  * one workgroup per work item (head, segment, 256-row query tile), eight
+//    waves of 32 query rows each, one workgroup per CU (two waves per SIMD);
+//    the 256 rows share every K / V tile brought into LDS, which halves the
+//    global -> LDS traffic of a 128-row tile; the work list comes from the
+//    bookkeeping kernel, so no padded token is ever loaded or computed;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane owns one query row (lane % 32) and
 //    16 of every 32 keys, so row statistics are lane-local plus one exchange
@@ -21,8 +23,8 @@
 //    (no staging registers), double buffered, with XOR-swizzled 16-byte
 //    chunks so both fragment reads are free of bank conflicts;
 //  * each key tile: S^T MFMAs, softmax, P V MFMAs, while the next tile's K
-//    and V stream into the other LDS stage; two waves per SIMD (two
-//    workgroups per CU) overlap one wave's softmax with the other's MFMAs;
+//    and V stream into the other LDS stage; the two waves of a SIMD overlap
+//    one wave's softmax with the other's MFMAs;
 //  * softmax in the exp2 domain with a reference max that only moves when a
 //    lane's partial sum of exp2 values exceeds 2^16 (or is infinite):
 //    then the tile's true max is taken, O and l are rescaled and the tile's
@@ -35,14 +37,15 @@ namespace h3 {
 namespace {
 
 constexpr int kBN = 64;        // keys per tile
-constexpr int kThreads = 256;  // four waves
+constexpr int kWaves = 8;      // 32 query rows each
+constexpr int kThreads = 64 * kWaves;
 
 template <int D>
 struct Cfg {
     static constexpr int RB = D * 2;               // bytes per K / V row in LDS
     static constexpr int CPR = D / 8;              // 16-byte chunks per row
     static constexpr int RPI = 1024 / RB;          // rows per 1 KB DMA instruction
-    static constexpr int NI = kBN / RPI / 4;       // DMA instructions per wave per operand
+    static constexpr int NI = kBN / RPI / kWaves;       // DMA instructions per wave per operand
     static constexpr int TILE = kBN * RB;          // bytes per K or V tile
     static constexpr int KC = D / 16;              // MFMA k-steps over the head dim
     static constexpr int DB = D / 32;              // 32-wide output blocks
@@ -71,7 +74,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int64_t qs, int64_t ks,
     int64_t vs, int64_t os, const int32_t* __restrict__ cu, const int4* __restrict__ items,

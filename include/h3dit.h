@@ -61,7 +61,7 @@ extern "C" {
 /* Largest number of packed segments accepted by one call. */
 #define H3_MAX_SEGMENTS 65536
 /* Query rows per attention work item (the tile of the work list). */
-#define H3_ATTN_BLOCK_M 128
+#define H3_ATTN_BLOCK_M 256
 /* Tokens per fp8 Q/K scale block (aligned to each segment's start). */
 #define H3_FP8_QK_BLOCK 64
 

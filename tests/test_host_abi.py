@@ -103,7 +103,8 @@ def test_workspace_sizes(lib):
     # capacity covers the worst case over all cu_seqlens with these sizes
     for b, n in [(1, 1), (3, 3), (5, 700), (64, 64 * 129)]:
         need = lib.h3_attn_varlen_workspace_size(b, n, 4, 64, None)
-        assert need >= 16 * 4 * (n + b * 127) // 128
+        bm = L.H3_ATTN_BLOCK_M
+        assert need >= 16 * 4 * ((n + b * (bm - 1)) // bm)
     dims = L.DitDims(3072, 24, 128, 8192, (C.c_int32 * 3)(32, 48, 48), 1e4, 1e-6)
     ws = lib.h3_dit_block_workspace_size(C.byref(dims), 1, 57960)
     n, c = 57960, 3072
