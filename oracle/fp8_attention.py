@@ -64,16 +64,28 @@ def e4m3_round(a) -> np.ndarray:
     return np.copysign(r, a)
 
 
-def _scale_of(block: np.ndarray, axis=None) -> np.ndarray:
-    amax = np.max(np.abs(block), axis=axis)
-    return np.where(amax > 0, amax / E4M3_MAX, 1.0)
+def _scale_of(block: np.ndarray, axis=None, decide=_F) -> np.ndarray:
+    """amax / 448, or 1 where amax == 0; computed in the `decide` precision."""
+    amax = np.max(np.abs(block), axis=axis).astype(decide)
+    return np.where(amax > 0, amax / decide(E4M3_MAX), decide(1.0)).astype(decide)
 
 
-def quantize_qk_blocks(x, cu: Sequence[int], block: int = 64) -> Tuple[np.ndarray, np.ndarray]:
+def _codes(x: np.ndarray, sc: np.ndarray, decide=_F) -> np.ndarray:
+    """e4m3(x / scale) with the quotient formed in the `decide` precision."""
+    quot = x.astype(decide) / sc.astype(decide)
+    return e4m3_round(quot.astype(_F))
+
+
+def quantize_qk_blocks(x, cu: Sequence[int], block: int = 64,
+                       decide=_F) -> Tuple[np.ndarray, np.ndarray]:
     """Per (head, segment-aligned `block`-token block) quantisation of q or k.
 
     x: [N, H, D]. Returns (codes as float64 values on the e4m3 grid [N, H, D],
     scales [num_blocks, H]) with blocks enumerated segment by segment.
+    `decide` is the precision of the scale and of the quotient x / scale that
+    selects each code: float64 by default; np.float32 reproduces, bit for bit,
+    an fp32 implementation of the same definition (IEEE fp32 division), which
+    is how codes are compared exactly against a kernel.
     """
     x = np.asarray(x, dtype=_F)
     n, heads, _ = x.shape
@@ -83,15 +95,16 @@ def quantize_qk_blocks(x, cu: Sequence[int], block: int = 64) -> Tuple[np.ndarra
     for s in range(cu.size - 1):
         for t0 in range(int(cu[s]), int(cu[s + 1]), block):
             t1 = min(int(cu[s + 1]), t0 + block)
-            sc = _scale_of(x[t0:t1], axis=(0, 2))          # [H]
-            codes[t0:t1] = e4m3_round(x[t0:t1] / sc[None, :, None])
+            sc = _scale_of(x[t0:t1], axis=(0, 2), decide=decide)          # [H]
+            codes[t0:t1] = _codes(x[t0:t1], sc[None, :, None], decide)
             scales.append(sc)
     sc_arr = np.array(scales, dtype=_F).reshape(-1, heads)
     return codes, sc_arr
 
 
-def quantize_v_channels(v, cu: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
-    """Per (segment, head, channel) quantisation of v: codes [N,H,D], scales [B,H,D]."""
+def quantize_v_channels(v, cu: Sequence[int], decide=_F) -> Tuple[np.ndarray, np.ndarray]:
+    """Per (segment, head, channel) quantisation of v: codes [N,H,D], scales [B,H,D].
+    `decide` as in quantize_qk_blocks."""
     v = np.asarray(v, dtype=_F)
     n, heads, d = v.shape
     cu = np.asarray(cu, dtype=np.int64)
@@ -101,8 +114,8 @@ def quantize_v_channels(v, cu: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
         a, b = int(cu[s]), int(cu[s + 1])
         if b == a:
             continue
-        sc = _scale_of(v[a:b], axis=0)                       # [H, D]
-        codes[a:b] = e4m3_round(v[a:b] / sc[None])
+        sc = _scale_of(v[a:b], axis=0, decide=decide)                       # [H, D]
+        codes[a:b] = _codes(v[a:b], sc[None], decide)
         scales[s] = sc
     return codes, scales
 

@@ -145,3 +145,55 @@ def test_groups_restrict_the_work():
     part, rep = fp8_attn_emulated_ref(q, k, v, cu, groups=[(1, 64)])
     assert np.array_equal(part[64:96, 1], full[64:96, 1])
     assert not part[:, 0].any() and len(rep) == 1
+
+
+def _bf16_values(shape, seed, std=1.0):
+    """float64 values that are exactly bf16 (what the quantiser reads)."""
+    a = (std * np.random.default_rng(seed).standard_normal(shape)).astype(np.float32)
+    bits = a.view(np.uint32)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.view(np.float32).astype(np.float64)
+
+
+def test_float32_decision_matches_torch_float32_pipeline():
+    """decide=np.float32: scale = fp32(amax) / 448 and code = e4m3(fp32(x / scale)),
+    pinned against torch's float32 division and its float8_e4m3fn cast."""
+    torch = pytest.importorskip("torch")
+    cu = [0, 100, 100, 229]
+    x = _bf16_values((229, 3, 128), 21, 1.7)
+    codes, scales = quantize_qk_blocks(x, cu, 64, decide=np.float32)
+    blocks = [(0, 64), (64, 100), (100, 164), (164, 228), (228, 229)]
+    assert scales.shape == (len(blocks), 3)
+    for bi, (a, b) in enumerate(blocks):
+        xt = torch.from_numpy(x[a:b].astype(np.float32))
+        amax = xt.abs().amax(dim=(0, 2))
+        sc = amax / torch.tensor(448.0, dtype=torch.float32)
+        assert np.array_equal(scales[bi].astype(np.float32), sc.numpy())
+        ref = (xt / sc[None, :, None]).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        assert np.array_equal(codes[a:b], ref)
+    vc, vs = quantize_v_channels(x, cu, decide=np.float32)
+    for s, (a, b) in enumerate([(0, 100), (100, 100), (100, 229)]):
+        if a == b:
+            assert (vs[s] == 1.0).all()
+            continue
+        xt = torch.from_numpy(x[a:b].astype(np.float32))
+        sc = xt.abs().amax(dim=0) / torch.tensor(448.0, dtype=torch.float32)
+        assert np.array_equal(vs[s].astype(np.float32), sc.numpy())
+        ref = (xt / sc[None]).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        assert np.array_equal(vc[a:b], ref)
+
+
+def test_float32_and_float64_decisions_differ_only_at_boundaries():
+    """The two precisions pick the same code except where the float64 quotient
+    sits within float32 rounding of a rounding boundary; then by one step."""
+    x = _bf16_values((640, 4, 128), 22, 0.8)
+    c64, s64 = quantize_qk_blocks(x, [0, 640], 64)
+    c32, s32 = quantize_qk_blocks(x, [0, 640], 64, decide=np.float32)
+    assert np.allclose(s32, s64, rtol=2 ** -23, atol=0)
+    diff = c32 != c64
+    assert diff.mean() < 1e-3
+    if diff.any():
+        step = np.abs(c32 - c64)[diff]
+        mag = np.maximum(np.abs(c32), np.abs(c64))[diff]
+        ulp = np.power(2.0, np.floor(np.log2(np.maximum(mag, 2.0 ** -6))) - 3)
+        assert np.all(step <= ulp * 1.0000001)
