@@ -16,7 +16,8 @@ Sources, cited by page title and section:
 The pages do not give the quantisation granularity, the P encoding or the
 skip threshold. This module follows this reading:
   * format: OCP e4m3fn (max 448, subnormals down to 2^-9), round to nearest
-    even, saturating; scale = amax / 448 (1 when amax == 0);
+    even, saturating; scale = amax / 448 (1 when amax == 0); the code of x is
+    e4m3(x / scale) with the scale taken exactly, i.e. RNE(448 x / amax);
   * Q and K: one scale per (head, 64-token block), blocks aligned to the
     segment start (the last block of a segment may be short);
   * V: one scale per (segment, head, channel), so it factors out of the sum
@@ -64,28 +65,28 @@ def e4m3_round(a) -> np.ndarray:
     return np.copysign(r, a)
 
 
-def _scale_of(block: np.ndarray, axis=None, decide=_F) -> np.ndarray:
-    """amax / 448, or 1 where amax == 0; computed in the `decide` precision."""
-    amax = np.max(np.abs(block), axis=axis).astype(decide)
-    return np.where(amax > 0, amax / decide(E4M3_MAX), decide(1.0)).astype(decide)
+def _amax_scale(block: np.ndarray, axis=None) -> Tuple[np.ndarray, np.ndarray]:
+    """(amax, scale): scale = amax / 448, or 1 where amax == 0."""
+    amax = np.max(np.abs(block), axis=axis)
+    return amax, np.where(amax > 0, amax / E4M3_MAX, 1.0)
 
 
-def _codes(x: np.ndarray, sc: np.ndarray, decide=_F) -> np.ndarray:
-    """e4m3(x / scale) with the quotient formed in the `decide` precision."""
-    quot = x.astype(decide) / sc.astype(decide)
-    return e4m3_round(quot.astype(_F))
+def _codes(x: np.ndarray, amax: np.ndarray) -> np.ndarray:
+    """e4m3(x / scale) with scale = amax / 448 taken exactly: the code is
+    RNE(448 x / amax), evaluated without rounding the scale first (zero where
+    amax == 0). For bf16 inputs 448 x is exact and the one division decides
+    exactly: a quotient that is exactly a rounding midpoint stays one and
+    goes to the even code, any other is at least 2^-12 (relative) away from
+    one, far beyond the division's rounding."""
+    den = np.where(amax > 0, amax, 1.0)
+    return e4m3_round(E4M3_MAX * x / den)
 
 
-def quantize_qk_blocks(x, cu: Sequence[int], block: int = 64,
-                       decide=_F) -> Tuple[np.ndarray, np.ndarray]:
+def quantize_qk_blocks(x, cu: Sequence[int], block: int = 64) -> Tuple[np.ndarray, np.ndarray]:
     """Per (head, segment-aligned `block`-token block) quantisation of q or k.
 
     x: [N, H, D]. Returns (codes as float64 values on the e4m3 grid [N, H, D],
     scales [num_blocks, H]) with blocks enumerated segment by segment.
-    `decide` is the precision of the scale and of the quotient x / scale that
-    selects each code: float64 by default; np.float32 reproduces, bit for bit,
-    an fp32 implementation of the same definition (IEEE fp32 division), which
-    is how codes are compared exactly against a kernel.
     """
     x = np.asarray(x, dtype=_F)
     n, heads, _ = x.shape
@@ -95,16 +96,15 @@ def quantize_qk_blocks(x, cu: Sequence[int], block: int = 64,
     for s in range(cu.size - 1):
         for t0 in range(int(cu[s]), int(cu[s + 1]), block):
             t1 = min(int(cu[s + 1]), t0 + block)
-            sc = _scale_of(x[t0:t1], axis=(0, 2), decide=decide)          # [H]
-            codes[t0:t1] = _codes(x[t0:t1], sc[None, :, None], decide)
+            amax, sc = _amax_scale(x[t0:t1], axis=(0, 2))          # [H]
+            codes[t0:t1] = _codes(x[t0:t1], amax[None, :, None])
             scales.append(sc)
     sc_arr = np.array(scales, dtype=_F).reshape(-1, heads)
     return codes, sc_arr
 
 
-def quantize_v_channels(v, cu: Sequence[int], decide=_F) -> Tuple[np.ndarray, np.ndarray]:
-    """Per (segment, head, channel) quantisation of v: codes [N,H,D], scales [B,H,D].
-    `decide` as in quantize_qk_blocks."""
+def quantize_v_channels(v, cu: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """Per (segment, head, channel) quantisation of v: codes [N,H,D], scales [B,H,D]."""
     v = np.asarray(v, dtype=_F)
     n, heads, d = v.shape
     cu = np.asarray(cu, dtype=np.int64)
@@ -114,8 +114,8 @@ def quantize_v_channels(v, cu: Sequence[int], decide=_F) -> Tuple[np.ndarray, np
         a, b = int(cu[s]), int(cu[s + 1])
         if b == a:
             continue
-        sc = _scale_of(v[a:b], axis=0, decide=decide)                       # [H, D]
-        codes[a:b] = _codes(v[a:b], sc[None], decide)
+        amax, sc = _amax_scale(v[a:b], axis=0)                       # [H, D]
+        codes[a:b] = _codes(v[a:b], amax[None])
         scales[s] = sc
     return codes, scales
 

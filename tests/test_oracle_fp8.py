@@ -155,45 +155,68 @@ def _bf16_values(shape, seed, std=1.0):
     return bits.view(np.float32).astype(np.float64)
 
 
-def test_float32_decision_matches_torch_float32_pipeline():
-    """decide=np.float32: scale = fp32(amax) / 448 and code = e4m3(fp32(x / scale)),
-    pinned against torch's float32 division and its float8_e4m3fn cast."""
+def _exact_e4m3_code(fr):
+    """Exact RNE of a Fraction onto the e4m3fn grid (saturating at 448): the
+    nearest grid value, ties to the even code (codes of non-negative values
+    are their index in the ascending grid)."""
+    from fractions import Fraction
+    grid = [Fraction(0)] + [Fraction(v) for v in _positive_e4m3_grid()]
+    mag = min(abs(fr), Fraction(448))
+    best = min(range(len(grid)), key=lambda i: (abs(grid[i] - mag), i % 2))
+    return float(grid[best]) * (-1.0 if fr < 0 else 1.0)
+
+
+def test_codes_are_exact_decisions_for_bf16_inputs():
+    """For bf16 x and amax the float64 code RNE(448 x / amax) equals the
+    exact rational decision, including exact midpoints (ties to even)."""
+    from fractions import Fraction
+    x = _bf16_values((64, 1, 128), 21, 1.3)
+    x[0, 0, 0] = 4.0                   # a power-of-two amax puts many quotients on midpoints
+    codes, scales = quantize_qk_blocks(np.clip(x, -4, 4), [0, 64], 64)
+    xs = np.clip(x, -4, 4)
+    amax = Fraction(4)
+    ties = 0
+    for t in range(64):
+        for d in range(0, 128, 3):
+            q = Fraction(448) * Fraction(float(xs[t, 0, d])) / amax
+            want = _exact_e4m3_code(q)
+            assert codes[t, 0, d] == want, (t, d, float(q))
+            ties += q.denominator <= 2 and abs(q) > 16
+    assert ties > 10
+    assert scales[0, 0] == 4.0 / 448.0
+
+
+def test_tie_example_goes_to_even():
+    """448 * (-1.4296875) / 3.8125 = -168 exactly, the midpoint of -160 and
+    -176: the code is -160 (even mantissa). Dividing by a rounded scale
+    amax / 448 instead would land just past the midpoint."""
+    x = np.zeros((1, 1, 4))
+    x[0, 0, :2] = [-1.4296875, 3.8125]
+    codes, scales = quantize_qk_blocks(x, [0, 1], 64)
+    assert codes[0, 0, 0] == -160.0 and codes[0, 0, 1] == 448.0
+    assert e4m3_round(-1.4296875 / (3.8125 / 448.0)) == -176.0
+
+
+def test_codes_match_torch_float32_pipeline():
+    """The fp32 evaluation (448 x) / amax of bf16 inputs followed by torch's
+    float8_e4m3fn cast gives the same codes (448 x is exact in fp32 and one
+    correctly rounded division decides)."""
     torch = pytest.importorskip("torch")
     cu = [0, 100, 100, 229]
-    x = _bf16_values((229, 3, 128), 21, 1.7)
-    codes, scales = quantize_qk_blocks(x, cu, 64, decide=np.float32)
-    blocks = [(0, 64), (64, 100), (100, 164), (164, 228), (228, 229)]
-    assert scales.shape == (len(blocks), 3)
-    for bi, (a, b) in enumerate(blocks):
+    x = _bf16_values((229, 3, 128), 22, 1.7)
+    codes, scales = quantize_qk_blocks(x, cu, 64)
+    for bi, (a, b) in enumerate([(0, 64), (64, 100), (100, 164), (164, 228), (228, 229)]):
         xt = torch.from_numpy(x[a:b].astype(np.float32))
         amax = xt.abs().amax(dim=(0, 2))
-        sc = amax / torch.tensor(448.0, dtype=torch.float32)
-        assert np.array_equal(scales[bi].astype(np.float32), sc.numpy())
-        ref = (xt / sc[None, :, None]).to(torch.float8_e4m3fn).to(torch.float64).numpy()
-        assert np.array_equal(codes[a:b], ref)
-    vc, vs = quantize_v_channels(x, cu, decide=np.float32)
+        ref = ((xt * 448.0) / amax[None, :, None]).to(torch.float8_e4m3fn).to(torch.float64)
+        assert np.array_equal(codes[a:b], ref.numpy())
+        assert np.array_equal(scales[bi].astype(np.float32), (amax / 448.0).numpy())
+    vc, vs = quantize_v_channels(x, cu)
     for s, (a, b) in enumerate([(0, 100), (100, 100), (100, 229)]):
         if a == b:
             assert (vs[s] == 1.0).all()
             continue
         xt = torch.from_numpy(x[a:b].astype(np.float32))
-        sc = xt.abs().amax(dim=0) / torch.tensor(448.0, dtype=torch.float32)
-        assert np.array_equal(vs[s].astype(np.float32), sc.numpy())
-        ref = (xt / sc[None]).to(torch.float8_e4m3fn).to(torch.float64).numpy()
-        assert np.array_equal(vc[a:b], ref)
-
-
-def test_float32_and_float64_decisions_differ_only_at_boundaries():
-    """The two precisions pick the same code except where the float64 quotient
-    sits within float32 rounding of a rounding boundary; then by one step."""
-    x = _bf16_values((640, 4, 128), 22, 0.8)
-    c64, s64 = quantize_qk_blocks(x, [0, 640], 64)
-    c32, s32 = quantize_qk_blocks(x, [0, 640], 64, decide=np.float32)
-    assert np.allclose(s32, s64, rtol=2 ** -23, atol=0)
-    diff = c32 != c64
-    assert diff.mean() < 1e-3
-    if diff.any():
-        step = np.abs(c32 - c64)[diff]
-        mag = np.maximum(np.abs(c32), np.abs(c64))[diff]
-        ulp = np.power(2.0, np.floor(np.log2(np.maximum(mag, 2.0 ** -6))) - 3)
-        assert np.all(step <= ulp * 1.0000001)
+        amax = xt.abs().amax(dim=0)
+        ref = ((xt * 448.0) / amax[None]).to(torch.float8_e4m3fn).to(torch.float64)
+        assert np.array_equal(vc[a:b], ref.numpy())
