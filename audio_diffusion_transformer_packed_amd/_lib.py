@@ -19,12 +19,14 @@ H3_ERR_HIP = 4
 H3_ATTN_BF16 = 0
 H3_ATTN_FP8_E4M3 = 1
 H3_ATTN_BLOCK_M = 256
+H3_FP8_QK_BLOCK = 64
 
 # Every exported symbol, in header order.
 EXPORTS = (
     "h3_status_string", "h3_last_error_message", "h3_abi_version", "h3_build_schedule_host",
     "h3_varlen_bookkeeping_workspace_size", "h3_varlen_bookkeeping",
     "h3_attn_varlen_workspace_size", "h3_attn_varlen_num_items", "h3_attn_varlen",
+    "h3_fp8_num_tiles", "h3_fp8_quantize_workspace_size", "h3_fp8_quantize",
     "h3_qk_rmsnorm_rope", "h3_modulation", "h3_adaln_rmsnorm_modulate", "h3_linear_bf16",
     "h3_linear_swiglu_bf16", "h3_linear_gated_residual_bf16", "h3_dit_block_workspace_size",
     "h3_dit_block_forward",
@@ -75,6 +77,10 @@ def _declare(lib):
         "h3_attn_varlen_num_items": (C.c_int, [P, I32, I32, P]),
         "h3_attn_varlen": (C.c_int, [P, P, P, P, I64, I64, I64, I64, P, P, I32, I32, I32, I32, P,
                                      P, SZ, P]),
+        "h3_fp8_num_tiles": (C.c_int, [P, I32, P]),
+        "h3_fp8_quantize_workspace_size": (SZ, [I32, I32, I32]),
+        "h3_fp8_quantize": (C.c_int, [P, P, P, I64, I64, I64, P, P, I32, I32, I32, I32, P, P, P, P,
+                                      P, P, P, SZ, P]),
         "h3_qk_rmsnorm_rope": (C.c_int, [P, P, I64, I64, P, P, P, I32, I32, I32, P, F32, F32, P]),
         "h3_modulation": (C.c_int, [P, P, P, I32, I32, P]),
         "h3_adaln_rmsnorm_modulate": (C.c_int, [P, P, P, P, I64, P, P, I32, I32, I32, F32, P]),

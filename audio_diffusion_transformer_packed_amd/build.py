@@ -43,6 +43,7 @@ def sources():
 # operands is dropped there.
 EXTRA_FLAGS = {
     "attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "attn_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 
 

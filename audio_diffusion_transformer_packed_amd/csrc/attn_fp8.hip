@@ -1,18 +1,322 @@
-// fp8 (e4m3) attention: not built yet; the entry point reports it as unsupported.
+// fp8 (e4m3) varlen attention with skip-softmax on gfx950 fp8 MFMA
+// ("MiniMax H3 FastH3 real-time serving with vLLM-Omni", section "Scaling
+// beyond the FastH3 profile", sparse & quantized attention bullet; "FastH3
+// 在八卡 B300 上实现完整 MP4 生成快于播放时长", section "其他加速路径：有损但可控":
+// SAGE quantises attention to FP8, Skip-Softmax skips the Softmax and P x V
+// work of unimportant parts while Q K^T is still computed).
+//
+// Per segment and head, over the codes and scales written by the quantise
+// pass (fp8_quant.hip):
+//   S = (Q8 K8^T) s_q s_k * scale, online softmax over 64-key tiles in
+//   ascending order with the exact running row max m,
+//   P8 = e4m3(448 p), p = exp(S - m), l = sum of the unquantised p,
+//   O = (sum P8 V8) s_v / (448 l).
+// Skip rule: for the 32 query rows of a wave, a key tile other than the
+// segment's first is skipped (no exp, no P V) when every valid row has its
+// tile maximum more than `threshold` (natural-log units) below its running
+// maximum. Each work item reports its number of skipped (32-row group, key
+// tile) pairs; the count is summed in LDS, no atomics.
+//
+// Design (CDNA4): the bf16 kernel's layout with v_mfma_f32_32x32x64_f8f6f4.
+//  * one workgroup of eight waves per 256-row work item, 32 query rows per
+//    wave, each lane owning one query row of S^T = K Q^T (lane % 32);
+//  * K tiles (64 keys x 128 B) and V^T tiles (128 channels x 64 B, keys
+//    already in the lanes' P order) are contiguous 8 KB blocks in HBM, moved
+//    to LDS with global_load_lds_dwordx4 (one instruction per wave and
+//    operand), double buffered, XOR-swizzled for conflict-free 16-byte
+//    fragment reads; no transposing reads are needed;
+//  * P is converted to e4m3 in registers, already in the B-operand byte
+//    order of the P V MFMA; per tile a wave issues 4 + 4 fp8 MFMAs.
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
 namespace h3 {
+namespace {
 
-bool fp8_attention_available() { return false; }
+constexpr int kD = 128;
+constexpr int kBN = 64;                    // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKT = kBN * kD;              // bytes of a K tile
+constexpr int kVT = kD * kBN;              // bytes of a V^T tile
+constexpr float kLog2_448 = 8.807354922057604f;
 
-size_t fp8_scratch_bytes(int, int, int, int) { return 0; }
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-hipError_t launch_attn_fp8(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int64_t,
-                           int64_t, int64_t, int64_t, const int32_t*, const int32_t*,
-                           const int32_t*, int64_t, int, int, int, int, float, int, float,
-                           int32_t*, void*, hipStream_t) {
-    return hipErrorNotSupported;
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                              reinterpret_cast<uintptr_t>(lds_dst)),
+                                     16, 0, 0);
+}
+
+// Chunk swizzles (physical 16-byte chunk = logical chunk ^ swizzle(row)):
+// K rows are 128 B (8 chunks), V^T rows 64 B (4 chunks).
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int vswz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ i32x8 read32(const char* p0, const char* p1) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p0);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p1);
+    return i32x8{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z), static_cast<int>(a.w),
+                 static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z), static_cast<int>(b.w)};
+}
+
+__global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
+    const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
+    const float* __restrict__ qsc, const float* __restrict__ ksc, const float* __restrict__ vsc,
+    uint16_t* __restrict__ o, int64_t os, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ tb, const int4* __restrict__ items, int num_seqs,
+    int total_tokens, int num_heads, int64_t num_tiles, float scale_log2, int skip,
+    float thr_log2, int32_t* __restrict__ skip_counts) {
+    // K stage 0, K stage 1, V stage 0, V stage 1
+    __shared__ __attribute__((aligned(1024))) char smem[2 * kKT + 2 * kVT];
+    __shared__ int32_t wskip[kWaves];
+
+    const int tid = threadIdx.x;
+    const int4 it = items[blockIdx.x];
+    const int head = it.x, seg = it.y, q0 = it.z, qlen = it.w;
+    bool ok = seg >= 0 && seg < num_seqs && head >= 0 && head < num_heads;
+    const int kv0 = ok ? max(0, cu[seg]) : 0;
+    const int kv1 = ok ? min(total_tokens, cu[seg + 1]) : 0;
+    ok = ok && q0 >= kv0 && qlen > 0 && q0 + qlen <= kv1;
+    if (!ok) {
+        if (skip_counts && tid == 0) skip_counts[blockIdx.x] = 0;
+        return;
+    }
+    const int len = kv1 - kv0;
+    const int ntiles = (len + kBN - 1) / kBN;
+    const int keys_left = len - (ntiles - 1) * kBN;
+    const int tbs = tb[seg];
+
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int qrow_local = wave * 32 + l32;
+    const bool qvalid = qrow_local < qlen;
+    const bool wave_active = wave * 32 < qlen;   // wave-uniform
+    const int64_t row_bytes = static_cast<int64_t>(num_heads) * kD;
+
+    // Q fragments (B operand of S^T): k-step c holds bytes 64c + 32g + [0, 32)
+    i32x8 qf[2];
+    {
+        const uint8_t* qp = q8 + static_cast<int64_t>(q0 + qrow_local) * row_bytes + head * kD + 32 * g;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            if (qvalid) {
+                qf[c] = read32(reinterpret_cast<const char*>(qp + 64 * c),
+                               reinterpret_cast<const char*>(qp + 64 * c + 16));
+            } else {
+                qf[c] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+    }
+    // s_q * scale * log2(e) of this lane's row
+    const int qblk = tbs + (q0 - kv0 + min(qrow_local, qlen - 1)) / kBN;
+    const float sq = qsc[static_cast<int64_t>(qblk) * num_heads + head] * scale_log2;
+
+    // DMA: instruction `wave` of a tile fills LDS bytes [1024 wave, +1024):
+    // K rows 8 wave + lane / 8 (chunk lane % 8), V^T rows 16 wave + lane / 4
+    // (chunk lane % 4), each loading the logical chunk that the swizzle puts there.
+    const int krow = 8 * wave + (lane >> 3), vrow = 16 * wave + (lane >> 2);
+    const uint32_t ksrc = krow * kD + 16 * ((lane & 7) ^ kswz(krow));
+    const uint32_t vsrc = vrow * kBN + 16 * ((lane & 3) ^ vswz(vrow));
+    const uint8_t* kbase = k8 + (static_cast<int64_t>(head) * num_tiles + tbs) * kKT;
+    const uint8_t* vbase = v8t + (static_cast<int64_t>(head) * num_tiles + tbs) * kVT;
+    auto dma = [&](int tile, int stage) __attribute__((always_inline)) {
+        lds_dma16(kbase + static_cast<int64_t>(tile) * kKT + ksrc, smem + stage * kKT + 1024 * wave);
+        lds_dma16(vbase + static_cast<int64_t>(tile) * kVT + vsrc,
+                  smem + 2 * kKT + stage * kVT + 1024 * wave);
+    };
+
+    // LDS fragment offsets. K block b, k-step c: row 32b + l32, logical
+    // chunks 4c + 2g + {0, 1}. V^T block db: row 32db + l32, chunks 2g + {0, 1}.
+    const int ksw = kswz(l32), vsw = vswz(l32);
+    int kro[2][2], vro[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) kro[c][h] = l32 * kD + 16 * ((4 * c + 2 * g + h) ^ ksw);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vro[h] = l32 * kBN + 16 * ((2 * g + h) ^ vsw);
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) oacc[b] = f32x16{};
+    float m_run = -1e30f;     // running row max, exp2 units (finite start: no inf - inf)
+    float l_run = 0.f;        // partial sum of 448 p over this lane's keys
+    int nskip = 0;
+
+    dma(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int stage = t & 1;
+        const bool last = t + 1 == ntiles;
+        if (!last) dma(t + 1, stage ^ 1);
+        const float sk = ksc[static_cast<int64_t>(tbs + t) * num_heads + head];
+        if (wave_active) {
+            const char* kl = smem + stage * kKT;
+            const char* vl = smem + 2 * kKT + stage * kVT;
+            f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    sc[b] = mfma_fp8(read32(kl + 4096 * b + kro[c][0], kl + 4096 * b + kro[c][1]), qf[c], sc[b]);
+            if (last && keys_left < kBN) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * b + 8 * (r >> 2) + 4 * g + (r & 3) >= keys_left) sc[b][r] = -INFINITY;
+            }
+            float mx = sc[0][0];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float ct = sq * sk;          // exp2 units per raw score
+            const float tmax = mx * ct;
+            bool run_tile = true;
+            if (skip && t > 0) {
+                const bool below = !qvalid || tmax < m_run - thr_log2;
+                if (__all(below)) {                       // wave-uniform
+                    run_tile = false;
+                    ++nskip;
+                }
+            }
+            if (run_tile) {
+                const float m_new = fmaxf(m_run, tmax);
+                if (__any(m_new > m_run)) {               // wave-uniform
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    l_run *= alpha;
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+                }
+                m_run = m_new;
+                // 448 p = exp2(s ct - m + log2 448); bytes in B-operand order:
+                // byte 16 b + r of this lane holds score sc[b][r]
+                const float mb = m_new - kLog2_448;
+                i32x8 pf;
+                float ps = 0.f;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    const int b = w >> 2, r = 4 * (w & 3);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][r], ct, -mb));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 1], ct, -mb));
+                    const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 2], ct, -mb));
+                    const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 3], ct, -mb));
+                    ps += (p0 + p1) + (p2 + p3);
+                    int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                    word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+                    pf[w] = word;
+                }
+                l_run += ps;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    oacc[db] = mfma_fp8(read32(vl + 2048 * db + vro[0], vl + 2048 * db + vro[1]), pf, oacc[db]);
+            }
+        }
+        if (!last) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    }
+
+    // ---- O = acc s_v / l; lane holds channels 32 db + 8 r4 + 4 g + [0, 4) ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.f / l_tot;
+    if (qvalid) {
+        uint16_t* op = o + static_cast<int64_t>(q0 + qrow_local) * os + static_cast<int64_t>(head) * kD;
+        const float* svp = vsc + (static_cast<int64_t>(seg) * num_heads + head) * kD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * g;
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(svp + d);
+                u32x2 w;
+                w.x = pack_bf16x2(oacc[db][4 * r4 + 0] * (sv.x * inv), oacc[db][4 * r4 + 1] * (sv.y * inv));
+                w.y = pack_bf16x2(oacc[db][4 * r4 + 2] * (sv.z * inv), oacc[db][4 * r4 + 3] * (sv.w * inv));
+                *reinterpret_cast<u32x2*>(op + d) = w;
+            }
+    }
+    if (skip_counts) {
+        if (lane == 0) wskip[wave] = wave_active ? nskip : 0;
+        __syncthreads();
+        if (tid == 0) {
+            int32_t s = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) s += wskip[w];
+            skip_counts[blockIdx.x] = s;
+        }
+    }
+}
+
+// Byte offsets of the fp8 scratch (codes, scales, quantise workspace).
+struct Fp8Scratch {
+    size_t q8, k8, v8t, qsc, ksc, vsc, ws, total;
+};
+
+size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
+
+Fp8Scratch fp8_scratch_layout(int num_seqs, int total_tokens, int num_heads) {
+    const size_t t = fp8_tiles_upper_bound(num_seqs, total_tokens);
+    const size_t hd = static_cast<size_t>(num_heads) * kD;
+    Fp8Scratch s;
+    size_t off = 0;
+    s.q8 = off;  off += up256(static_cast<size_t>(total_tokens) * hd);
+    s.k8 = off;  off += up256(t * kBN * hd);
+    s.v8t = off; off += up256(t * kBN * hd);
+    s.qsc = off; off += up256(t * num_heads * sizeof(float));
+    s.ksc = off; off += up256(t * num_heads * sizeof(float));
+    s.vsc = off; off += up256(static_cast<size_t>(num_seqs) * hd * sizeof(float));
+    s.ws = off;  off += up256(fp8_quant_workspace_bytes(num_seqs, total_tokens, num_heads));
+    s.total = off;
+    return s;
+}
+
+}  // namespace
+
+bool fp8_attention_available() { return true; }
+
+size_t fp8_scratch_bytes(int num_seqs, int total_tokens, int num_heads, int head_dim) {
+    if (head_dim != kD) return 0;
+    return fp8_scratch_layout(num_seqs, total_tokens, num_heads).total;
+}
+
+hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                           int64_t qs, int64_t ks, int64_t vs, int64_t os, const int32_t* cu,
+                           const int32_t* cu_host, const int32_t* items, int64_t num_items,
+                           int num_seqs, int total_tokens, int num_heads, int head_dim,
+                           float softmax_scale, int skip, float skip_threshold,
+                           int32_t* skip_counts, void* scratch, hipStream_t stream) {
+    if (head_dim != kD) return hipErrorInvalidValue;
+    if (num_items <= 0 || num_seqs <= 0) return hipSuccess;
+    int64_t tiles = 0;
+    for (int s = 0; s < num_seqs; ++s) tiles += (cu_host[s + 1] - cu_host[s] + kBN - 1) / kBN;
+    const Fp8Scratch L = fp8_scratch_layout(num_seqs, total_tokens, num_heads);
+    char* base = static_cast<char*>(scratch);
+    uint8_t* q8 = reinterpret_cast<uint8_t*>(base + L.q8);
+    uint8_t* k8 = reinterpret_cast<uint8_t*>(base + L.k8);
+    uint8_t* v8t = reinterpret_cast<uint8_t*>(base + L.v8t);
+    float* qsc = reinterpret_cast<float*>(base + L.qsc);
+    float* ksc = reinterpret_cast<float*>(base + L.ksc);
+    float* vsc = reinterpret_cast<float*>(base + L.vsc);
+    void* ws = base + L.ws;
+    hipError_t e = launch_fp8_quantize(q, k, v, qs, ks, vs, cu, num_seqs, num_heads, tiles, q8, k8,
+                                       v8t, qsc, ksc, vsc, ws, stream);
+    if (e != hipSuccess) return e;
+    const int32_t* tb = static_cast<const int32_t*>(ws);   // tile prefix sums from the quantise pass
+    hipLaunchKernelGGL(attn_fp8_kernel, dim3(static_cast<unsigned>(num_items)), dim3(kThreads), 0,
+                       stream, q8, k8, v8t, qsc, ksc, vsc, o, os, cu, tb,
+                       reinterpret_cast<const int4*>(items), num_seqs, total_tokens, num_heads,
+                       tiles, softmax_scale * kLog2e, skip, skip_threshold * kLog2e, skip_counts);
+    return hipGetLastError();
 }
 
 }  // namespace h3

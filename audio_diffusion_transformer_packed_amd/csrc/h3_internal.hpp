@@ -22,7 +22,16 @@ hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t
                             int num_seqs, int total_tokens, int num_heads, int head_dim,
                             float softmax_scale, hipStream_t stream);
 
-// fp8 quantisation + fp8 attention (attn_fp8.hip)
+// fp8 quantisation (fp8_quant.hip): Q/K block codes, V channel codes, scales
+size_t fp8_tiles_upper_bound(int num_seqs, int total_tokens);
+size_t fp8_quant_workspace_bytes(int num_seqs, int total_tokens, int num_heads);
+hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t qs,
+                               int64_t ks, int64_t vs, const int32_t* cu, int num_seqs,
+                               int num_heads, int64_t num_tiles, uint8_t* q8, uint8_t* k8,
+                               uint8_t* v8t, float* qsc, float* ksc, float* vsc, void* workspace,
+                               hipStream_t stream);
+
+// fp8 attention over the quantised codes (attn_fp8.hip)
 bool fp8_attention_available();
 size_t fp8_scratch_bytes(int num_seqs, int total_tokens, int num_heads, int head_dim);
 hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -307,6 +307,67 @@ H3_API h3_status h3_attn_varlen(const void* q, const void* k, const void* v, voi
                          head_dim, opts, workspace, static_cast<hipStream_t>(hip_stream));
 }
 
+H3_API h3_status h3_fp8_num_tiles(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                  int64_t* tiles_out) {
+    if (tiles_out == nullptr) return fail(H3_ERR_INVALID_ARGUMENT, "tiles_out is NULL");
+    if (cu_seqlens_host == nullptr || num_seqs < 0)
+        return fail(H3_ERR_INVALID_ARGUMENT, "bad cu_seqlens_host / num_seqs");
+    h3_status st = check_cu(cu_seqlens_host, num_seqs, cu_seqlens_host[num_seqs]);
+    if (st != H3_OK) return st;
+    *tiles_out = count_items(cu_seqlens_host, num_seqs, 1, H3_FP8_QK_BLOCK);
+    return ok();
+}
+
+H3_API size_t h3_fp8_quantize_workspace_size(int32_t num_seqs, int32_t total_tokens,
+                                             int32_t num_heads) {
+    if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0) return 0;
+    return align_up(h3::fp8_quant_workspace_bytes(num_seqs, total_tokens, num_heads));
+}
+
+H3_API h3_status h3_fp8_quantize(const void* q, const void* k, const void* v,
+                                 int64_t q_tok_stride, int64_t k_tok_stride,
+                                 int64_t v_tok_stride, const int32_t* cu_seqlens_dev,
+                                 const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                 int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                 void* q8, void* k8, void* v8t, float* q_scale,
+                                 float* k_scale, float* v_scale, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+    h3_status st = check_cu(cu_seqlens_host, num_seqs, total_tokens);
+    if (st != H3_OK) return st;
+    if (num_heads <= 0) return fail(H3_ERR_INVALID_ARGUMENT, "num_heads=%d <= 0", num_heads);
+    if (head_dim != 128) return fail(H3_ERR_UNSUPPORTED, "fp8 quantisation needs head_dim 128 (got %d)", head_dim);
+    if (total_tokens == 0) return ok();
+    if (!q || !k || !v || !cu_seqlens_dev || !q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    const int64_t row = static_cast<int64_t>(num_heads) * head_dim;
+    if (q_tok_stride < row || k_tok_stride < row || v_tok_stride < row)
+        return fail(H3_ERR_INVALID_ARGUMENT, "token strides must be >= num_heads * head_dim = %lld",
+                    (long long)row);
+    if ((q_tok_stride | k_tok_stride | v_tok_stride) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+         reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(q8) |
+         reinterpret_cast<uintptr_t>(k8) | reinterpret_cast<uintptr_t>(v8t)) & 15)
+        return fail(H3_ERR_UNSUPPORTED, "q/k/v and the code buffers must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+         reinterpret_cast<uintptr_t>(v_scale)) & 3)
+        return fail(H3_ERR_INVALID_ARGUMENT, "scale buffers must be 4-byte aligned");
+    const size_t need = h3_fp8_quantize_workspace_size(num_seqs, total_tokens, num_heads);
+    if (workspace_bytes < need || workspace == nullptr)
+        return fail(H3_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+        return fail(H3_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const int64_t tiles = count_items(cu_seqlens_host, num_seqs, 1, H3_FP8_QK_BLOCK);
+    hipError_t e = h3::launch_fp8_quantize(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), q_tok_stride, k_tok_stride, v_tok_stride, cu_seqlens_dev,
+        num_seqs, num_heads, tiles, static_cast<uint8_t*>(q8), static_cast<uint8_t*>(k8),
+        static_cast<uint8_t*>(v8t), q_scale, k_scale, v_scale, workspace,
+        static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "fp8 quantise launch");
+    return ok();
+}
+
 H3_API h3_status h3_qk_rmsnorm_rope(void* q, void* k, int64_t q_tok_stride,
                                     int64_t k_tok_stride, const void* w_q, const void* w_k,
                                     const int32_t* rope_grid, int32_t total_tokens,

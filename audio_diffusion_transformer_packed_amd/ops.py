@@ -140,6 +140,46 @@ def attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
     return out
 
 
+def fp8_num_tiles(cu_host) -> int:
+    """T = sum over segments of ceil(L_s / 64): the key tiles of the fp8 layouts."""
+    cu = _host_cu(cu_host)
+    count = C.c_int64(0)
+    check(lib().h3_fp8_num_tiles(cu.ctypes.data_as(C.c_void_p), cu.size - 1, C.byref(count)))
+    return count.value
+
+
+def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                 cu_host, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """e4m3 codes and scales of q, k, v [N, H, 128] bf16 (layouts in h3dit.h):
+    q8 [N, H, 128], k8 [H, T, 64, 128], v8t [H, T, 128, 64] (uint8),
+    q_scale / k_scale [T, H], v_scale [B, H, 128] (float32)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, BF16, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    n, heads, d = q.shape
+    strides = [_token_view(t, nm, heads, d) for nm, t in (("q", q), ("k", k), ("v", v))]
+    cu = _host_cu(cu_host)
+    b = cu.size - 1
+    t = fp8_num_tiles(cu)
+    u8 = torch.uint8
+    out = {
+        "q8": torch.empty((n, heads, d), dtype=u8, device=dev),
+        "k8": torch.empty((heads, t, L.H3_FP8_QK_BLOCK, d), dtype=u8, device=dev),
+        "v8t": torch.empty((heads, t, d, L.H3_FP8_QK_BLOCK), dtype=u8, device=dev),
+        "q_scale": torch.empty((t, heads), dtype=torch.float32, device=dev),
+        "k_scale": torch.empty((t, heads), dtype=torch.float32, device=dev),
+        "v_scale": torch.empty((b, heads, d), dtype=torch.float32, device=dev),
+    }
+    ws = _workspace(lib().h3_fp8_quantize_workspace_size(b, n, heads), dev, workspace)
+    check(lib().h3_fp8_quantize(_ptr(q), _ptr(k), _ptr(v), *strides, _ptr(cu_seqlens),
+                                cu.ctypes.data_as(C.c_void_p), b, n, heads, d, _ptr(out["q8"]),
+                                _ptr(out["k8"]), _ptr(out["v8t"]), _ptr(out["q_scale"]),
+                                _ptr(out["k_scale"]), _ptr(out["v_scale"]), _ptr(ws), ws.numel(),
+                                _stream(dev)))
+    return out
+
+
 # --------------------------------------------------------------------------
 # Per-block fused operators
 # --------------------------------------------------------------------------

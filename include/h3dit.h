@@ -163,6 +163,44 @@ H3_API h3_status h3_attn_varlen(const void* q, const void* k, const void* v, voi
                                 size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * fp8 quantisation of Q, K and V, the first step of the fp8 attention path
+ * ([FastH3-EN] sparse & quantized attention bullet; [FastH3-ZH] section
+ * "其他加速路径：有损但可控": SAGE runs the attention computation in FP8).
+ * h3_attn_varlen with H3_ATTN_FP8_E4M3 runs it internally; it is exported so
+ * the codes can be inspected and reused.
+ *
+ * Format OCP e4m3fn (max 448). scale = amax / 448 (1 when amax == 0),
+ * code = round-to-nearest-even(x / scale) clamped to +-448, the division in
+ * IEEE fp32. Q and K: one scale per (64-token block aligned to the segment
+ * start, head); V: one scale per (segment, head, channel). head_dim must be
+ * 128. q, k, v as for h3_attn_varlen (bf16, token strides in elements,
+ * multiples of 8, 16-byte aligned). T = sum over segments of ceil(L_s / 64)
+ * (h3_fp8_num_tiles); block j of segment s is tile tile_cu64[s] + j.
+ * Outputs (device, caller-owned):
+ *   q8      uint8 [total_tokens, num_heads, 128], token-major;
+ *   k8      uint8 [num_heads, T, 64, 128]: 64-token key tiles, rows past a
+ *           segment's end are 0;
+ *   v8t     uint8 [num_heads, T, 128, 64]: V transposed per tile; key
+ *           32b + 8i + 4g + e of a tile (b, g in {0, 1}; i, e in 0..3) is at
+ *           position 32g + 16b + 4i + e of its 64-byte channel row;
+ *   q_scale, k_scale float [T, num_heads]; v_scale float [num_seqs,
+ *           num_heads, 128].
+ * Needs a workspace of h3_fp8_quantize_workspace_size(...) bytes.
+ * ---------------------------------------------------------------------- */
+H3_API h3_status h3_fp8_num_tiles(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                  int64_t* tiles_out);
+H3_API size_t h3_fp8_quantize_workspace_size(int32_t num_seqs, int32_t total_tokens,
+                                             int32_t num_heads);
+H3_API h3_status h3_fp8_quantize(const void* q, const void* k, const void* v,
+                                 int64_t q_tok_stride, int64_t k_tok_stride,
+                                 int64_t v_tok_stride, const int32_t* cu_seqlens_dev,
+                                 const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                 int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                 void* q8, void* k8, void* v8t, float* q_scale,
+                                 float* k_scale, float* v_scale, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Fused Q/K RMSNorm + 3D RoPE, in place ([FastH3-ZH] "融合 DiT 算子": the
  * Q/K normalisation is merged with RoPE).
  *

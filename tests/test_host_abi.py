@@ -204,3 +204,39 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(RuntimeError, match="build the HIP library"):
         L.lib()
+
+
+def test_fp8_num_tiles_and_workspace(lib):
+    cu, cup = _cu([0, 1, 65, 65, 193])
+    t = C.c_int64(-1)
+    assert lib.h3_fp8_num_tiles(cup, 4, C.byref(t)) == L.H3_OK and t.value == 4
+    bad, badp = _cu([0, 5, 3])
+    assert lib.h3_fp8_num_tiles(badp, 2, C.byref(t)) == L.H3_ERR_INVALID_ARGUMENT
+    assert lib.h3_fp8_num_tiles(cup, 4, None) == L.H3_ERR_INVALID_ARGUMENT
+    small = lib.h3_fp8_quantize_workspace_size(1, 100, 2)
+    big = lib.h3_fp8_quantize_workspace_size(1, 100000, 24)
+    assert 0 < small < big and small % 256 == 0
+    assert lib.h3_fp8_quantize_workspace_size(1, 100, 0) == 0
+
+
+def test_fp8_quantize_argument_errors(lib):
+    """Every case is rejected on the host before any launch (fake aligned
+    device addresses are never dereferenced)."""
+    cu, cup = _cu([0, 10])
+    fake = C.c_void_p(1 << 20)
+    ws_ok = lib.h3_fp8_quantize_workspace_size(1, 10, 2)
+
+    def call(d=128, q=fake, stride=256, ws=ws_ok, k8=fake, n=10, cu_p=cup, align=0):
+        qq = C.c_void_p(q.value + align) if q is not None and q.value else q
+        return lib.h3_fp8_quantize(qq, fake, fake, stride, stride, stride, fake, cu_p, 1, n, 2, d,
+                                   fake, k8, fake, fake, fake, fake, fake, ws, None)
+    assert call(d=64) == L.H3_ERR_UNSUPPORTED
+    assert call(q=C.c_void_p(0)) == L.H3_ERR_INVALID_ARGUMENT
+    assert call(k8=C.c_void_p(0)) == L.H3_ERR_INVALID_ARGUMENT
+    assert call(stride=200) == L.H3_ERR_INVALID_ARGUMENT
+    assert call(stride=260) == L.H3_ERR_UNSUPPORTED
+    assert call(align=8) == L.H3_ERR_UNSUPPORTED
+    assert call(ws=ws_ok - 1) == L.H3_ERR_WORKSPACE_TOO_SMALL
+    assert call(n=11) == L.H3_ERR_INVALID_ARGUMENT            # cu[B] != total_tokens
+    zcu, zcup = _cu([0, 0])
+    assert call(n=0, cu_p=zcup) == L.H3_OK                    # nothing to do, nothing launched
