@@ -148,11 +148,23 @@ def fp8_num_tiles(cu_host) -> int:
     return count.value
 
 
+def attn_workspace_bytes(cu_host, total_tokens: int, num_heads: int, head_dim: int,
+                         precision: str = "bf16") -> int:
+    """Workspace bytes h3_attn_varlen needs for these sizes and precision."""
+    cu = _host_cu(cu_host)
+    prec = {"bf16": L.H3_ATTN_BF16, "fp8": L.H3_ATTN_FP8_E4M3}[precision]
+    opts = AttnOpts(prec, 0, 0.0, 0.0, None)
+    return lib().h3_attn_varlen_workspace_size(cu.size - 1, total_tokens, num_heads, head_dim,
+                                               C.byref(opts))
+
+
 def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
-                 cu_host, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+                 cu_host, out: Optional[Dict[str, torch.Tensor]] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """e4m3 codes and scales of q, k, v [N, H, 128] bf16 (layouts in h3dit.h):
     q8 [N, H, 128], k8 [H, T, 64, 128], v8t [H, T, 128, 64] (uint8),
-    q_scale / k_scale [T, H], v_scale [B, H, 128] (float32)."""
+    q_scale / k_scale [T, H], v_scale [B, H, 128] (float32). `out` may hold
+    buffers of those shapes from an earlier call."""
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, BF16, dev)
@@ -163,7 +175,11 @@ def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: 
     b = cu.size - 1
     t = fp8_num_tiles(cu)
     u8 = torch.uint8
-    out = {
+    if out is not None:
+        _need(out["q8"], "q8", u8, dev)
+        if tuple(out["k8"].shape) != (heads, t, L.H3_FP8_QK_BLOCK, d):
+            raise ValueError("out buffers do not match these sizes")
+    out = out if out is not None else {
         "q8": torch.empty((n, heads, d), dtype=u8, device=dev),
         "k8": torch.empty((heads, t, L.H3_FP8_QK_BLOCK, d), dtype=u8, device=dev),
         "v8t": torch.empty((heads, t, d, L.H3_FP8_QK_BLOCK), dtype=u8, device=dev),

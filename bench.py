@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "varlen attention TFLOP/s + DiT-block ms at 58k packed tokens; % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 ATTN_SRC = os.path.join(ROOT, "audio_diffusion_transformer_packed_amd", "csrc", "attn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_block_10s_58k_traffic.json")
 
@@ -126,6 +127,7 @@ def main():
     ap.add_argument("--workload", default="block_10s_58k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this hot path runs on one GPU; --gpus must be 1 "
@@ -244,6 +246,45 @@ def main():
                                                     out=taps["h2"]), it),
             flops=2.0 * n * wl.ffn * c)
 
+    fp8 = None
+    if not args.no_fp8:
+        log("timing fp8 attention")
+        it = max(3, args.steps)
+        o8 = torch.empty_like(o_att)
+        fp8_ws = torch.empty(ops.attn_workspace_bytes(cu, n, wl.heads, wl.head_dim, "fp8"),
+                             dtype=torch.uint8, device=dev)
+        n_items = ops.attn_num_items(cu, wl.heads)
+        counts = torch.zeros(n_items, dtype=torch.int32, device=dev)
+
+        def fp8_attn(skip):
+            return ops.attn_varlen(qv, kv, vv, cu_d, cu, out=o8, precision="fp8",
+                                   skip_softmax=skip, skip_counts=counts, workspace=fp8_ws)
+        fp8_attn(False)
+        ms_fp8 = timer(lambda: fp8_attn(False), it)
+        fp8_attn(True)
+        ms_fp8_skip = timer(lambda: fp8_attn(True), it)
+        skipped = int(counts.sum().item())
+        pairs = wl.heads * sum(((L + 31) // 32) * ((L + 63) // 64) for L in wl.lengths)
+        qbufs = ops.fp8_quantize(qv, kv, vv, cu_d, cu)
+        qws = torch.empty(max(1 << 20, ops.lib().h3_fp8_quantize_workspace_size(b, n, wl.heads)),
+                          dtype=torch.uint8, device=dev)
+        ms_q = timer(lambda: ops.fp8_quantize(qv, kv, vv, cu_d, cu, out=qbufs, workspace=qws), it)
+        q_bytes = 3 * n * c * 2 + n * c * 2 + 3 * n * c
+        ms_k = ms_fp8 - ms_q
+        fp8 = {"workload": "attn_fp8_10s_58k shape on the block's q/k/v",
+               "quantize_ms": round(ms_q, 4),
+               "quantize_gbs": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
+               "quantize_frac_hbm_peak": round(q_bytes / (ms_q * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+               "attention_ms": round(ms_fp8, 4),
+               "attention_dense_equiv_tflops": round(f_attn / (ms_fp8 * 1e-3) / 1e12, 2),
+               "attention_kernel_ms": round(ms_k, 4),
+               "attention_kernel_frac_fp8_peak": round(f_attn / (ms_k * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+               "skip_attention_ms": round(ms_fp8_skip, 4),
+               "skip_fraction": round(skipped / pairs, 5),
+               "skip_threshold": 8.0}
+        stages["fp8_quantize"] = {"ms": round(ms_q, 4), "gbs": fp8["quantize_gbs"],
+                                  "frac_hbm_peak": fp8["quantize_frac_hbm_peak"]}
+
     traffic = load_traffic()
     result = {
         "metric": METRIC,
@@ -272,6 +313,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
         "stages": stages,
+        "fp8_attention": fp8,
         "timed_wall_s": round(t_wall, 3),
     }
     if not args.no_cpu_baseline:
