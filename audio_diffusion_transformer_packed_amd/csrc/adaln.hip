@@ -6,8 +6,9 @@
 //    the 6C x C weight, one wave per weight row, every segment's cond is
 //    applied to the row while it is in registers;
 //  * RMSNorm + modulate: h[t] = RMSNorm(x[t]) * (1 + scale[seg(t)]) +
-//    shift[seg(t)]; one wave per token row, 16-byte coalesced loads, the
-//    row's sum of squares reduced across the wave, one bf16 rounding.
+//    shift[seg(t)]; one thread per 16-byte chunk of a row, a few rows per
+//    workgroup, the rows' sums of squares reduced through one LDS exchange,
+//    one bf16 rounding.
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -47,49 +48,79 @@ __global__ __launch_bounds__(kThreads) void modulation_kernel(
     }
 }
 
-template <int NCH>
-__global__ __launch_bounds__(kThreads) void adaln_kernel(
+// RMSNorm + modulate over kRows consecutive tokens per workgroup: one thread
+// per 16-byte chunk (8 channels) of a row, hidden / 8 threads, each thread
+// loading one chunk of each of the kRows rows (all loads in flight at once)
+// and storing one chunk of each output row. The rows' sums of squares are
+// reduced across the wave and then, once for all kRows rows, across the
+// workgroup through LDS. The thread's 8 shift / scale values stay in
+// registers for all its rows (reloaded only where a row changes segment).
+// x and h are streamed with nontemporal loads / stores (each byte is touched
+// once): at 57,960 x 3072 this reaches ~0.93x of a plain device copy of the
+// same bytes, against ~0.8x with cached accesses.
+constexpr int kRows = 4;
+
+__global__ __launch_bounds__(1024) void adaln_kernel(
     const uint16_t* __restrict__ x, uint16_t* __restrict__ h, const float* __restrict__ shift,
     const float* __restrict__ scale, int64_t mod_stride, const int32_t* __restrict__ cu,
     int num_seqs, int total_tokens, int hidden, float eps) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-    if (t >= total_tokens) return;
-    const int seg = num_seqs == 1 ? 0 : find_segment(cu, num_seqs, t);
-    const uint16_t* xp = x + t * hidden;
-    Chunk16 xc[NCH];
-    float ss = 0.f;
+    __shared__ float red[kRows][16];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRows;
+    const int c0 = 8 * tid;
+    Chunk16 xc[kRows];
+    float ss[kRows];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        xc[i].u = *reinterpret_cast<const uint4*>(xp + (i * 64 + lane) * 8);
+    for (int r = 0; r < kRows; ++r) {
+        ss[r] = 0.f;
+        if (t0 + r < total_tokens) {
+            xc[r].u = load_stream16(x + (t0 + r) * hidden + c0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float f = bf2f(xc[i].h[e]);
-            ss = fmaf(f, f, ss);
+            for (int e = 0; e < 8; ++e) {
+                const float f = bf2f(xc[r].h[e]);
+                ss[r] = fmaf(f, f, ss[r]);
+            }
         }
     }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(fmaf(ss, 1.0f / hidden, eps));
-    const float* shp = shift + static_cast<int64_t>(seg) * mod_stride;
-    const float* scp = scale + static_cast<int64_t>(seg) * mod_stride;
-    uint16_t* hp = h + t * hidden;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c0 = (i * 64 + lane) * 8;
-        const float4 sh0 = *reinterpret_cast<const float4*>(shp + c0);
-        const float4 sh1 = *reinterpret_cast<const float4*>(shp + c0 + 4);
-        const float4 sc0 = *reinterpret_cast<const float4*>(scp + c0);
-        const float4 sc1 = *reinterpret_cast<const float4*>(scp + c0 + 4);
-        const float shv[8] = {sh0.x, sh0.y, sh0.z, sh0.w, sh1.x, sh1.y, sh1.z, sh1.w};
-        const float scv[8] = {sc0.x, sc0.y, sc0.z, sc0.w, sc1.x, sc1.y, sc1.z, sc1.w};
+    for (int r = 0; r < kRows; ++r) {
+        ss[r] = wave_sum(ss[r]);
+        if (lane == 0) red[r][wave] = ss[r];
+    }
+    __syncthreads();
+    int seg_loaded = -1;
+    float shv[8], scv[8];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t t = t0 + r;
+        if (t >= total_tokens) break;
+        float tot = 0.f;
+        for (int w = 0; w < nwaves; ++w) tot += red[r][w];
+        const float rinv = 1.0f / sqrtf(fmaf(tot, 1.0f / hidden, eps));
+        const int seg = num_seqs == 1 ? 0 : find_segment(cu, num_seqs, t);
+        if (seg != seg_loaded) {
+            const float* shp = shift + static_cast<int64_t>(seg) * mod_stride + c0;
+            const float* scp = scale + static_cast<int64_t>(seg) * mod_stride + c0;
+            const float4 sh0 = *reinterpret_cast<const float4*>(shp);
+            const float4 sh1 = *reinterpret_cast<const float4*>(shp + 4);
+            const float4 sc0 = *reinterpret_cast<const float4*>(scp);
+            const float4 sc1 = *reinterpret_cast<const float4*>(scp + 4);
+            shv[0] = sh0.x; shv[1] = sh0.y; shv[2] = sh0.z; shv[3] = sh0.w;
+            shv[4] = sh1.x; shv[5] = sh1.y; shv[6] = sh1.z; shv[7] = sh1.w;
+            scv[0] = 1.0f + sc0.x; scv[1] = 1.0f + sc0.y; scv[2] = 1.0f + sc0.z; scv[3] = 1.0f + sc0.w;
+            scv[4] = 1.0f + sc1.x; scv[5] = 1.0f + sc1.y; scv[6] = 1.0f + sc1.z; scv[7] = 1.0f + sc1.w;
+            seg_loaded = seg;
+        }
         Chunk16 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float a = fmaf(bf2f(xc[i].h[2 * e]) * r, 1.0f + scv[2 * e], shv[2 * e]);
-            const float b = fmaf(bf2f(xc[i].h[2 * e + 1]) * r, 1.0f + scv[2 * e + 1], shv[2 * e + 1]);
+            const float a = fmaf(bf2f(xc[r].h[2 * e]) * rinv, scv[2 * e], shv[2 * e]);
+            const float b = fmaf(bf2f(xc[r].h[2 * e + 1]) * rinv, scv[2 * e + 1], shv[2 * e + 1]);
             out.w[e] = pack_bf16x2(a, b);
         }
-        *reinterpret_cast<uint4*>(hp + c0) = out.u;
+        store_stream16(h + t * hidden + c0, out.u);
     }
 }
 
@@ -114,21 +145,6 @@ hipError_t launch_modulation_nch(int nch, dim3 grid, hipStream_t stream, Args...
     return hipGetLastError();
 }
 
-template <typename... Args>
-hipError_t launch_adaln_nch(int nch, dim3 grid, hipStream_t stream, Args... args) {
-    switch (nch) {
-        H3_NCH_CASE(1, adaln_kernel) H3_NCH_CASE(2, adaln_kernel)
-        H3_NCH_CASE(3, adaln_kernel) H3_NCH_CASE(4, adaln_kernel)
-        H3_NCH_CASE(5, adaln_kernel) H3_NCH_CASE(6, adaln_kernel)
-        H3_NCH_CASE(7, adaln_kernel) H3_NCH_CASE(8, adaln_kernel)
-        H3_NCH_CASE(9, adaln_kernel) H3_NCH_CASE(10, adaln_kernel)
-        H3_NCH_CASE(11, adaln_kernel) H3_NCH_CASE(12, adaln_kernel)
-        H3_NCH_CASE(13, adaln_kernel) H3_NCH_CASE(14, adaln_kernel)
-        H3_NCH_CASE(15, adaln_kernel) H3_NCH_CASE(16, adaln_kernel)
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
 #undef H3_NCH_CASE
 
 }  // namespace
@@ -146,9 +162,11 @@ hipError_t launch_adaln(const uint16_t* x, uint16_t* h, const float* shift, cons
                         int64_t mod_stride, const int32_t* cu, int num_seqs, int total_tokens,
                         int hidden, float eps, hipStream_t stream) {
     if (total_tokens == 0) return hipSuccess;
-    const dim3 grid((total_tokens + 3) / 4);
-    return launch_adaln_nch(hidden / 512, grid, stream, x, h, shift, scale, mod_stride, cu,
-                            num_seqs, total_tokens, hidden, eps);
+    if (hidden % 512 != 0 || hidden > 8192) return hipErrorInvalidValue;
+    const dim3 grid((total_tokens + kRows - 1) / kRows);
+    hipLaunchKernelGGL(adaln_kernel, grid, dim3(hidden / 8), 0, stream, x, h, shift, scale,
+                       mod_stride, cu, num_seqs, total_tokens, hidden, eps);
+    return hipGetLastError();
 }
 
 }  // namespace h3

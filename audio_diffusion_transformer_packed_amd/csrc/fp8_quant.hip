@@ -122,8 +122,8 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ base, int
     }
 }
 
-// One workgroup per key tile: Q and K codes + block scales for every head,
-// and the per-tile channel amax of V (reduced per segment afterwards).
+// One workgroup per (key tile, head): Q and K codes + block scales, and the
+// tile's channel amax of V (reduced per segment afterwards).
 __global__ __launch_bounds__(256) void quant_qk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int64_t qs, int64_t ks, int64_t vs, const int32_t* __restrict__ cu,
@@ -132,75 +132,64 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
     float* __restrict__ ksc, float* __restrict__ vpart) {
     __shared__ float red[4];
     __shared__ float vred[4][kD];
-    const int tile = blockIdx.x;
+    const int tile = blockIdx.x, h = blockIdx.y;
     int seg, t0, rows;
     tile_origin(cu, tb, num_seqs, tile, seg, t0, rows);
     const int tid = threadIdx.x;
     const int64_t row_bytes = static_cast<int64_t>(num_heads) * kD;
-    for (int h = 0; h < num_heads; ++h) {
-        float x[4][8];
-        // ---- Q ----
-        load_tile(q, qs, t0, rows, h, x);
-        float m = 0.f;
+    float xq[4][8], xk[4][8], xv[4][8];
+    load_tile(q, qs, t0, rows, h, xq);
+    load_tile(k, ks, t0, rows, h, xk);
+    load_tile(v, vs, t0, rows, h, xv);
+    float mq = 0.f, mk = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[i][j]));
-        float amax = block_max(m, red);
-        float den = fp8_den_of(amax);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
-            const int tok = c >> 4, dc = c & 15;
-            if (tok < rows) {
-                u32x2 w;
-                w.x = codes4(x[i], 0, den);
-                w.y = codes4(x[i], 4, den);
-                *reinterpret_cast<u32x2*>(q8 + (t0 + tok) * row_bytes + h * kD + 8 * dc) = w;
-            }
-        }
-        if (tid == 0) qsc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax);
-        // ---- K (padded rows written as 0) ----
-        load_tile(k, ks, t0, rows, h, x);
-        m = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[i][j]));
-        amax = block_max(m, red);
-        den = fp8_den_of(amax);
-        uint8_t* kt = k8 + ((static_cast<int64_t>(h) * num_tiles + tile) * kTB) * kD;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
-            const int tok = c >> 4, dc = c & 15;
-            u32x2 w;
-            w.x = codes4(x[i], 0, den);
-            w.y = codes4(x[i], 4, den);
-            *reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc) = w;
-        }
-        if (tid == 0) ksc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax);
-        // ---- V: channel amax over this tile's tokens ----
-        load_tile(v, vs, t0, rows, h, x);
-        float vm[8];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float a = fmaxf(fmaxf(fabsf(x[0][j]), fabsf(x[1][j])), fmaxf(fabsf(x[2][j]), fabsf(x[3][j])));
-            // the 4 tokens tid/16 + 16 i share channel chunk tid % 16 with lanes tid ^ 16, tid ^ 32
-            a = fmaxf(a, __shfl_xor(a, 16, 64));
-            a = fmaxf(a, __shfl_xor(a, 32, 64));
-            vm[j] = a;
+            mq = fmaxf(mq, fabsf(xq[i][j]));
+            mk = fmaxf(mk, fabsf(xk[i][j]));
         }
-        if ((tid & 63) < 16) {
+    const float amax_q = block_max(mq, red);
+    const float amax_k = block_max(mk, red);
+    const float dq = fp8_den_of(amax_q), dk = fp8_den_of(amax_k);
+    uint8_t* kt = k8 + ((static_cast<int64_t>(h) * num_tiles + tile) * kTB) * kD;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) vred[tid >> 6][8 * (tid & 15) + j] = vm[j];
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i;
+        const int tok = c >> 4, dc = c & 15;
+        if (tok < rows) {
+            u32x2 w;
+            w.x = codes4(xq[i], 0, dq);
+            w.y = codes4(xq[i], 4, dq);
+            *reinterpret_cast<u32x2*>(q8 + (t0 + tok) * row_bytes + h * kD + 8 * dc) = w;
         }
-        __syncthreads();
-        if (tid < kD) {
-            const float a = fmaxf(fmaxf(vred[0][tid], vred[1][tid]), fmaxf(vred[2][tid], vred[3][tid]));
-            vpart[(static_cast<int64_t>(tile) * num_heads + h) * kD + tid] = a;
-        }
-        __syncthreads();
+        u32x2 w;                              // K rows past the segment end are 0
+        w.x = codes4(xk[i], 0, dk);
+        w.y = codes4(xk[i], 4, dk);
+        *reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc) = w;
+    }
+    if (tid == 0) {
+        qsc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_q);
+        ksc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_k);
+    }
+    // V: channel amax over this tile's tokens; the 4 tokens tid / 16 + 16 i
+    // share channel chunk tid % 16 with lanes tid ^ 16 and tid ^ 32
+    float vm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float a = fmaxf(fmaxf(fabsf(xv[0][j]), fabsf(xv[1][j])), fmaxf(fabsf(xv[2][j]), fabsf(xv[3][j])));
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        a = fmaxf(a, __shfl_xor(a, 32, 64));
+        vm[j] = a;
+    }
+    if ((tid & 63) < 16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vred[tid >> 6][8 * (tid & 15) + j] = vm[j];
+    }
+    __syncthreads();
+    if (tid < kD) {
+        const float a = fmaxf(fmaxf(vred[0][tid], vred[1][tid]), fmaxf(vred[2][tid], vred[3][tid]));
+        vpart[(static_cast<int64_t>(tile) * num_heads + h) * kD + tid] = a;
     }
 }
 
@@ -288,7 +277,7 @@ hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint1
     float* vamax = reinterpret_cast<float*>(static_cast<char*>(workspace) + tb_bytes);
     float* vpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + tb_bytes + va_bytes);
     hipLaunchKernelGGL(tile64_scan_kernel, dim3(1), dim3(1024), 0, stream, cu, num_seqs, tb);
-    hipLaunchKernelGGL(quant_qk_kernel, dim3(static_cast<unsigned>(num_tiles)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(quant_qk_kernel, dim3(static_cast<unsigned>(num_tiles), num_heads), dim3(256), 0, stream,
                        q, k, v, qs, ks, vs, cu, tb, num_seqs, num_heads, num_tiles, q8, k8, qsc, ksc,
                        vpart);
     hipLaunchKernelGGL(vscale_kernel, dim3(num_seqs, num_heads * kD / 32), dim3(1024), 0, stream,

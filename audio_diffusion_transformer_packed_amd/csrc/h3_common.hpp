@@ -34,6 +34,14 @@ union Chunk8 {
     uint32_t w[2];
 };
 
+// Streaming (nontemporal) 16-byte global access for data touched once.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+__device__ __forceinline__ void store_stream16(void* p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
