@@ -20,8 +20,10 @@
 //    stores, no LDS round trip in the epilogue);
 //  * tiles move global -> LDS with global_load_lds_dwordx4 (no staging
 //    registers), double buffered; each wave instruction fills 1 KB = 8 rows
-//    of 64 bf16, with the 16-byte chunks of row r stored at chunk ^ (r % 8) so
-//    the fragment reads (32 rows x one chunk) spread over all LDS banks;
+//    of 64 bf16, with the 16-byte chunks of row r stored at chunk ^ ((r / 2)
+//    % 8): a 16-lane phase of a fragment read (16 consecutive rows, one
+//    logical chunk) then covers 2 row parities x 8 chunk slots = all 64
+//    banks once (chunk ^ (r % 8) would put rows r and r + 8 on the same banks);
 //  * SwiGLU: the W tile interleaves 32-row blocks of Wg and Wu, so the gate
 //    and up accumulators of one output sit in the same lane;
 //  * workgroup ids are remapped so each XCD (ids are dealt round-robin over
@@ -85,14 +87,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     constexpr int OUT_N = EPI == kEpiSwiGLU ? kBN / 2 : kBN;
     const int64_t n0 = static_cast<int64_t>(tn) * OUT_N;
 
-    // ---- per-lane DMA sources: wave w fills tile rows 64 w + 8 i + lane/8 ----
+    // ---- per-lane DMA sources: wave w fills tile rows 64 w + 8 i + lane/8;
+    // the lane's LDS slot is physical chunk lane % 8, which holds logical
+    // chunk (lane % 8) ^ ((row / 2) % 8) ----
     const int rl = lane >> 3;
-    const int chunk = (lane & 7) ^ rl;            // row % 8 == rl for these rows
     const uint16_t* asrc[8];
     const uint16_t* wsrc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = 64 * wave + 8 * i + rl;     // tile row
+        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
         int64_t am = m0 + r;
         if (am >= M) am = M - 1;                  // clamped rows are computed, never stored
         asrc[i] = A + am * K + 8 * chunk;
@@ -123,9 +127,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    // fragment read offsets: row R (tile row), chunk c -> R * 128 + 16 * (c ^ (R % 8))
-    // rows used by this lane: 128 w* + 32 b + l32, so R % 8 == l32 % 8
-    const int rsw = l32 & 7;
+    // fragment read offsets: row R (tile row), chunk c -> R * 128 + 16 * (c ^ ((R / 2) % 8))
+    // rows used by this lane: 128 w* + 32 b + l32, so (R / 2) % 8 == (l32 / 2) % 8
+    const int rsw = (l32 >> 1) & 7;
     const int wrow0 = (128 * wn + l32) * 128;
     const int arow0 = (128 * wm + l32) * 128;
 
