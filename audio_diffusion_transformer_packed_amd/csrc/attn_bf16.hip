@@ -19,9 +19,11 @@
 //  * O^T = V^T P^T: P stays in registers, converted to bf16 directly in the
 //    MFMA operand layout; V^T fragments come from row-major V in LDS through
 //    ds_read_b64_tr_b16 (transposing 16-lane read);
-//  * K and V tiles of 64 keys move global -> LDS with global_load_lds_dwordx4
-//    (no staging registers), double buffered, with XOR-swizzled 16-byte
-//    chunks so both fragment reads are free of bank conflicts;
+//  * K and V tiles of 64 keys move global -> LDS with buffer_load_dwordx4
+//    ... lds (no staging registers; the tile base lives in scalar registers,
+//    so the DMA costs no vector address arithmetic), double buffered, with
+//    XOR-swizzled 16-byte chunks so both fragment reads are free of bank
+//    conflicts;
 //  * each key tile: S^T MFMAs, softmax, P V MFMAs, while the next tile's K
 //    and V stream into the other LDS stage; the two waves of a SIMD overlap
 //    one wave's softmax with the other's MFMAs;
@@ -29,7 +31,8 @@
 //    lane's partial sum of exp2 values exceeds 2^16 (or is infinite):
 //    then the tile's true max is taken, O and l are rescaled and the tile's
 //    p recomputed. Between such events p <= 2^16 and O is never touched; the
-//    final O / l is the same softmax.
+//    final O / l is the same softmax. Row sums use fp32 adds, not v_dot2,
+//    which would occupy the matrix pipe.
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -60,10 +63,16 @@ template <int D> __device__ __forceinline__ int vswz(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                              reinterpret_cast<uintptr_t>(lds_dst)),
-                                     16, 0, 0);
+// Buffer resource word 3 for raw (untyped, stride 0) access on gfx9-family
+// parts: 32-bit data format; out-of-range loads return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS at lds_dst
+// (lane i writes lds_dst + 16 i), no staging registers.
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_dst)),
+        16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
@@ -114,39 +123,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
         }
     }
 
-    // ---- DMA sources: instruction i of a tile fills rows RPI*i .. RPI*i+RPI-1;
+    // ---- DMA: instruction i of a tile fills rows RPI*i .. RPI*i+RPI-1;
     // this wave issues i = NI*wave + j; lane -> row RPI*i + lane/CPR, physical
     // chunk lane % CPR, which holds logical chunk (lane % CPR) ^ swizzle(row).
-    // Rows past the segment end are clamped to its last row (finite data of
-    // this segment); their scores are masked to -inf in the last tile.
+    // A buffer resource based at the tile's first row (scalar registers) and
+    // sized to the segment's remaining rows makes every tile one code path:
+    // rows past the segment end are out of range and load as zeros, and
+    // their scores are masked to -inf in the last tile.
     const uint16_t* kbase = k + static_cast<int64_t>(head) * D;
     const uint16_t* vbase = v + static_cast<int64_t>(head) * D;
-    int drow[C::NI];
     uint32_t koffb[C::NI], voffb[C::NI];      // byte offsets from the tile's first row
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
-        drow[j] = C::RPI * (C::NI * wave + j) + lane / CPR;
-        koffb[j] = static_cast<uint32_t>((drow[j] * ks + 8 * ((lane % CPR) ^ kswz<D>(drow[j]))) * 2);
-        voffb[j] = static_cast<uint32_t>((drow[j] * vs + 8 * ((lane % CPR) ^ vswz<D>(drow[j]))) * 2);
+        const int drow = C::RPI * (C::NI * wave + j) + lane / CPR;
+        koffb[j] = static_cast<uint32_t>((drow * ks + 8 * ((lane % CPR) ^ kswz<D>(drow))) * 2);
+        voffb[j] = static_cast<uint32_t>((drow * vs + 8 * ((lane % CPR) ^ vswz<D>(drow))) * 2);
     }
-    // Full tiles: wave-uniform row base (scalar) + per-lane 32-bit offset.
-    // The last, partial tile clamps rows past the segment end to its last row.
     auto dma = [&](const uint16_t* base, int64_t stride, const uint32_t (&offb)[C::NI], int tile,
                    char* dst) __attribute__((always_inline)) {
         const int key0 = kv0 + tile * kBN;
-        if (key0 + kBN <= kv1) {
-            const char* rb = reinterpret_cast<const char*>(base + static_cast<int64_t>(key0) * stride);
+        const int rows = min(kBN, kv1 - key0);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(base + static_cast<int64_t>(key0) * stride), 0,
+            static_cast<int>(rows * stride * 2), kBufferWord3);
 #pragma unroll
-            for (int j = 0; j < C::NI; ++j) lds_dma16(rb + offb[j], dst + (C::NI * wave + j) * 1024);
-        } else {
-#pragma unroll
-            for (int j = 0; j < C::NI; ++j) {
-                const int key = min(key0 + drow[j], kv1 - 1);
-                const uint32_t col = offb[j] - static_cast<uint32_t>(drow[j] * stride * 2);
-                lds_dma16(reinterpret_cast<const char*>(base + static_cast<int64_t>(key) * stride) + col,
-                          dst + (C::NI * wave + j) * 1024);
-            }
-        }
+        for (int j = 0; j < C::NI; ++j) buf_dma16(rsrc, offb[j], dst + (C::NI * wave + j) * 1024);
     };
     auto dma_k = [&](int tile, int stage) __attribute__((always_inline)) {
         dma(kbase, ks, koffb, tile, smem + stage * C::TILE);
@@ -209,15 +210,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     auto pexp = [&](const f32x16 (&s)[2], int r, float mb) __attribute__((always_inline)) {
         return __builtin_amdgcn_exp2f(fmaf(s[r >> 4][r & 15], scale_log2, -mb));
     };
-    // bf16 P in the B-operand layout: pf[b][t][e] = p of score 16 b + 8 t + e;
-    // the row sum accumulates the rounded pair (v_dot2_f32_bf16 against 1, 1),
-    // so l normalises exactly the weights that enter P V
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    // bf16 P in the B-operand layout: pf[b][t][e] = p of score 16 b + 8 t + e.
+    // The row sum adds the fp32 p with plain adds: v_dot2 (a dot on the
+    // rounded pair) would share the matrix pipe and stall the other wave's
+    // MFMAs, and the bf16 rounding of P is unbiased, so l of the unrounded p
+    // normalises the same softmax to well inside the bf16 error.
     auto put = [&](bf16x8 (&pf)[2][2], int r, float v0, float v1, float& sum) __attribute__((always_inline)) {
         const bf16x2 pr = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
         pf[r >> 4][(r >> 3) & 1][r & 7] = pr[0];
         pf[r >> 4][(r >> 3) & 1][(r & 7) + 1] = pr[1];
-        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
+        sum += v0 + v1;
     };
 
     // plain exp / sum / bf16 of one tile's scores
