@@ -94,11 +94,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     // K stage 0, K stage 1, V stage 0, V stage 1
     __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
 
+    // work-item fields and segment bounds are workgroup-uniform: keep them in
+    // scalar registers (so the K / V buffer descriptors are scalar too)
     const int4 it = items[blockIdx.x];
-    const int head = it.x, seg = it.y, q0 = it.z, qlen = it.w;
+    const int head = __builtin_amdgcn_readfirstlane(it.x);
+    const int seg = __builtin_amdgcn_readfirstlane(it.y);
+    const int q0 = __builtin_amdgcn_readfirstlane(it.z);
+    const int qlen = __builtin_amdgcn_readfirstlane(it.w);
     if (seg < 0 || seg >= num_seqs || head < 0 || head >= num_heads) return;
-    const int kv0 = max(0, cu[seg]);
-    const int kv1 = min(total_tokens, cu[seg + 1]);
+    const int kv0 = max(0, __builtin_amdgcn_readfirstlane(cu[seg]));
+    const int kv1 = min(total_tokens, __builtin_amdgcn_readfirstlane(cu[seg + 1]));
     if (q0 < kv0 || qlen <= 0 || q0 + qlen > kv1) return;
     const int len = kv1 - kv0;
     const int ntiles = (len + kBN - 1) / kBN;
