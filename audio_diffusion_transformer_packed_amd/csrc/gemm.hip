@@ -18,8 +18,9 @@
 //    activation tile the B operand, so each lane ends up owning one output
 //    row and four consecutive output columns per register group (8-byte
 //    stores, no LDS round trip in the epilogue);
-//  * tiles move global -> LDS with global_load_lds_dwordx4 (no staging
-//    registers), double buffered; each wave instruction fills 1 KB = 8 rows
+//  * tiles move global -> LDS with buffer_load_dwordx4 ... lds (no staging
+//    registers; scalar buffer descriptors, so the loads cost no vector
+//    address arithmetic), double buffered; each wave instruction fills 1 KB = 8 rows
 //    of 64 bf16, with the 16-byte chunks of row r stored at chunk ^ ((r / 2)
 //    % 8): a 16-lane phase of a fragment read (16 consecutive rows, one
 //    logical chunk) then covers 2 row parities x 8 chunk slots = all 64
@@ -44,10 +45,17 @@ constexpr int kStageBytes = 2 * kTileBytes;    // W tile then activation tile
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                              reinterpret_cast<uintptr_t>(lds_dst)),
-                                     16, 0, 0);
+// Buffer resource word 3 for raw (untyped, stride 0) access on gfx9-family
+// parts: 32-bit data format; out-of-range loads return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 bytes per lane from buffer offset voff + soff straight into LDS at
+// lds_dst (lane i writes lds_dst + 16 i), no staging registers.
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int soff,
+                                          void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_dst)),
+        16, voff, soff, 0, 0);
 }
 
 // Tile id -> (row panel, column panel), XCD-aware and grouped.
@@ -87,37 +95,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     constexpr int OUT_N = EPI == kEpiSwiGLU ? kBN / 2 : kBN;
     const int64_t n0 = static_cast<int64_t>(tn) * OUT_N;
 
-    // ---- per-lane DMA sources: wave w fills tile rows 64 w + 8 i + lane/8;
-    // the lane's LDS slot is physical chunk lane % 8, which holds logical
-    // chunk (lane % 8) ^ ((row / 2) % 8) ----
+    // ---- DMA: wave w fills tile rows 64 w + 8 i + lane/8 (i = 0..7); the
+    // lane's LDS slot is physical chunk lane % 8, which holds logical chunk
+    // (lane % 8) ^ ((row / 2) % 8). Buffer descriptors based at the tile's
+    // first row live in scalar registers and are sized to the rows that
+    // exist: rows past M (or N) are out of range and load as zeros (their
+    // outputs are never stored). Per lane only a constant byte offset is
+    // kept; the K position is the scalar offset of each load.
     const int rl = lane >> 3;
-    const uint16_t* asrc[8];
-    const uint16_t* wsrc[8];
+    const int64_t a_rows = min<int64_t>(kBM, M - m0);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(A + m0 * K), 0, static_cast<int>(a_rows * K * 2), kBufferWord3);
+    constexpr int W_ROWS = EPI == kEpiSwiGLU ? kBN / 2 : kBN;   // W rows per operand matrix
+    const int64_t w_rows = min<int64_t>(W_ROWS, N - n0);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(W + n0 * K), 0, static_cast<int>(w_rows * K * 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>((EPI == kEpiSwiGLU ? W2 : W) + n0 * K), 0,
+        static_cast<int>(w_rows * K * 2), kBufferWord3);
+    uint32_t aoff[8], woff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = 64 * wave + 8 * i + rl;     // tile row
         const int chunk = (lane & 7) ^ ((r >> 1) & 7);
-        int64_t am = m0 + r;
-        if (am >= M) am = M - 1;                  // clamped rows are computed, never stored
-        asrc[i] = A + am * K + 8 * chunk;
-        // W rows past N are clamped the same way (their columns are not stored)
+        aoff[i] = static_cast<uint32_t>((r * K + 8 * chunk) * 2);
         if (EPI == kEpiSwiGLU) {
-            // W rows: [128 wn' + 32 bj + j]: bj even -> gate, odd -> up, for output
-            // column n0 + 64 wn' + 32 (bj / 2) + j
+            // W-tile row r = 128 wnp + 32 bj + j: bj even -> gate (W), odd -> up
+            // (W2), for output column n0 + 64 wnp + 32 (bj / 2) + j; the
+            // parity of bj is (i >= 4), uniform per instruction
             const int wnp = r >> 7, bj = (r >> 5) & 3, j = r & 31;
-            const int64_t col = min(n0 + 64 * wnp + 32 * (bj >> 1) + j, N - 1);
-            wsrc[i] = ((bj & 1) ? W2 : W) + col * K + 8 * chunk;
+            woff[i] = static_cast<uint32_t>(((64 * wnp + 32 * (bj >> 1) + j) * K + 8 * chunk) * 2);
         } else {
-            wsrc[i] = W + min(n0 + r, N - 1) * K + 8 * chunk;
+            woff[i] = static_cast<uint32_t>((r * K + 8 * chunk) * 2);
         }
     }
 
     auto issue = [&](int stage, int64_t k0) __attribute__((always_inline)) {
         char* base = smem + stage * kStageBytes;
+        const int kb = static_cast<int>(k0 * 2);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            lds_dma16(wsrc[i] + k0, base + (8 * wave + i) * 1024);
-            lds_dma16(asrc[i] + k0, base + kTileBytes + (8 * wave + i) * 1024);
+            buf_dma16(EPI == kEpiSwiGLU && i >= 4 ? rw2 : rw, woff[i], kb, base + (8 * wave + i) * 1024);
+            buf_dma16(ra, aoff[i], kb, base + kTileBytes + (8 * wave + i) * 1024);
         }
     };
 
