@@ -22,9 +22,10 @@
 //    wave, each lane owning one query row of S^T = K Q^T (lane % 32);
 //  * K tiles (64 keys x 128 B) and V^T tiles (128 channels x 64 B, keys
 //    already in the lanes' P order) are contiguous 8 KB blocks in HBM, moved
-//    to LDS with global_load_lds_dwordx4 (one instruction per wave and
-//    operand), double buffered, XOR-swizzled for conflict-free 16-byte
-//    fragment reads; no transposing reads are needed;
+//    to LDS with buffer_load_dwordx4 ... lds through scalar descriptors (one
+//    instruction per wave and operand, no vector address arithmetic), double
+//    buffered, XOR-swizzled for conflict-free 16-byte fragment reads; no
+//    transposing reads are needed;
 //  * P is converted to e4m3 in registers, already in the B-operand byte
 //    order of the P V MFMA; per tile a wave issues 4 + 4 fp8 MFMAs.
 #include "h3_common.hpp"
@@ -47,10 +48,17 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                              reinterpret_cast<uintptr_t>(lds_dst)),
-                                     16, 0, 0);
+// Buffer resource word 3 for raw (untyped, stride 0) access on gfx9-family
+// parts: 32-bit data format; out-of-range loads return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 bytes per lane from buffer offset voff + soff straight into LDS at
+// lds_dst (lane i writes lds_dst + 16 i), no staging registers.
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int soff,
+                                          void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_dst)),
+        16, voff, soff, 0, 0);
 }
 
 // Chunk swizzles (physical 16-byte chunk = logical chunk ^ swizzle(row)):
@@ -77,11 +85,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     __shared__ int32_t wskip[kWaves];
 
     const int tid = threadIdx.x;
+    // work-item fields and segment bounds are workgroup-uniform: keep them in
+    // scalar registers (so the tile buffer descriptors are scalar too)
     const int4 it = items[blockIdx.x];
-    const int head = it.x, seg = it.y, q0 = it.z, qlen = it.w;
+    const int head = __builtin_amdgcn_readfirstlane(it.x);
+    const int seg = __builtin_amdgcn_readfirstlane(it.y);
+    const int q0 = __builtin_amdgcn_readfirstlane(it.z);
+    const int qlen = __builtin_amdgcn_readfirstlane(it.w);
     bool ok = seg >= 0 && seg < num_seqs && head >= 0 && head < num_heads;
-    const int kv0 = ok ? max(0, cu[seg]) : 0;
-    const int kv1 = ok ? min(total_tokens, cu[seg + 1]) : 0;
+    const int kv0 = ok ? max(0, __builtin_amdgcn_readfirstlane(cu[seg])) : 0;
+    const int kv1 = ok ? min(total_tokens, __builtin_amdgcn_readfirstlane(cu[seg + 1])) : 0;
     ok = ok && q0 >= kv0 && qlen > 0 && q0 + qlen <= kv1;
     if (!ok) {
         if (skip_counts && tid == 0) skip_counts[blockIdx.x] = 0;
@@ -90,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const int len = kv1 - kv0;
     const int ntiles = (len + kBN - 1) / kBN;
     const int keys_left = len - (ntiles - 1) * kBN;
-    const int tbs = tb[seg];
+    const int tbs = __builtin_amdgcn_readfirstlane(tb[seg]);
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -125,12 +138,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const int krow = 8 * wave + (lane >> 3), vrow = 16 * wave + (lane >> 2);
     const uint32_t ksrc = krow * kD + 16 * ((lane & 7) ^ kswz(krow));
     const uint32_t vsrc = vrow * kBN + 16 * ((lane & 3) ^ vswz(vrow));
-    const uint8_t* kbase = k8 + (static_cast<int64_t>(head) * num_tiles + tbs) * kKT;
-    const uint8_t* vbase = v8t + (static_cast<int64_t>(head) * num_tiles + tbs) * kVT;
+    // one descriptor per operand covering this segment's tiles of this head;
+    // the tile is the scalar offset of each load
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(k8 + (static_cast<int64_t>(head) * num_tiles + tbs) * kKT), 0,
+        ntiles * kKT, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(v8t + (static_cast<int64_t>(head) * num_tiles + tbs) * kVT), 0,
+        ntiles * kVT, kBufferWord3);
     auto dma = [&](int tile, int stage) __attribute__((always_inline)) {
-        lds_dma16(kbase + static_cast<int64_t>(tile) * kKT + ksrc, smem + stage * kKT + 1024 * wave);
-        lds_dma16(vbase + static_cast<int64_t>(tile) * kVT + vsrc,
-                  smem + 2 * kKT + stage * kVT + 1024 * wave);
+        buf_dma16(rk, ksrc, tile * kKT, smem + stage * kKT + 1024 * wave);
+        buf_dma16(rv, vsrc, tile * kVT, smem + 2 * kKT + stage * kVT + 1024 * wave);
     };
 
     // LDS fragment offsets. K block b, k-step c: row 32b + l32, logical
