@@ -33,6 +33,8 @@
 //    p recomputed. Between such events p <= 2^16 and O is never touched; the
 //    final O / l is the same softmax. Row sums use fp32 adds, not v_dot2,
 //    which would occupy the matrix pipe.
+#include <type_traits>
+
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -302,14 +304,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 
     // Tile t sits in K / V stage t % 2. Iteration t: DMA tile t+1 into the
     // other stage, then S^T(t), softmax(t), P V(t) from this stage, then wait
-    // for the DMA and a barrier (one per tile).
+    // for the DMA and a barrier (one per tile). The loop runs two tiles per
+    // trip so each stage is a compile-time constant and the LDS stage offsets
+    // fold into the fragment reads' immediate offsets.
     dma_k(0, 0);
     dma_v(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int keys_left = len - (ntiles - 1) * kBN;
-    for (int t = 0; t < ntiles; ++t) {
-        const int stage = t & 1;
+    auto tile = [&](int t, auto stage_c) __attribute__((always_inline)) {
+        constexpr int stage = decltype(stage_c)::value;
         const bool last = t + 1 == ntiles;
         if (!last) {
             dma_k(t + 1, stage ^ 1);
@@ -324,6 +328,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        tile(t, std::integral_constant<int, 0>{});
+        if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- normalise and store: lane holds dims 32 db + 8 r4 + 4 g + [0, 4) ----
