@@ -12,8 +12,10 @@
 // works on the fp32 accumulator and rounds once to bf16.
 //
 // Design (CDNA4):
-//  * 256 x 256 output tile per workgroup, K step 64, four waves of 128 x 128
-//    (4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 accumulators per lane);
+//  * 256 x 256 output tile per workgroup, K step 64, eight waves (two per
+//    SIMD, so one wave's LDS waits are covered by the other's MFMAs), each
+//    128 activation rows x 64 W rows (2 x 4 blocks of
+//    v_mfma_f32_32x32x16_bf16, 128 accumulators per lane);
 //  * the MFMA computes C^T = W a^T: the W tile is the A operand, the
 //    activation tile the B operand, so each lane ends up owning one output
 //    row and four consecutive output columns per register group (8-byte
@@ -25,8 +27,9 @@
 //    % 8): a 16-lane phase of a fragment read (16 consecutive rows, one
 //    logical chunk) then covers 2 row parities x 8 chunk slots = all 64
 //    banks once (chunk ^ (r % 8) would put rows r and r + 8 on the same banks);
-//  * SwiGLU: the W tile interleaves 32-row blocks of Wg and Wu, so the gate
-//    and up accumulators of one output sit in the same lane;
+//  * SwiGLU: the W tile interleaves 32-row blocks of Wg and Wu, so each
+//    wave's 64 W rows are the gate and up blocks of the same 32 outputs and
+//    both accumulators of one output sit in the same lane;
 //  * workgroup ids are remapped so each XCD (ids are dealt round-robin over
 //    the 8 XCDs) gets a contiguous run of tiles, grouped 4 row-panels at a
 //    time, so concurrently running tiles share A and W panels in that XCD's L2.
@@ -39,7 +42,11 @@ namespace {
 constexpr int kBM = 256;          // activation rows per tile
 constexpr int kBN = 256;          // W rows per tile (output columns, or gate+up pairs)
 constexpr int kBK = 64;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;         // two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWN = 2;            // 32-row W blocks per wave (64 output columns, or one gate+up pair)
+constexpr int kWM = 4;            // 32-row activation blocks per wave (128 rows)
+constexpr int kDmaPerWave = kBM / 8 / kWaves;   // 1 KB DMA instructions per wave and operand
 constexpr int kTileBytes = kBM * kBK * 2;      // 32 KB per operand tile
 constexpr int kStageBytes = 2 * kTileBytes;    // W tile then activation tile
 constexpr int kGroupM = 4;
@@ -86,8 +93,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
-    const int wn = wave >> 1;     // W rows 128 wn .. (output columns)
-    const int wm = wave & 1;      // activation rows 128 wm ..
+    const int wn = wave >> 1;     // W-tile rows 64 wn .. 64 wn + 63
+    const int wm = wave & 1;      // activation rows 128 wm .. 128 wm + 127
 
     int tm, tn;
     tile_coords(blockIdx.x, gridDim.x, mtiles, ntiles, tm, tn);
@@ -113,16 +120,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>((EPI == kEpiSwiGLU ? W2 : W) + n0 * K), 0,
         static_cast<int>(w_rows * K * 2), kBufferWord3);
-    uint32_t aoff[8], woff[8];
+    uint32_t aoff[kDmaPerWave], woff[kDmaPerWave];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 64 * wave + 8 * i + rl;     // tile row
+    for (int i = 0; i < kDmaPerWave; ++i) {
+        const int r = 8 * kDmaPerWave * wave + 8 * i + rl;     // tile row
         const int chunk = (lane & 7) ^ ((r >> 1) & 7);
         aoff[i] = static_cast<uint32_t>((r * K + 8 * chunk) * 2);
         if (EPI == kEpiSwiGLU) {
             // W-tile row r = 128 wnp + 32 bj + j: bj even -> gate (W), odd -> up
-            // (W2), for output column n0 + 64 wnp + 32 (bj / 2) + j; the
-            // parity of bj is (i >= 4), uniform per instruction
+            // (W2), for output column n0 + 64 wnp + 32 (bj / 2) + j; a wave's
+            // rows share one bj (r / 32 = wave), so the matrix is wave-uniform
             const int wnp = r >> 7, bj = (r >> 5) & 3, j = r & 31;
             woff[i] = static_cast<uint32_t>(((64 * wnp + 32 * (bj >> 1) + j) * K + 8 * chunk) * 2);
         } else {
@@ -133,23 +140,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     auto issue = [&](int stage, int64_t k0) __attribute__((always_inline)) {
         char* base = smem + stage * kStageBytes;
         const int kb = static_cast<int>(k0 * 2);
+        const bool up = EPI == kEpiSwiGLU && (wave & 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            buf_dma16(EPI == kEpiSwiGLU && i >= 4 ? rw2 : rw, woff[i], kb, base + (8 * wave + i) * 1024);
-            buf_dma16(ra, aoff[i], kb, base + kTileBytes + (8 * wave + i) * 1024);
+        for (int i = 0; i < kDmaPerWave; ++i) {
+            buf_dma16(up ? rw2 : rw, woff[i], kb, base + (kDmaPerWave * wave + i) * 1024);
+            buf_dma16(ra, aoff[i], kb, base + kTileBytes + (kDmaPerWave * wave + i) * 1024);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[kWN][kWM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kWN; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < kWM; ++j) acc[i][j] = f32x16{};
 
     // fragment read offsets: row R (tile row), chunk c -> R * 128 + 16 * (c ^ ((R / 2) % 8))
     // rows used by this lane: 128 w* + 32 b + l32, so (R / 2) % 8 == (l32 / 2) % 8
     const int rsw = (l32 >> 1) & 7;
-    const int wrow0 = (128 * wn + l32) * 128;
+    const int wrow0 = (64 * wn + l32) * 128;
     const int arow0 = (128 * wm + l32) * 128;
 
     const int64_t ksteps = K / kBK;
@@ -164,55 +172,53 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             const int off = 16 * ((2 * ks + g) ^ rsw);
-            bf16x8 wf[4], af[4];
+            bf16x8 wf[kWN], af[kWM];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                wf[b] = *reinterpret_cast<const bf16x8*>(wt + wrow0 + b * 32 * 128 + off);
-                af[b] = *reinterpret_cast<const bf16x8*>(at + arow0 + b * 32 * 128 + off);
-            }
+            for (int b = 0; b < kWN; ++b) wf[b] = *reinterpret_cast<const bf16x8*>(wt + wrow0 + b * 32 * 128 + off);
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi)
+            for (int b = 0; b < kWM; ++b) af[b] = *reinterpret_cast<const bf16x8*>(at + arow0 + b * 32 * 128 + off);
 #pragma unroll
-                for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mfma32x32x16(wf[bi], af[bj], acc[bi][bj]);
+            for (int bi = 0; bi < kWN; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < kWM; ++bj) acc[bi][bj] = mfma32x32x16(wf[bi], af[bj], acc[bi][bj]);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
     // ---- epilogue: acc[bi][bj] register 4 q + e holds output row
-    // m = m0 + 128 wm + 32 bj + l32, W-tile row 128 wn + 32 bi + 8 q + 4 g + e ----
+    // m = m0 + 128 wm + 32 bj + l32, W-tile row 64 wn + 32 bi + 8 q + 4 g + e ----
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
+    for (int bj = 0; bj < kWM; ++bj) {
         const int64_t m = m0 + 128 * wm + 32 * bj + l32;
         if (m >= M) continue;
         int seg = 0;
         if (EPI == kEpiGatedResidual && num_seqs > 1) seg = find_segment(cu, num_seqs, m);
         if (EPI == kEpiSwiGLU) {
+            // bi = 0 is the gate block, bi = 1 the up block of output columns
+            // n0 + 32 wn + [0, 32)
 #pragma unroll
-            for (int pb = 0; pb < 2; ++pb) {           // (gate, up) block pairs
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + 32 * wn + 8 * q + 4 * g;
+                if (n >= N) continue;                // N % 4 == 0: groups are all in or out
+                float o[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t n = n0 + 64 * wn + 32 * pb + 8 * q + 4 * g;
-                    if (n >= N) continue;                // N % 4 == 0: groups are all in or out
-                    float o[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float gv = acc[2 * pb][bj][4 * q + e];
-                        const float uv = acc[2 * pb + 1][bj][4 * q + e];
-                        o[e] = gv / (1.0f + __expf(-gv)) * uv;
-                    }
-                    u32x2 w;
-                    w.x = pack_bf16x2(o[0], o[1]);
-                    w.y = pack_bf16x2(o[2], o[3]);
-                    *reinterpret_cast<u32x2*>(Y + m * N + n) = w;
+                for (int e = 0; e < 4; ++e) {
+                    const float gv = acc[0][bj][4 * q + e];
+                    const float uv = acc[1][bj][4 * q + e];
+                    o[e] = gv / (1.0f + __expf(-gv)) * uv;
                 }
+                u32x2 w;
+                w.x = pack_bf16x2(o[0], o[1]);
+                w.y = pack_bf16x2(o[2], o[3]);
+                *reinterpret_cast<u32x2*>(Y + m * N + n) = w;
             }
         } else {
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi) {
+            for (int bi = 0; bi < kWN; ++bi) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int64_t n = n0 + 128 * wn + 32 * bi + 8 * q + 4 * g;
+                    const int64_t n = n0 + 64 * wn + 32 * bi + 8 * q + 4 * g;
                     if (n >= N) continue;
                     float o[4];
                     if (EPI == kEpiStore) {
