@@ -3,8 +3,9 @@
 // operators bullet: modulation and normalization fused).
 //
 //  * modulation GEMV: mod[b, :] = cond[b, :] . W_mod^T in fp32; HBM-bound on
-//    the 6C x C weight, one wave per weight row, every segment's cond is
-//    applied to the row while it is in registers;
+//    the 6C x C weight, one wave per weight row (streamed once), every
+//    segment's cond (staged in LDS per workgroup) applied to the row while
+//    it is in registers;
 //  * RMSNorm + modulate: h[t] = RMSNorm(x[t]) * (1 + scale[seg(t)]) +
 //    shift[seg(t)]; one thread per 16-byte chunk of a row, a few rows per
 //    workgroup, the rows' sums of squares reduced through one LDS exchange,
@@ -17,34 +18,51 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Segments of cond staged in LDS per pass of the modulation kernel.
+constexpr int kCondChunk = 4;
+
 template <int NCH>
 __global__ __launch_bounds__(kThreads) void modulation_kernel(
     const uint16_t* __restrict__ cond, const uint16_t* __restrict__ w, float* __restrict__ mod,
     int num_seqs, int hidden, int rows) {
+    // cond rows are shared by the workgroup's four waves: staged once in LDS
+    // (kCondChunk segments per pass) instead of re-read from L2 per wave
+    __shared__ __attribute__((aligned(16))) uint16_t cs[kCondChunk * NCH * 512];
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    const bool active = row < rows;                 // every wave stays for the barriers
     float wr[NCH * 8];
-    const uint16_t* wp = w + static_cast<int64_t>(row) * hidden;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        Chunk16 c;
-        c.u = *reinterpret_cast<const uint4*>(wp + (i * 64 + lane) * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) wr[i * 8 + e] = bf2f(c.h[e]);
-    }
-    for (int b = 0; b < num_seqs; ++b) {
-        const uint16_t* cp = cond + static_cast<int64_t>(b) * hidden;
-        float acc = 0.f;
+    if (active) {
+        const uint16_t* wp = w + static_cast<int64_t>(row) * hidden;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             Chunk16 c;
-            c.u = *reinterpret_cast<const uint4*>(cp + (i * 64 + lane) * 8);
+            c.u = load_stream16(wp + (i * 64 + lane) * 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf(bf2f(c.h[e]), wr[i * 8 + e], acc);
+            for (int e = 0; e < 8; ++e) wr[i * 8 + e] = bf2f(c.h[e]);
         }
-        acc = wave_sum(acc);
-        if (lane == 0) mod[static_cast<int64_t>(b) * rows + row] = acc;
+    }
+    for (int b0 = 0; b0 < num_seqs; b0 += kCondChunk) {
+        const int nb = min(kCondChunk, num_seqs - b0);
+        __syncthreads();
+        for (int c = threadIdx.x; c < nb * hidden / 8; c += kThreads)
+            reinterpret_cast<uint4*>(cs)[c] =
+                *reinterpret_cast<const uint4*>(cond + static_cast<int64_t>(b0) * hidden + 8 * c);
+        __syncthreads();
+        if (!active) continue;
+        for (int b = 0; b < nb; ++b) {
+            const uint16_t* cp = cs + b * hidden;
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                Chunk16 c;
+                c.u = *reinterpret_cast<const uint4*>(cp + (i * 64 + lane) * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf(bf2f(c.h[e]), wr[i * 8 + e], acc);
+            }
+            acc = wave_sum(acc);
+            if (lane == 0) mod[static_cast<int64_t>(b0 + b) * rows + row] = acc;
+        }
     }
 }
 

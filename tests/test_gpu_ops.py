@@ -65,9 +65,11 @@ def test_qk_norm_rope_in_place_on_packed_qkv(dev, ops):
     assert torch.equal(t[:, 2 * c:], before_v)
 
 
-def test_modulation(dev, ops):
-    announce("modulation GEMV B=3 C=3072")
-    b, c = 3, 3072
+@pytest.mark.parametrize("b", [1, 3, 6])
+def test_modulation(dev, ops, b):
+    """B = 6 spans two passes of the kernel's staged segment chunk."""
+    announce(f"modulation GEMV B={b} C=3072")
+    c = 3072
     cond = _bf((b, c), 30)
     w = _bf((6 * c, c), 31, 0.02)
     mod = ops.modulation(to_dev_bf16(cond, dev), to_dev_bf16(w, dev))
