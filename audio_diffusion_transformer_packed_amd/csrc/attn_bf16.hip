@@ -8,32 +8,38 @@
 //
 // Design (CDNA4, 64-lane waves):
 //  * one workgroup per work item (head, segment, 256-row query tile), eight
-//    waves of 32 query rows each, one workgroup per CU (two waves per SIMD);
-//    the 256 rows share every K / V tile brought into LDS, which halves the
-//    global -> LDS traffic of a 128-row tile; the work list comes from the
-//    bookkeeping kernel, so no padded token is ever loaded or computed;
+//    waves of 32 query rows, one workgroup per CU (two waves per SIMD); the
+//    work list comes from the bookkeeping kernel, so no padded token is ever
+//    loaded or computed;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane owns one query row (lane % 32) and
 //    16 of every 32 keys, so row statistics are lane-local plus one exchange
-//    with the lane 32 away;
-//  * O^T = V^T P^T: P stays in registers, converted to bf16 directly in the
-//    MFMA operand layout; V^T fragments come from row-major V in LDS through
-//    ds_read_b64_tr_b16 (transposing 16-lane read);
+//    with the lane 32 away; O^T = V^T P^T with P converted to bf16 in
+//    registers directly in the MFMA operand layout and V^T fragments read
+//    from row-major V through ds_read_b64_tr_b16;
+//  * ping-pong: per 64-key tile a wave runs an MFMA block (P V of the
+//    previous tile, then S^T of this tile) and a softmax block (exp2, row
+//    sums, bf16 P). The two waves of a SIMD run these half a tile apart, one
+//    in its MFMA block while the other is in its softmax, with a workgroup
+//    barrier at every half tile; both groups run the same instruction
+//    stream, the second group shifted by one barrier, which keeps register
+//    allocation to a single path (a barrier counts arrivals, not program
+//    locations). The softmax VALU work of one wave then hides under the
+//    other's MFMAs instead of the two phases alternating on the whole SIMD;
 //  * K and V tiles of 64 keys move global -> LDS with buffer_load_dwordx4
-//    ... lds (no staging registers; the tile base lives in scalar registers,
-//    so the DMA costs no vector address arithmetic), double buffered, with
-//    XOR-swizzled 16-byte chunks so both fragment reads are free of bank
-//    conflicts;
-//  * each key tile: S^T MFMAs, softmax, P V MFMAs, while the next tile's K
-//    and V stream into the other LDS stage; the two waves of a SIMD overlap
-//    one wave's softmax with the other's MFMAs;
+//    ... lds from scalar buffer descriptors (rows past the segment end read
+//    as zeros, their scores are masked), double buffered, issued by the
+//    second group in its softmax half; XOR-swizzled 16-byte chunks keep both
+//    fragment reads free of bank conflicts. Fragment reads run a few MFMAs
+//    ahead of the MFMA stream;
 //  * softmax in the exp2 domain with a reference max that only moves when a
-//    lane's partial sum of exp2 values exceeds 2^16 (or is infinite):
-//    then the tile's true max is taken, O and l are rescaled and the tile's
-//    p recomputed. Between such events p <= 2^16 and O is never touched; the
-//    final O / l is the same softmax. Row sums use fp32 adds, not v_dot2,
-//    which would occupy the matrix pipe.
+//    lane's partial sum of exp2 values exceeds 2^16 (or is infinite): then
+//    the tile's true max is taken, O and l are rescaled and the tile's p
+//    recomputed. Between such events p <= 2^16 and O is never touched; the
+//    final O / l is the same softmax. Row sums use fp32 adds of the
+//    unrounded p.
 #include <type_traits>
+#include <utility>
 
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
@@ -42,35 +48,39 @@ namespace h3 {
 namespace {
 
 constexpr int kBN = 64;        // keys per tile
-constexpr int kWaves = 8;      // 32 query rows each
+constexpr int kWaves = 8;      // 32 query rows each; waves w and w + 4 share a SIMD
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 4;       // fragment reads in flight ahead of the MFMA stream
 
 template <int D>
 struct Cfg {
-    static constexpr int RB = D * 2;               // bytes per K / V row in LDS
-    static constexpr int CPR = D / 8;              // 16-byte chunks per row
-    static constexpr int RPI = 1024 / RB;          // rows per 1 KB DMA instruction
-    static constexpr int NI = kBN / RPI / kWaves;       // DMA instructions per wave per operand
-    static constexpr int TILE = kBN * RB;          // bytes per K or V tile
-    static constexpr int KC = D / 16;              // MFMA k-steps over the head dim
-    static constexpr int DB = D / 32;              // 32-wide output blocks
+    static constexpr int RB = D * 2;
+    static constexpr int CPR = D / 8;
+    static constexpr int RPI = 1024 / RB;
+    static constexpr int NI = kBN / RPI / (kWaves / 2);   // DMA instructions per DMA wave per operand
+    static constexpr int TILE = kBN * RB;
+    static constexpr int KC = D / 16;
+    static constexpr int DB = D / 32;
+    static constexpr int NQ = 2 * KC;   // S^T MFMAs per tile
+    static constexpr int NP = 4 * DB;   // P V MFMAs per tile
 };
 
-// Chunk swizzles (physical chunk = logical chunk ^ swizzle(row)).
-// K: fragment reads take one chunk of 32 consecutive rows; row % CPR spreads them.
-// V: a transposing read takes 4 chunks (64 B) of 8 consecutive rows; the
-// swizzle moves neighbouring rows to different 64-byte quarters.
 template <int D> __device__ __forceinline__ int kswz(int r) { return r % (D / 8); }
 template <int D> __device__ __forceinline__ int vswz(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-// Buffer resource word 3 for raw (untyped, stride 0) access on gfx9-family
-// parts: 32-bit data format; out-of-range loads return zero.
 constexpr int kBufferWord3 = 0x00020000;
 
-// 16 bytes per lane from buffer offset `voff` straight into LDS at lds_dst
-// (lane i writes lds_dst + 16 i), no staging registers.
+template <class F, int... J>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+    (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds_dst) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_dst)),
@@ -91,13 +101,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     int64_t vs, int64_t os, const int32_t* __restrict__ cu, const int4* __restrict__ items,
     int num_seqs, int total_tokens, int num_heads, float scale_log2) {
     using C = Cfg<D>;
-    constexpr int KC = C::KC, DB = C::DB, RB = C::RB, CPR = C::CPR;
+    constexpr int KC = C::KC, DB = C::DB, RB = C::RB, CPR = C::CPR, NQ = C::NQ, NP = C::NP;
+    constexpr int NM = NQ + NP;
 
     // K stage 0, K stage 1, V stage 0, V stage 1
     __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
 
-    // work-item fields and segment bounds are workgroup-uniform: keep them in
-    // scalar registers (so the K / V buffer descriptors are scalar too)
     const int4 it = items[blockIdx.x];
     const int head = __builtin_amdgcn_readfirstlane(it.x);
     const int seg = __builtin_amdgcn_readfirstlane(it.y);
@@ -111,12 +120,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     const int ntiles = (len + kBN - 1) / kBN;
 
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;          // 0: MFMA block on even half-tiles, 1: on odd
+    const int wg = wave & 3;            // index within the group
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
-    // ---- Q fragment in registers (B operand of S^T = K Q^T) ----
     const int qrow_local = wave * 32 + l32;
     const bool qvalid = qrow_local < qlen;
     bf16x8 qf[KC];
@@ -130,19 +140,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
         }
     }
 
-    // ---- DMA: instruction i of a tile fills rows RPI*i .. RPI*i+RPI-1;
-    // this wave issues i = NI*wave + j; lane -> row RPI*i + lane/CPR, physical
-    // chunk lane % CPR, which holds logical chunk (lane % CPR) ^ swizzle(row).
-    // A buffer resource based at the tile's first row (scalar registers) and
-    // sized to the segment's remaining rows makes every tile one code path:
-    // rows past the segment end are out of range and load as zeros, and
-    // their scores are masked to -inf in the last tile.
+    // ---- DMA (issued by the group in its softmax half): wave wg of the
+    // group fills 1 KB blocks NI*wg .. NI*wg+NI-1 of a tile ----
     const uint16_t* kbase = k + static_cast<int64_t>(head) * D;
     const uint16_t* vbase = v + static_cast<int64_t>(head) * D;
-    uint32_t koffb[C::NI], voffb[C::NI];      // byte offsets from the tile's first row
+    uint32_t koffb[C::NI], voffb[C::NI];
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
-        const int drow = C::RPI * (C::NI * wave + j) + lane / CPR;
+        const int drow = C::RPI * (C::NI * wg + j) + lane / CPR;
         koffb[j] = static_cast<uint32_t>((drow * ks + 8 * ((lane % CPR) ^ kswz<D>(drow))) * 2);
         voffb[j] = static_cast<uint32_t>((drow * vs + 8 * ((lane % CPR) ^ vswz<D>(drow))) * 2);
     }
@@ -154,25 +159,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
             const_cast<uint16_t*>(base + static_cast<int64_t>(key0) * stride), 0,
             static_cast<int>(rows * stride * 2), kBufferWord3);
 #pragma unroll
-        for (int j = 0; j < C::NI; ++j) buf_dma16(rsrc, offb[j], dst + (C::NI * wave + j) * 1024);
+        for (int j = 0; j < C::NI; ++j) buf_dma16(rsrc, offb[j], dst + (C::NI * wg + j) * 1024);
     };
-    auto dma_k = [&](int tile, int stage) __attribute__((always_inline)) {
-        dma(kbase, ks, koffb, tile, smem + stage * C::TILE);
+    auto dma_k = [&](int tile) __attribute__((always_inline)) {
+        dma(kbase, ks, koffb, tile, smem + (tile & 1) * C::TILE);
     };
-    auto dma_v = [&](int tile, int stage) __attribute__((always_inline)) {
-        dma(vbase, vs, voffb, tile, smem + (2 + stage) * C::TILE);
+    auto dma_v = [&](int tile) __attribute__((always_inline)) {
+        dma(vbase, vs, voffb, tile, smem + (2 + (tile & 1)) * C::TILE);
     };
 
-    // ---- LDS read offsets ----
-    // K fragment (A operand of S^T): rows 32b + l32, logical chunk 2c + g.
+    // ---- LDS fragment offsets ----
     const int ksw = kswz<D>(l32);
     int koff[KC];
 #pragma unroll
     for (int c = 0; c < KC; ++c) koff[c] = l32 * RB + 16 * ((2 * c + g) ^ ksw);
-    // V^T fragment by transposing read: in each 16-lane group, lane 4e + qq
-    // addresses V[row0 + e][dbase + 4 qq] with row0 = 32b + 16t + 8 half + 4g
-    // and dbase = 32 db + 16 h16; lane j of the group then receives
-    // V[row0 + e][dbase + j] for e = 0..3.
     const int e4 = (lane & 15) >> 2;
     const int qq = lane & 3;
     const int h16 = (lane >> 4) & 1;
@@ -181,73 +181,110 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db)
         voff[db] = (4 * g + e4) * RB + 16 * ((4 * db + 2 * h16 + (qq >> 1)) ^ vsw) + 8 * (qq & 1);
+    auto kfrag = [&](const char* kl, int i) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(kl + 32 * (i & 1) * RB + koff[i >> 1]);
+    };
+    // P V MFMA i: db = i % DB (consecutive MFMAs on different accumulators),
+    // key step (b, t) = ((i / DB) >> 1, (i / DB) & 1)
+    auto vfrag = [&](const char* vl, int i) __attribute__((always_inline)) {
+        const int db = i % DB, b = (i / DB) >> 1, t = (i / DB) & 1;
+        const char* base = vl + (32 * b + 16 * t) * RB + voff[db];
+        const u32x2 lo = lds_read_tr16(base);
+        const u32x2 hi = lds_read_tr16(base + 8 * RB);
+        const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
+        return __builtin_bit_cast(bf16x8, vf);
+    };
 
     f32x16 oacc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
-    // reference max (raw score units) of this lane's row; a large finite start
-    // value makes the first tile trigger through an infinite sum, never NaN
     float m_run = -1e30f;
-    float l_run = 0.f;         // partial row sum over this lane's keys
+    float l_run = 0.f;
     constexpr float kTrig = 65536.0f;
+    f32x16 sc[2];
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) pf[b][t] = bf16x8{};
 
-    // S^T(tile) from K stage `stage`; K fragments are read PK MFMAs ahead
-    auto qk = [&](int stage, f32x16 (&sc)[2]) __attribute__((always_inline)) {
-        const char* kl = smem + stage * C::TILE;
-        constexpr int NM = 2 * KC, PK = 3;
-        auto kfrag = [&](int i) __attribute__((always_inline)) {
-            return *reinterpret_cast<const bf16x8*>(kl + 32 * (i & 1) * RB + koff[i >> 1]);
+    // MFMA blocks. Both: O += P(u-1) V(u-1) then S^T = K(u) Q^T, the
+    // fragment reads kRing MFMAs ahead across the two; stages are
+    // compile-time so LDS offsets are immediates.
+    auto qk_pv = [&](auto kst_c) __attribute__((always_inline)) {
+        constexpr int kst = decltype(kst_c)::value;       // K(u) stage = u & 1
+        const char* kl = smem + kst * C::TILE;
+        const char* vl = smem + (2 + (kst ^ 1)) * C::TILE;   // V(u-1)
+        auto frag = [&](int j) __attribute__((always_inline)) {
+            return j < NQ ? kfrag(kl, j) : vfrag(vl, j - NQ);
         };
-        sc[0] = f32x16{};
-        sc[1] = f32x16{};
-        bf16x8 kq[PK];
-#pragma unroll
-        for (int i = 0; i < PK; ++i) kq[i] = kfrag(i);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            bf16x8 kn;
-            if (i + PK < NM) kn = kfrag(i + PK);
-            sc[i & 1] = mfma32x32x16(kq[i % PK], qf[i >> 1], sc[i & 1]);
+        bf16x8 ring[kRing];
+        static_for<kRing>([&](auto jc) { ring[decltype(jc)::value] = frag(decltype(jc)::value); });
+        static_for<NM>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            const bf16x8 a = ring[j % kRing];
+            if constexpr (j + kRing < NM) ring[j % kRing] = frag(j + kRing);
+            if constexpr (j < NQ) {
+                sc[j & 1] = mfma32x32x16(a, qf[j >> 1], j < 2 ? f32x16{} : sc[j & 1]);
+            } else {
+                constexpr int i = j - NQ;
+                oacc[i % DB] = mfma32x32x16(a, pf[(i / DB) >> 1][(i / DB) & 1], oacc[i % DB]);
+            }
             __builtin_amdgcn_sched_barrier(0);
-            if (i + PK < NM) kq[i % PK] = kn;
-        }
+        });
     };
-
-    // exp2 of score r of a tile against the current reference max
-    auto pexp = [&](const f32x16 (&s)[2], int r, float mb) __attribute__((always_inline)) {
-        return __builtin_amdgcn_exp2f(fmaf(s[r >> 4][r & 15], scale_log2, -mb));
+    auto qk_only = [&]() __attribute__((always_inline)) {      // tile 0, stage 0
+        const char* kl = smem;
+        bf16x8 ring[kRing];
+        static_for<kRing>([&](auto jc) { ring[decltype(jc)::value] = kfrag(kl, decltype(jc)::value); });
+        static_for<NQ>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int i = decltype(jc)::value;
+            const bf16x8 a = ring[i % kRing];
+            if constexpr (i + kRing < NQ) ring[i % kRing] = kfrag(kl, i + kRing);
+            sc[i & 1] = mfma32x32x16(a, qf[i >> 1], i < 2 ? f32x16{} : sc[i & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
-    // bf16 P in the B-operand layout: pf[b][t][e] = p of score 16 b + 8 t + e.
-    // The row sum adds the fp32 p with plain adds: v_dot2 (a dot on the
-    // rounded pair) would share the matrix pipe and stall the other wave's
-    // MFMAs, and the bf16 rounding of P is unbiased, so l of the unrounded p
-    // normalises the same softmax to well inside the bf16 error.
-    auto put = [&](bf16x8 (&pf)[2][2], int r, float v0, float v1, float& sum) __attribute__((always_inline)) {
-        const bf16x2 pr = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
-        pf[r >> 4][(r >> 3) & 1][r & 7] = pr[0];
-        pf[r >> 4][(r >> 3) & 1][(r & 7) + 1] = pr[1];
-        sum += v0 + v1;
-    };
-
-    // plain exp / sum / bf16 of one tile's scores
-    auto softmax_exp = [&](const f32x16 (&s)[2], bf16x8 (&pf)[2][2], float& psum) __attribute__((always_inline)) {
-        const float mb = m_run * scale_log2;
-        psum = 0.f;
+    auto pv_only = [&](int vst) __attribute__((always_inline)) {   // last tile
+        const char* vl = smem + (2 + vst) * C::TILE;
 #pragma unroll
-        for (int r = 0; r < 32; r += 2) {
-            put(pf, r, pexp(s, r, mb), pexp(s, r + 1, mb), psum);
-        }
+        for (int i = 0; i < NP; ++i)
+            oacc[i % DB] = mfma32x32x16(vfrag(vl, i), pf[(i / DB) >> 1][(i / DB) & 1], oacc[i % DB]);
     };
 
-    // If any lane's sum exceeded 2^16 (a new max far above the reference, or
-    // the first tile), move the reference to the true max, rescale O and l,
-    // and redo the tile's p. Then accumulate l.
-    auto softmax_fix = [&](const f32x16 (&s)[2], bf16x8 (&pf)[2][2], float psum) __attribute__((always_inline)) {
-        if (__any(!(psum <= kTrig))) {            // wave-uniform
+    // softmax of tile u's scores into P(u): exp2 against the reference max;
+    // if a lane's partial sum passes 2^16 (or the first tile), move the
+    // reference to the true max, rescale O and l, and redo p
+    const int keys_left = len - (ntiles - 1) * kBN;
+    auto softmax = [&](int u) __attribute__((always_inline)) {
+        if (u + 1 == ntiles && keys_left < kBN) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (key >= keys_left) sc[b][r] = -INFINITY;
+                }
+        }
+        auto pass = [&](float mb) __attribute__((always_inline)) {
+            float ps = 0.f;
+#pragma unroll
+            for (int r = 0; r < 32; r += 2) {
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[r >> 4][r & 15], scale_log2, -mb));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[r >> 4][(r & 15) + 1], scale_log2, -mb));
+                ps += e0 + e1;
+                const bf16x2 pr = {static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
+                pf[r >> 4][(r >> 3) & 1][r & 7] = pr[0];
+                pf[r >> 4][(r >> 3) & 1][(r & 7) + 1] = pr[1];
+            }
+            return ps;
+        };
+        float psum = pass(m_run * scale_log2);
+        if (__any(!(psum <= kTrig))) {
             asm volatile("" ::: "memory");
-            float mt = s[0][0];
+            float mt = sc[0][0];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(s[0][r], s[1][r]));
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(sc[0][r], sc[1][r]));
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
             const float m_new = fmaxf(m_run, mt);
             const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
@@ -255,86 +292,86 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-            softmax_exp(s, pf, psum);
+            psum = pass(m_new * scale_log2);
         }
         l_run += psum;
     };
 
-    // O^T += V^T P^T from V stage `stage`; k-step (b, t) covers keys
-    // 32b + 16t + [0, 16): lane half g holds keys 4g + [0,4) and 8 + 4g + [0,4)
-    // of it (the S^T accumulator rows), the transposing reads fetch the same.
-    auto pv = [&](int stage, const bf16x8 (&pf)[2][2]) __attribute__((always_inline)) {
-        const char* vl = smem + (2 + stage) * C::TILE;
-        // MFMA i: db = i / 4, (b, t) = (i / 2 % 2, i % 2); fragments read ahead
-        auto frag = [&](int i) __attribute__((always_inline)) {
-            const int db = i >> 2, b = (i >> 1) & 1, t = i & 1;
-            const char* base = vl + (32 * b + 16 * t) * RB + voff[db];
-            const u32x2 lo = lds_read_tr16(base);
-            const u32x2 hi = lds_read_tr16(base + 8 * RB);
-            const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
-            return __builtin_bit_cast(bf16x8, vf);
-        };
-        constexpr int NM = 4 * DB, PV_AHEAD = 2;
-        bf16x8 vq[PV_AHEAD];
+    // ---- prologue: K(0) in LDS (every wave a share) ----
+    {
+        const int key0 = kv0;
+        const int rows = min(kBN, kv1 - key0);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(kbase + static_cast<int64_t>(key0) * ks), 0,
+            static_cast<int>(rows * ks * 2), kBufferWord3);
+        constexpr int NI8 = kBN / C::RPI / kWaves;
 #pragma unroll
-        for (int i = 0; i < PV_AHEAD; ++i) vq[i] = frag(i);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            bf16x8 vn;
-            if (i + PV_AHEAD < NM) vn = frag(i + PV_AHEAD);
-            oacc[i >> 2] = mfma32x32x16(vq[i % PV_AHEAD], pf[(i >> 1) & 1][i & 1], oacc[i >> 2]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (i + PV_AHEAD < NM) vq[i % PV_AHEAD] = vn;
+        for (int j = 0; j < NI8; ++j) {
+            const int drow = C::RPI * (NI8 * wave + j) + lane / CPR;
+            const uint32_t off = static_cast<uint32_t>((drow * ks + 8 * ((lane % CPR) ^ kswz<D>(drow))) * 2);
+            buf_dma16(rsrc, off, smem + (NI8 * wave + j) * 1024);
         }
-    };
-
-    auto mask_tail = [&](f32x16 (&s)[2], int keys_left) __attribute__((always_inline)) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (key >= keys_left) s[b][r] = -INFINITY;
-            }
-    };
-
-    f32x16 sc[2];
-    bf16x8 pf[2][2];
-    float psum;
-
-    // Tile t sits in K / V stage t % 2. Iteration t: DMA tile t+1 into the
-    // other stage, then S^T(t), softmax(t), P V(t) from this stage, then wait
-    // for the DMA and a barrier (one per tile). The loop runs two tiles per
-    // trip so each stage is a compile-time constant and the LDS stage offsets
-    // fold into the fragment reads' immediate offsets.
-    dma_k(0, 0);
-    dma_v(0, 0);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int keys_left = len - (ntiles - 1) * kBN;
-    auto tile = [&](int t, auto stage_c) __attribute__((always_inline)) {
-        constexpr int stage = decltype(stage_c)::value;
-        const bool last = t + 1 == ntiles;
-        if (!last) {
-            dma_k(t + 1, stage ^ 1);
-            dma_v(t + 1, stage ^ 1);
-        }
-        qk(stage, sc);
-        if (last && keys_left < kBN) mask_tail(sc, keys_left);
-        softmax_exp(sc, pf, psum);
-        softmax_fix(sc, pf, psum);
-        pv(stage, pf);
-        if (!last) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+
+    // Every wave runs the same sequence, MFMA block M(u) (P V(u-1), S^T(u))
+    // then softmax S(u), with a barrier after each; group 1 runs one
+    // half-tile behind group 0 (an extra barrier before its first block, and
+    // group 0 an extra one after its last), so in every half-tile one wave of
+    // each SIMD issues MFMAs while the other runs its softmax.
+    // Group 1 issues the DMA of K(u+2) and V(u+1) at the start of its S(u),
+    // i.e. after barrier 2u+2: their stages held K(u) and V(u-1), which M(u)
+    // of both groups has read by then. They are next read in M(u+2), from
+    // half-tile 2u+4 on; group 1 waits for its DMA at the end of its M(u+1),
+    // before barrier 2u+4. (Its V reads in M(u+1) already wait for it: the
+    // compiler cannot tell the DMA's LDS stage from the one being read.)
+    const bool g0 = grp == 0;
+    // LDS writes done and a workgroup barrier; outstanding DMA is waited for
+    // only where its data is needed (the memory clobber keeps the compiler
+    // from moving LDS accesses across)
+    auto bar = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    auto dma_wait = [&]() __attribute__((always_inline)) {
+        if (!g0) __builtin_amdgcn_s_waitcnt(0);
+    };
+    auto issue_dma = [&](int u) __attribute__((always_inline)) {
+        if (!g0) {
+            if (u + 2 < ntiles) dma_k(u + 2);
+            if (u + 1 < ntiles) dma_v(u + 1);
         }
     };
-    for (int t = 0; t < ntiles; t += 2) {
-        tile(t, std::integral_constant<int, 0>{});
-        if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
+    if (!g0) {
+        // K(1), V(0) for M(1)
+        if (1 < ntiles) dma_k(1);
+        dma_v(0);
+        bar();
     }
+    qk_only();
+    dma_wait();
+    bar();
+    issue_dma(0);
+    softmax(0);
+    bar();
+    auto tile = [&](int u, auto kst_c) __attribute__((always_inline)) {
+        qk_pv(kst_c);
+        dma_wait();
+        bar();
+        issue_dma(u);
+        softmax(u);
+        bar();
+    };
+    int u = 1;
+    for (; u + 2 <= ntiles; u += 2) {
+        tile(u, std::integral_constant<int, 1>{});
+        tile(u + 1, std::integral_constant<int, 0>{});
+    }
+    if (u < ntiles) tile(u, std::integral_constant<int, 1>{});
+    pv_only((ntiles - 1) & 1);
+    if (g0) bar();
 
-    // ---- normalise and store: lane holds dims 32 db + 8 r4 + 4 g + [0, 4) ----
+    // ---- normalise and store ----
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = 1.f / l_tot;
     if (qvalid) {
