@@ -22,12 +22,14 @@
 //    wave, each lane owning one query row of S^T = K Q^T (lane % 32);
 //  * K tiles (64 keys x 128 B) and V^T tiles (128 channels x 64 B, keys
 //    already in the lanes' P order) are contiguous 8 KB blocks in HBM, moved
-//    to LDS with buffer_load_dwordx4 ... lds through scalar descriptors (one
-//    instruction per wave and operand, no vector address arithmetic), double
-//    buffered, XOR-swizzled for conflict-free 16-byte fragment reads; no
-//    transposing reads are needed;
+//    to LDS with buffer_load_dwordx4 ... lds through scalar descriptors (no
+//    vector address arithmetic), double buffered, XOR-swizzled for
+//    conflict-free 16-byte fragment reads; no transposing reads are needed;
 //  * P is converted to e4m3 in registers, already in the B-operand byte
-//    order of the P V MFMA; per tile a wave issues 4 + 4 fp8 MFMAs.
+//    order of the P V MFMA; per tile a wave issues 4 + 4 fp8 MFMAs;
+//  * ping-pong: the two waves of a SIMD run their MFMA and softmax blocks
+//    half a tile apart (see the bf16 kernel), so one wave's softmax VALU
+//    work overlaps the other's MFMAs.
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -132,12 +134,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const int qblk = tbs + (q0 - kv0 + min(qrow_local, qlen - 1)) / kBN;
     const float sq = qsc[static_cast<int64_t>(qblk) * num_heads + head] * scale_log2;
 
-    // DMA: instruction `wave` of a tile fills LDS bytes [1024 wave, +1024):
-    // K rows 8 wave + lane / 8 (chunk lane % 8), V^T rows 16 wave + lane / 4
-    // (chunk lane % 4), each loading the logical chunk that the swizzle puts there.
-    const int krow = 8 * wave + (lane >> 3), vrow = 16 * wave + (lane >> 2);
-    const uint32_t ksrc = krow * kD + 16 * ((lane & 7) ^ kswz(krow));
-    const uint32_t vsrc = vrow * kBN + 16 * ((lane & 3) ^ vswz(vrow));
+    // Ping-pong as in the bf16 kernel: waves 0-3 and 4-7 (the two waves of
+    // each SIMD) run the same sequence of MFMA blocks M(u) (S^T of tile u,
+    // P V of tile u-1) and softmax blocks S(u), half a tile apart, with a
+    // workgroup barrier between consecutive blocks; the second group issues
+    // the DMA at the start of its softmax block.
+    const int grp = wave >> 2;
+    const bool g0 = grp == 0;
+    const int wg = wave & 3;
+    // DMA: 1 KB block j of a tile: K rows 8 j + lane / 8 (chunk lane % 8),
+    // V^T rows 16 j + lane / 4 (chunk lane % 4), each loading the logical
+    // chunk that the swizzle puts there. The second group's wave wg fills
+    // blocks 2 wg and 2 wg + 1; in the prologue every wave fills K block `wave`.
+    auto ksrc_of = [&](int j) __attribute__((always_inline)) {
+        const int krow = 8 * j + (lane >> 3);
+        return static_cast<uint32_t>(krow * kD + 16 * ((lane & 7) ^ kswz(krow)));
+    };
+    auto vsrc_of = [&](int j) __attribute__((always_inline)) {
+        const int vrow = 16 * j + (lane >> 2);
+        return static_cast<uint32_t>(vrow * kBN + 16 * ((lane & 3) ^ vswz(vrow)));
+    };
+    const uint32_t ksrc0 = ksrc_of(2 * wg), ksrc1 = ksrc_of(2 * wg + 1);
+    const uint32_t vsrc0 = vsrc_of(2 * wg), vsrc1 = vsrc_of(2 * wg + 1);
     // one descriptor per operand covering this segment's tiles of this head;
     // the tile is the scalar offset of each load
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -146,9 +164,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(v8t + (static_cast<int64_t>(head) * num_tiles + tbs) * kVT), 0,
         ntiles * kVT, kBufferWord3);
-    auto dma = [&](int tile, int stage) __attribute__((always_inline)) {
-        buf_dma16(rk, ksrc, tile * kKT, smem + stage * kKT + 1024 * wave);
-        buf_dma16(rv, vsrc, tile * kVT, smem + 2 * kKT + stage * kVT + 1024 * wave);
+    auto dma_k = [&](int tile) __attribute__((always_inline)) {
+        char* dst = smem + (tile & 1) * kKT + 2048 * wg;
+        buf_dma16(rk, ksrc0, tile * kKT, dst);
+        buf_dma16(rk, ksrc1, tile * kKT, dst + 1024);
+    };
+    auto dma_v = [&](int tile) __attribute__((always_inline)) {
+        char* dst = smem + 2 * kKT + (tile & 1) * kVT + 2048 * wg;
+        buf_dma16(rv, vsrc0, tile * kVT, dst);
+        buf_dma16(rv, vsrc1, tile * kVT, dst + 1024);
     };
 
     // LDS fragment offsets. K block b, k-step c: row 32b + l32, logical
@@ -168,82 +192,130 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     float m_run = -1e30f;     // running row max, exp2 units (finite start: no inf - inf)
     float l_run = 0.f;        // partial sum of 448 p over this lane's keys
     int nskip = 0;
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    i32x8 pf = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    bool pv_pending = false;  // P of the previous tile waits for its P V (not skipped)
 
-    dma(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int stage = t & 1;
-        const bool last = t + 1 == ntiles;
-        if (!last) dma(t + 1, stage ^ 1);
-        const float sk = ksc[static_cast<int64_t>(tbs + t) * num_heads + head];
-        if (wave_active) {
-            const char* kl = smem + stage * kKT;
-            const char* vl = smem + 2 * kKT + stage * kVT;
-            f32x16 sc[2] = {f32x16{}, f32x16{}};
+    // MFMA block M(u): S^T(u) from K stage u & 1 (u < T), O += P(u-1) V(u-1)
+    // from V stage (u-1) & 1 (u >= 1, tile not skipped)
+    auto mfma_block = [&](int u) __attribute__((always_inline)) {
+        if (!wave_active) return;
+        if (u < ntiles) {
+            const char* kl = smem + (u & 1) * kKT;
+            sc[0] = f32x16{};
+            sc[1] = f32x16{};
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
                     sc[b] = mfma_fp8(read32(kl + 4096 * b + kro[c][0], kl + 4096 * b + kro[c][1]), qf[c], sc[b]);
-            if (last && keys_left < kBN) {
+        }
+        if (u >= 1 && pv_pending) {
+            const char* vl = smem + 2 * kKT + ((u - 1) & 1) * kVT;
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+            for (int db = 0; db < 4; ++db)
+                oacc[db] = mfma_fp8(read32(vl + 2048 * db + vro[0], vl + 2048 * db + vro[1]), pf, oacc[db]);
+        }
+    };
+    // softmax block S(u): tile max, skip rule, rescale, P of tile u
+    auto softmax_block = [&](int u) __attribute__((always_inline)) {
+        if (!wave_active) return;
+        const float sk = ksc[static_cast<int64_t>(tbs + u) * num_heads + head];
+        if (u + 1 == ntiles && keys_left < kBN) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * b + 8 * (r >> 2) + 4 * g + (r & 3) >= keys_left) sc[b][r] = -INFINITY;
-            }
-            float mx = sc[0][0];
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float ct = sq * sk;          // exp2 units per raw score
-            const float tmax = mx * ct;
-            bool run_tile = true;
-            if (skip && t > 0) {
-                const bool below = !qvalid || tmax < m_run - thr_log2;
-                if (__all(below)) {                       // wave-uniform
-                    run_tile = false;
-                    ++nskip;
-                }
-            }
-            if (run_tile) {
-                const float m_new = fmaxf(m_run, tmax);
-                if (__any(m_new > m_run)) {               // wave-uniform
-                    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                    l_run *= alpha;
+                for (int r = 0; r < 16; ++r)
+                    if (32 * b + 8 * (r >> 2) + 4 * g + (r & 3) >= keys_left) sc[b][r] = -INFINITY;
+        }
+        float mx = sc[0][0];
 #pragma unroll
-                    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-                }
-                m_run = m_new;
-                // 448 p = exp2(s ct - m + log2 448); bytes in B-operand order:
-                // byte 16 b + r of this lane holds score sc[b][r]
-                const float mb = m_new - kLog2_448;
-                i32x8 pf;
-                float ps = 0.f;
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    const int b = w >> 2, r = 4 * (w & 3);
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][r], ct, -mb));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 1], ct, -mb));
-                    const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 2], ct, -mb));
-                    const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 3], ct, -mb));
-                    ps += (p0 + p1) + (p2 + p3);
-                    int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                    word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-                    pf[w] = word;
-                }
-                l_run += ps;
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    oacc[db] = mfma_fp8(read32(vl + 2048 * db + vro[0], vl + 2048 * db + vro[1]), pf, oacc[db]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float ct = sq * sk;          // exp2 units per raw score
+        const float tmax = mx * ct;
+        bool run_tile = true;
+        if (skip && u > 0) {
+            const bool below = !qvalid || tmax < m_run - thr_log2;
+            if (__all(below)) {                       // wave-uniform
+                run_tile = false;
+                ++nskip;
             }
         }
-        if (!last) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+        pv_pending = run_tile;
+        if (run_tile) {
+            const float m_new = fmaxf(m_run, tmax);
+            if (__any(m_new > m_run)) {               // wave-uniform
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+            }
+            m_run = m_new;
+            // 448 p = exp2(s ct - m + log2 448); bytes in B-operand order:
+            // byte 16 b + r of this lane holds score sc[b][r]
+            const float mb = m_new - kLog2_448;
+            float ps = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const int b = w >> 2, r = 4 * (w & 3);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][r], ct, -mb));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 1], ct, -mb));
+                const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 2], ct, -mb));
+                const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 3], ct, -mb));
+                ps += (p0 + p1) + (p2 + p3);
+                int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+                pf[w] = word;
+            }
+            l_run += ps;
         }
+    };
+
+    // ---- prologue: K(0) in LDS, every wave one 1 KB block ----
+    buf_dma16(rk, ksrc_of(wave), 0, smem + 1024 * wave);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // LDS reads done (so the next DMA may overwrite), workgroup barrier; the
+    // memory clobber keeps the compiler from moving LDS accesses across
+    auto bar = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    auto dma_wait = [&]() __attribute__((always_inline)) {
+        if (!g0) __builtin_amdgcn_s_waitcnt(0);
+    };
+    // The second group issues K(u+2), V(u+1) at the start of its S(u), after
+    // barrier 2u+2: their stages held K(u), V(u-1), which M(u) of both
+    // groups has read. They are next read in M(u+2), from half-tile 2u+4 on;
+    // the group waits for its DMA at the end of its M(u+1), before barrier 2u+4.
+    auto issue_dma = [&](int u) __attribute__((always_inline)) {
+        if (!g0) {
+            if (u + 2 < ntiles) dma_k(u + 2);
+            if (u + 1 < ntiles) dma_v(u + 1);
+        }
+    };
+    if (!g0) {
+        if (1 < ntiles) dma_k(1);
+        dma_v(0);
+        bar();
     }
+    mfma_block(0);
+    dma_wait();
+    bar();
+    issue_dma(0);
+    softmax_block(0);
+    bar();
+    for (int u = 1; u < ntiles; ++u) {
+        mfma_block(u);
+        dma_wait();
+        bar();
+        issue_dma(u);
+        softmax_block(u);
+        bar();
+    }
+    mfma_block(ntiles);
+    if (g0) bar();
 
     // ---- O = acc s_v / l; lane holds channels 32 db + 8 r4 + 4 g + [0, 4) ----
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
