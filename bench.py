@@ -11,7 +11,9 @@ Prints ONE JSON line:
   roofline    the dominant kernel (varlen attention) against bf16 dense MFMA
               peak, its average launch duration timed with HIP events on the
               stream it runs on
-  stages      per-kernel timings (events) with TFLOP/s or GB/s
+  stages      per-kernel timings: median and p10/p90 of >= 20 launches, each
+              bracketed by HIP events; HBM-bound kernels run after a 512 MiB
+              scratch write so they do not read from the 256 MiB MALL
   cpu_baseline the float64 oracle on the host cores, on a bounded sample
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -86,6 +88,34 @@ class Timer:
         end.record()
         t.cuda.synchronize()
         return start.elapsed_time(end) / n
+
+
+class Sampler:
+    """Per-launch durations of a callable: a HIP event pair around each launch on
+    the current torch stream. With flush=True a 512 MiB scratch buffer is written
+    before every launch (outside the events), so an HBM-bound kernel reads its
+    inputs from HBM rather than from the 256 MiB Infinity Cache."""
+
+    def __init__(self, torch, flush_bytes=512 << 20):
+        self.torch = torch
+        self.scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+
+    def __call__(self, fn, n, flush):
+        t = self.torch
+        pairs = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True))
+                 for _ in range(n)]
+        fn()
+        t.cuda.synchronize()
+        for i, (start, end) in enumerate(pairs):
+            if flush:
+                self.scratch.fill_(i & 0xff)
+            start.record()
+            fn()
+            end.record()
+        t.cuda.synchronize()
+        ms = np.array([start.elapsed_time(end) for start, end in pairs])
+        return {"median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
+                "p90": float(np.percentile(ms, 90)), "n": n, "flush": flush}
 
 
 def cpu_baseline(inp, wl, rows_count=16):
@@ -201,49 +231,55 @@ def main():
     attn_tflops = f_attn / (ms_attn * 1e-3) / 1e12
 
     stages = {}
+    sampler = Sampler(torch)
+    stage_iters = max(20, args.steps)
+
+    def rec(name, t, flops=None, nbytes=None):
+        ms = t["median"]
+        e = {"ms": round(ms, 4), "p10_ms": round(t["p10"], 4), "p90_ms": round(t["p90"], 4),
+             "launches": t["n"], "mall_flushed": t["flush"]}
+        if flops is not None:
+            e["tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+            e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if nbytes is not None:
+            e["gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        stages[name] = e
+
     if not args.no_stages:
         log("timing stages")
         mod = taps["mod"]
-        it = max(3, args.steps)
+        it = stage_iters
         w = weights
+        hbm = lambda fn: sampler(fn, it, True)
+        mfma = lambda fn: sampler(fn, it, False)
 
-        def rec(name, ms, flops=None, nbytes=None):
-            e = {"ms": round(ms, 4)}
-            if flops is not None:
-                e["tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
-                e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
-            if nbytes is not None:
-                e["gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
-                e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
-            stages[name] = e
-
-        rec("modulation_gemv", timer(lambda: ops.modulation(cond, w["w_mod"]), it),
+        rec("modulation_gemv", hbm(lambda: ops.modulation(cond, w["w_mod"])),
             nbytes=6 * c * c * 2 + b * c * 2 + b * 6 * c * 4)
         rec("adaln_rmsnorm_modulate",
-            timer(lambda: ops.adaln_rmsnorm_modulate(x, mod[:, 0:c], mod[:, c:2 * c], cu_d, cu,
-                                                     out=taps["h"]), it),
+            hbm(lambda: ops.adaln_rmsnorm_modulate(x, mod[:, 0:c], mod[:, c:2 * c], cu_d, cu,
+                                                   out=taps["h"])),
             nbytes=2 * n * c * 2)
-        rec("qkv_gemm", timer(lambda: ops.linear(taps["h"], w["w_qkv"]), it),
+        rec("qkv_gemm", mfma(lambda: ops.linear(taps["h"], w["w_qkv"])),
             flops=2.0 * n * c * 3 * c)
         qkv2 = qkv.clone()
         q2 = qkv2[:, :hd].view(n, wl.heads, wl.head_dim)
         k2 = qkv2[:, hd:2 * hd].view(n, wl.heads, wl.head_dim)
         rec("qk_rmsnorm_rope",
-            timer(lambda: ops.qk_rmsnorm_rope(q2, k2, w["q_norm"], w["k_norm"], grid_d, split),
-                  it),
+            hbm(lambda: ops.qk_rmsnorm_rope(q2, k2, w["q_norm"], w["k_norm"], grid_d, split)),
             nbytes=4 * n * c * 2 + 12 * n)
         del qkv2
-        rec("attention_bf16", ms_attn, flops=f_attn)
+        rec("attention_bf16", mfma(attn), flops=f_attn)
         rec("out_proj_gated_residual",
-            timer(lambda: ops.linear_gated_residual(taps["o"], w["w_o"], x, mod[:, 2 * c:3 * c],
-                                                    cu_d, cu, out=taps["x1"]), it),
+            mfma(lambda: ops.linear_gated_residual(taps["o"], w["w_o"], x, mod[:, 2 * c:3 * c],
+                                                   cu_d, cu, out=taps["x1"])),
             flops=2.0 * n * c * c)
-        rec("swiglu_gemm", timer(lambda: ops.linear_swiglu(taps["h2"], w["w_gate"], w["w_up"]), it),
+        rec("swiglu_gemm", mfma(lambda: ops.linear_swiglu(taps["h2"], w["w_gate"], w["w_up"])),
             flops=2.0 * n * c * 2 * wl.ffn)
         rec("down_gated_residual",
-            timer(lambda: ops.linear_gated_residual(taps["a"], w["w_down"], taps["x1"],
-                                                    mod[:, 5 * c:6 * c], cu_d, cu,
-                                                    out=taps["h2"]), it),
+            mfma(lambda: ops.linear_gated_residual(taps["a"], w["w_down"], taps["x1"],
+                                                   mod[:, 5 * c:6 * c], cu_d, cu,
+                                                   out=taps["h2"])),
             flops=2.0 * n * wl.ffn * c)
 
     fp8 = None
@@ -268,7 +304,9 @@ def main():
         qbufs = ops.fp8_quantize(qv, kv, vv, cu_d, cu)
         qws = torch.empty(max(1 << 20, ops.lib().h3_fp8_quantize_workspace_size(b, n, wl.heads)),
                           dtype=torch.uint8, device=dev)
-        ms_q = timer(lambda: ops.fp8_quantize(qv, kv, vv, cu_d, cu, out=qbufs, workspace=qws), it)
+        tq = sampler(lambda: ops.fp8_quantize(qv, kv, vv, cu_d, cu, out=qbufs, workspace=qws),
+                     stage_iters, True)
+        ms_q = tq["median"]
         q_bytes = 3 * n * c * 2 + n * c * 2 + 3 * n * c
         ms_k = ms_fp8 - ms_q
         fp8 = {"workload": "attn_fp8_10s_58k shape on the block's q/k/v",
@@ -282,8 +320,7 @@ def main():
                "skip_attention_ms": round(ms_fp8_skip, 4),
                "skip_fraction": round(skipped / pairs, 5),
                "skip_threshold": 8.0}
-        stages["fp8_quantize"] = {"ms": round(ms_q, 4), "gbs": fp8["quantize_gbs"],
-                                  "frac_hbm_peak": fp8["quantize_frac_hbm_peak"]}
+        rec("fp8_quantize", tq, nbytes=q_bytes)
 
     traffic = load_traffic()
     result = {
