@@ -7,9 +7,9 @@
 //    segment's cond (staged in LDS per workgroup) applied to the row while
 //    it is in registers;
 //  * RMSNorm + modulate: h[t] = RMSNorm(x[t]) * (1 + scale[seg(t)]) +
-//    shift[seg(t)]; one thread per 16-byte chunk of a row, a few rows per
-//    workgroup, the rows' sums of squares reduced through one LDS exchange,
-//    one bf16 rounding.
+//    shift[seg(t)]; one wave per row (its sum of squares is a wave
+//    reduction, no workgroup barrier), two rows in flight per wave, one
+//    bf16 rounding.
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -66,79 +66,88 @@ __global__ __launch_bounds__(kThreads) void modulation_kernel(
     }
 }
 
-// RMSNorm + modulate over kRows consecutive tokens per workgroup: one thread
-// per 16-byte chunk (8 channels) of a row, hidden / 8 threads, each thread
-// loading one chunk of each of the kRows rows (all loads in flight at once)
-// and storing one chunk of each output row. The rows' sums of squares are
-// reduced across the wave and then, once for all kRows rows, across the
-// workgroup through LDS. The thread's 8 shift / scale values stay in
-// registers for all its rows (reloaded only where a row changes segment).
-// x and h are streamed with nontemporal loads / stores (each byte is touched
-// once): at 57,960 x 3072 this reaches ~0.93x of a plain device copy of the
-// same bytes, against ~0.8x with cached accesses.
-constexpr int kRows = 4;
+// RMSNorm + modulate, one wave per row: lane i owns 16-byte chunks i,
+// i + 64, ... (NCH = hidden / 512 of them) of the row, so the row's sum of
+// squares is a wave reduction and no workgroup barrier stands between a
+// wave's loads and its stores. Each wave takes kRowsPerWave consecutive rows
+// and issues all of their loads before the first reduction. The lane's
+// shift / scale values stay in registers across its rows (reloaded only
+// where a row changes segment) when they fit (NCH <= 8), otherwise they are
+// read per row from cache. x and h are streamed with nontemporal loads /
+// stores (each byte is touched once). At 57,960 x 3072 with the Infinity
+// Cache flushed this runs at ~0.9x of a plain device copy of the same bytes.
+constexpr int kRowsPerWave = 2;
+constexpr int kAdalnWaves = 4;
 
-__global__ __launch_bounds__(1024) void adaln_kernel(
+template <int NCH>
+__global__ __launch_bounds__(64 * kAdalnWaves) void adaln_kernel(
     const uint16_t* __restrict__ x, uint16_t* __restrict__ h, const float* __restrict__ shift,
     const float* __restrict__ scale, int64_t mod_stride, const int32_t* __restrict__ cu,
-    int num_seqs, int total_tokens, int hidden, float eps) {
-    __shared__ float red[kRows][16];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRows;
-    const int c0 = 8 * tid;
-    Chunk16 xc[kRows];
-    float ss[kRows];
+    int num_seqs, int total_tokens, float eps) {
+    constexpr int hidden = NCH * 512;
+    constexpr bool kCacheMod = NCH <= 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t t0 =
+        (static_cast<int64_t>(blockIdx.x) * kAdalnWaves + (threadIdx.x >> 6)) * kRowsPerWave;
+    Chunk16 xc[kRowsPerWave][NCH];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-        ss[r] = 0.f;
-        if (t0 + r < total_tokens) {
-            xc[r].u = load_stream16(x + (t0 + r) * hidden + c0);
+    for (int r = 0; r < kRowsPerWave; ++r)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float f = bf2f(xc[r].h[e]);
-                ss[r] = fmaf(f, f, ss[r]);
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-        ss[r] = wave_sum(ss[r]);
-        if (lane == 0) red[r][wave] = ss[r];
-    }
-    __syncthreads();
+        for (int i = 0; i < NCH; ++i)
+            if (t0 + r < total_tokens)
+                xc[r][i].u = load_stream16(x + (t0 + r) * hidden + (i * 64 + lane) * 8);
     int seg_loaded = -1;
-    float shv[8], scv[8];
+    float shv[kCacheMod ? NCH : 1][8], scv[kCacheMod ? NCH : 1][8];
+    auto load_mod = [&](int seg, int i, float (&sh)[8], float (&sc)[8]) __attribute__((always_inline)) {
+        const float* shp = shift + static_cast<int64_t>(seg) * mod_stride + (i * 64 + lane) * 8;
+        const float* scp = scale + static_cast<int64_t>(seg) * mod_stride + (i * 64 + lane) * 8;
+        const float4 sh0 = *reinterpret_cast<const float4*>(shp);
+        const float4 sh1 = *reinterpret_cast<const float4*>(shp + 4);
+        const float4 sc0 = *reinterpret_cast<const float4*>(scp);
+        const float4 sc1 = *reinterpret_cast<const float4*>(scp + 4);
+        sh[0] = sh0.x; sh[1] = sh0.y; sh[2] = sh0.z; sh[3] = sh0.w;
+        sh[4] = sh1.x; sh[5] = sh1.y; sh[6] = sh1.z; sh[7] = sh1.w;
+        sc[0] = 1.0f + sc0.x; sc[1] = 1.0f + sc0.y; sc[2] = 1.0f + sc0.z; sc[3] = 1.0f + sc0.w;
+        sc[4] = 1.0f + sc1.x; sc[5] = 1.0f + sc1.y; sc[6] = 1.0f + sc1.z; sc[7] = 1.0f + sc1.w;
+    };
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
+    for (int r = 0; r < kRowsPerWave; ++r) {
         const int64_t t = t0 + r;
         if (t >= total_tokens) break;
-        float tot = 0.f;
-        for (int w = 0; w < nwaves; ++w) tot += red[r][w];
-        const float rinv = 1.0f / sqrtf(fmaf(tot, 1.0f / hidden, eps));
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float f = bf2f(xc[r][i].h[e]);
+                ss = fmaf(f, f, ss);
+            }
+        ss = wave_sum(ss);
+        const float rinv = 1.0f / sqrtf(fmaf(ss, 1.0f / hidden, eps));
         const int seg = num_seqs == 1 ? 0 : find_segment(cu, num_seqs, t);
-        if (seg != seg_loaded) {
-            const float* shp = shift + static_cast<int64_t>(seg) * mod_stride + c0;
-            const float* scp = scale + static_cast<int64_t>(seg) * mod_stride + c0;
-            const float4 sh0 = *reinterpret_cast<const float4*>(shp);
-            const float4 sh1 = *reinterpret_cast<const float4*>(shp + 4);
-            const float4 sc0 = *reinterpret_cast<const float4*>(scp);
-            const float4 sc1 = *reinterpret_cast<const float4*>(scp + 4);
-            shv[0] = sh0.x; shv[1] = sh0.y; shv[2] = sh0.z; shv[3] = sh0.w;
-            shv[4] = sh1.x; shv[5] = sh1.y; shv[6] = sh1.z; shv[7] = sh1.w;
-            scv[0] = 1.0f + sc0.x; scv[1] = 1.0f + sc0.y; scv[2] = 1.0f + sc0.z; scv[3] = 1.0f + sc0.w;
-            scv[4] = 1.0f + sc1.x; scv[5] = 1.0f + sc1.y; scv[6] = 1.0f + sc1.z; scv[7] = 1.0f + sc1.w;
+        if (kCacheMod && seg != seg_loaded) {
+#pragma unroll
+            for (int i = 0; i < (kCacheMod ? NCH : 1); ++i) load_mod(seg, i, shv[i], scv[i]);
             seg_loaded = seg;
         }
-        Chunk16 out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float a = fmaf(bf2f(xc[r].h[2 * e]) * rinv, scv[2 * e], shv[2 * e]);
-            const float b = fmaf(bf2f(xc[r].h[2 * e + 1]) * rinv, scv[2 * e + 1], shv[2 * e + 1]);
-            out.w[e] = pack_bf16x2(a, b);
+        for (int i = 0; i < NCH; ++i) {
+            float sh[8], sc[8];
+            if (kCacheMod) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { sh[e] = shv[kCacheMod ? i : 0][e]; sc[e] = scv[kCacheMod ? i : 0][e]; }
+            } else {
+                load_mod(seg, i, sh, sc);
+            }
+            Chunk16 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = fmaf(bf2f(xc[r][i].h[2 * e]) * rinv, sc[2 * e], sh[2 * e]);
+                const float b = fmaf(bf2f(xc[r][i].h[2 * e + 1]) * rinv, sc[2 * e + 1], sh[2 * e + 1]);
+                out.w[e] = pack_bf16x2(a, b);
+            }
+            store_stream16(h + t * hidden + (i * 64 + lane) * 8, out.u);
         }
-        store_stream16(h + t * hidden + c0, out.u);
     }
 }
 
@@ -163,6 +172,23 @@ hipError_t launch_modulation_nch(int nch, dim3 grid, hipStream_t stream, Args...
     return hipGetLastError();
 }
 
+template <typename... Args>
+hipError_t launch_adaln_nch(int nch, dim3 grid, hipStream_t stream, Args... args) {
+    switch (nch) {
+#define H3_ADALN_CASE(N)                                                                       \
+    case N:                                                                                  \
+        hipLaunchKernelGGL(adaln_kernel<N>, grid, dim3(64 * kAdalnWaves), 0, stream, args...); \
+        break;
+        H3_ADALN_CASE(1) H3_ADALN_CASE(2) H3_ADALN_CASE(3) H3_ADALN_CASE(4)
+        H3_ADALN_CASE(5) H3_ADALN_CASE(6) H3_ADALN_CASE(7) H3_ADALN_CASE(8)
+        H3_ADALN_CASE(9) H3_ADALN_CASE(10) H3_ADALN_CASE(11) H3_ADALN_CASE(12)
+        H3_ADALN_CASE(13) H3_ADALN_CASE(14) H3_ADALN_CASE(15) H3_ADALN_CASE(16)
+#undef H3_ADALN_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 #undef H3_NCH_CASE
 
 }  // namespace
@@ -181,10 +207,10 @@ hipError_t launch_adaln(const uint16_t* x, uint16_t* h, const float* shift, cons
                         int hidden, float eps, hipStream_t stream) {
     if (total_tokens == 0) return hipSuccess;
     if (hidden % 512 != 0 || hidden > 8192) return hipErrorInvalidValue;
-    const dim3 grid((total_tokens + kRows - 1) / kRows);
-    hipLaunchKernelGGL(adaln_kernel, grid, dim3(hidden / 8), 0, stream, x, h, shift, scale,
-                       mod_stride, cu, num_seqs, total_tokens, hidden, eps);
-    return hipGetLastError();
+    constexpr int rows_per_block = kRowsPerWave * kAdalnWaves;
+    const dim3 grid((total_tokens + rows_per_block - 1) / rows_per_block);
+    return launch_adaln_nch(hidden / 512, grid, stream, x, h, shift, scale, mod_stride, cu,
+                            num_seqs, total_tokens, eps);
 }
 
 }  // namespace h3
