@@ -282,6 +282,17 @@ def main():
                                                    out=taps["h2"])),
             flops=2.0 * n * wl.ffn * c)
 
+    # Attention at one rank's share of an 8-way head split (3 of the 24 heads,
+    # all 57,960 tokens): 681 work items on 256 CUs, where the last partial
+    # wave of work items shows.
+    if not args.no_stages:
+        h_rank = max(1, wl.heads // 8)
+        o_rank = torch.empty(n, h_rank, wl.head_dim, dtype=torch.bfloat16, device=dev)
+        rank_attn = lambda: ops.attn_varlen(qv[:, :h_rank], kv[:, :h_rank], vv[:, :h_rank], cu_d,
+                                            cu, out=o_rank, workspace=attn_ws)
+        rec(f"attention_bf16_per_rank_h{h_rank}", sampler(rank_attn, stage_iters, False),
+            flops=attention_flops(wl.lengths, h_rank, wl.head_dim))
+
     fp8 = None
     if not args.no_fp8:
         log("timing fp8 attention")
