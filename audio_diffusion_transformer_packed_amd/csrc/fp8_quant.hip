@@ -9,9 +9,21 @@
 // segment start), V one scale per (segment, head, channel); scale = amax /
 // 448 (1 when amax is 0) and code = e4m3(x / scale), round to nearest even,
 // clamped to +-448, with the scale taken exactly: code = RNE(448 x / amax).
-// For bf16 x, 448 x is exact in fp32 and one IEEE division decides exactly
-// (a quotient on a rounding midpoint stays on it and goes to the even code;
-// any other is far from one), so no rounded scale enters the decision.
+//
+// The code decision is exact without a division per element. For bf16 x
+// and amax, 448 x has at most 11 significant bits, amax at most 8, and an
+// e4m3 rounding midpoint m at most 5, so 448 x - m amax is either 0 (the
+// quotient is on the midpoint) or a nonzero multiple of the smaller of the
+// two products' last-place units; both products have integer significands
+// below 255 * 31 = 7905, so the quotient then lies more than 2^-13
+// (relative) from m. The product x * fl(448 / amax) is within 2^-23 of
+// the quotient; rounding it to 16 significant bits (fp8_snap: half a step is
+// 2^-16) lands exactly on m in the first case and stays on the quotient's
+// side of m in the second, so the hardware's round-to-nearest-even
+// conversion of the snapped value gives the code of the exact quotient
+// (ties to even included). Since |x| <= amax the snapped value never exceeds
+// 448, so no clamp is needed. Blocks with amax < 2^-64 scale x and amax by
+// 2^64 first (exact) so that 448 / amax stays finite.
 //
 // Layouts written (T = sum over segments of ceil(L_s / 64), the key tiles):
 //   q8   [N, H, 128]        token-major, like q;
@@ -23,7 +35,13 @@
 //                           sits at position 32g + 16b + 4i + e, the order
 //                           in which the attention kernel's lanes hold P;
 //   q_scale, k_scale [T, H];  v_scale [B, H, 128].
-// All HBM-bound; each kernel reads its input once with 16-byte loads.
+// All HBM-bound: q, k, v are streamed once by quant_qk_kernel and v once
+// more by quant_v_kernel (V's scale needs the whole segment first), with
+// 16-byte nontemporal loads. Work items are ordered head-fastest, so the
+// workgroups resident at one time read whole token rows. Q and K codes are
+// stored nontemporally; V code rows are 64 bytes, half a cache line, so
+// they are stored through L2, which merges the two halves before write-back
+// (nontemporal stores there measured 15 % slower).
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -38,35 +56,59 @@ __device__ __forceinline__ float fp8_scale_of(float amax) {
     return amax > 0.f ? amax / kE4M3Max : 1.0f;
 }
 
-// Divisor of 448 x for the code (amax, or 1 when amax == 0 and x == 0).
-__device__ __forceinline__ float fp8_den_of(float amax) { return amax > 0.f ? amax : 1.0f; }
-
-// Two fp32 -> two e4m3 codes in the low 16 bits.
-__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
-    a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
-    b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
-    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
+// x -> 448 x / amax as (x * pre) * mul, see the header comment. amax == 0
+// means every x of the block is 0, and any finite mul gives code 0.
+struct Fp8Mul {
+    float pre, mul;
+};
+__device__ __forceinline__ Fp8Mul fp8_mul_of(float amax) {
+    const float pre = amax < 0x1p-64f ? 0x1p64f : 1.0f;
+    return {pre, amax > 0.f ? kE4M3Max / (amax * pre) : 0.f};
 }
 
-// Codes of x[j0 .. j0+3]: RNE(448 x / den), four bytes.
-__device__ __forceinline__ uint32_t codes4(const float (&x)[8], int j0, float den) {
-    return e4m3x2(kE4M3Max * x[j0] / den, kE4M3Max * x[j0 + 1] / den) |
-           (e4m3x2(kE4M3Max * x[j0 + 2] / den, kE4M3Max * x[j0 + 3] / den) << 16);
+// Round to 16 significant bits, ties away from zero (integer add on the
+// magnitude bits; the sign bit is untouched for finite values).
+__device__ __forceinline__ float fp8_snap(float y) {
+    return __uint_as_float((__float_as_uint(y) + 0x80u) & ~0xffu);
 }
 
-__device__ __forceinline__ float block_max(float v, float* red) {
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 8, 64));
-    v = fmaxf(v, __shfl_xor(v, 4, 64));
-    v = fmaxf(v, __shfl_xor(v, 2, 64));
-    v = fmaxf(v, __shfl_xor(v, 1, 64));
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wave] = v;
-    __syncthreads();
-    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
+__device__ __forceinline__ float fp8_prep(float x, Fp8Mul m) { return fp8_snap((x * m.pre) * m.mul); }
+
+// Codes of a and b into bytes 0, 1 (Hi = false) or 2, 3 (Hi = true) of `old`.
+template <bool Hi>
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b, uint32_t old) {
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(old), Hi));
+}
+
+// Codes of the eight values of a bf16 chunk, byte j = value j.
+__device__ __forceinline__ u32x2 codes8(uint4 raw, Fp8Mul m) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    u32x2 out;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const uint32_t lo = w[2 * p], hi = w[2 * p + 1];
+        uint32_t c = e4m3x2<false>(fp8_prep(__uint_as_float(lo << 16), m),
+                                   fp8_prep(__uint_as_float(lo & 0xffff0000u), m), 0u);
+        c = e4m3x2<true>(fp8_prep(__uint_as_float(hi << 16), m),
+                         fp8_prep(__uint_as_float(hi & 0xffff0000u), m), c);
+        out[p] = c;
+    }
+    return out;
+}
+
+__device__ __forceinline__ float absmax8(uint4 raw) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float m = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[p] << 16)), fabsf(__uint_as_float(w[p] & 0xffff0000u))));
     return m;
+}
+
+// Value j (0..7) of a bf16 chunk as fp32.
+__device__ __forceinline__ float chunk_val(uint4 raw, int j) {
+    const uint32_t w = j < 2 ? raw.x : j < 4 ? raw.y : j < 6 ? raw.z : raw.w;
+    return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
 // tb[s] = sum_{r < s} ceil(L_r / 64), tb[B] = T. One workgroup.
@@ -105,88 +147,86 @@ __device__ __forceinline__ void tile_origin(const int32_t* cu, const int32_t* tb
 // Thread's four 8-value chunks of a 64 x 128 tile: chunk c = tid + 256 i is
 // token c / 16, channels 8 (c % 16) + [0, 8); rows >= `rows` read as 0.
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ base, int64_t stride,
-                                          int64_t t0, int rows, int head, float (&x)[4][8]) {
+                                          int64_t t0, int rows, int head, uint4 (&x)[4]) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int c = tid + 256 * i;
         const int tok = c >> 4, dc = c & 15;
-        u32x4 raw = {0, 0, 0, 0};
-        if (tok < rows)
-            raw = *reinterpret_cast<const u32x4*>(base + (t0 + tok) * stride + head * kD + 8 * dc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[i][2 * j] = __uint_as_float(raw[j] << 16);
-            x[i][2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
-        }
+        x[i] = make_uint4(0, 0, 0, 0);
+        if (tok < rows) x[i] = load_stream16(base + (t0 + tok) * stride + head * kD + 8 * dc);
     }
 }
 
-// One workgroup per (key tile, head): Q and K codes + block scales, and the
-// tile's channel amax of V (reduced per segment afterwards).
+// One workgroup per (key tile, head), head-fastest: Q and K codes + block
+// scales, and the tile's channel amax of V (reduced per segment afterwards).
 __global__ __launch_bounds__(256) void quant_qk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int64_t qs, int64_t ks, int64_t vs, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ tb, int num_seqs, int num_heads, int64_t num_tiles,
     uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, float* __restrict__ qsc,
     float* __restrict__ ksc, float* __restrict__ vpart) {
-    __shared__ float red[4];
+    __shared__ float red[2][4];
     __shared__ float vred[4][kD];
-    const int tile = blockIdx.x, h = blockIdx.y;
+    const int tile = static_cast<int>(blockIdx.x / static_cast<unsigned>(num_heads));
+    const int h = static_cast<int>(blockIdx.x - static_cast<unsigned>(tile) * num_heads);
     int seg, t0, rows;
     tile_origin(cu, tb, num_seqs, tile, seg, t0, rows);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int64_t row_bytes = static_cast<int64_t>(num_heads) * kD;
-    float xq[4][8], xk[4][8], xv[4][8];
+    uint4 xq[4], xk[4], xv[4];
     load_tile(q, qs, t0, rows, h, xq);
     load_tile(k, ks, t0, rows, h, xk);
     load_tile(v, vs, t0, rows, h, xv);
     float mq = 0.f, mk = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            mq = fmaxf(mq, fabsf(xq[i][j]));
-            mk = fmaxf(mk, fabsf(xk[i][j]));
-        }
-    const float amax_q = block_max(mq, red);
-    const float amax_k = block_max(mk, red);
-    const float dq = fp8_den_of(amax_q), dk = fp8_den_of(amax_k);
-    uint8_t* kt = k8 + ((static_cast<int64_t>(h) * num_tiles + tile) * kTB) * kD;
-#pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;
-        const int tok = c >> 4, dc = c & 15;
-        if (tok < rows) {
-            u32x2 w;
-            w.x = codes4(xq[i], 0, dq);
-            w.y = codes4(xq[i], 4, dq);
-            *reinterpret_cast<u32x2*>(q8 + (t0 + tok) * row_bytes + h * kD + 8 * dc) = w;
-        }
-        u32x2 w;                              // K rows past the segment end are 0
-        w.x = codes4(xk[i], 0, dk);
-        w.y = codes4(xk[i], 4, dk);
-        *reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc) = w;
+        mq = fmaxf(mq, absmax8(xq[i]));
+        mk = fmaxf(mk, absmax8(xk[i]));
     }
-    if (tid == 0) {
-        qsc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_q);
-        ksc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_k);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        mq = fmaxf(mq, __shfl_xor(mq, off, 64));
+        mk = fmaxf(mk, __shfl_xor(mk, off, 64));
+    }
+    if ((tid & 63) == 0) {
+        red[0][wave] = mq;
+        red[1][wave] = mk;
     }
     // V: channel amax over this tile's tokens; the 4 tokens tid / 16 + 16 i
     // share channel chunk tid % 16 with lanes tid ^ 16 and tid ^ 32
     float vm[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        float a = fmaxf(fmaxf(fabsf(xv[0][j]), fabsf(xv[1][j])), fmaxf(fabsf(xv[2][j]), fabsf(xv[3][j])));
+        float a = fmaxf(fmaxf(fabsf(chunk_val(xv[0], j)), fabsf(chunk_val(xv[1], j))),
+                        fmaxf(fabsf(chunk_val(xv[2], j)), fabsf(chunk_val(xv[3], j))));
         a = fmaxf(a, __shfl_xor(a, 16, 64));
         a = fmaxf(a, __shfl_xor(a, 32, 64));
         vm[j] = a;
     }
     if ((tid & 63) < 16) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vred[tid >> 6][8 * (tid & 15) + j] = vm[j];
+        for (int j = 0; j < 8; ++j) vred[wave][8 * (tid & 15) + j] = vm[j];
     }
     __syncthreads();
+    const float amax_q = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    const float amax_k = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    const Fp8Mul mulq = fp8_mul_of(amax_q), mulk = fp8_mul_of(amax_k);
+    uint8_t* kt = k8 + ((static_cast<int64_t>(h) * num_tiles + tile) * kTB) * kD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i;
+        const int tok = c >> 4, dc = c & 15;
+        if (tok < rows)
+            __builtin_nontemporal_store(codes8(xq[i], mulq),
+                                        reinterpret_cast<u32x2*>(q8 + (t0 + tok) * row_bytes + h * kD + 8 * dc));
+        // K rows past the segment end are 0
+        __builtin_nontemporal_store(codes8(xk[i], mulk), reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc));
+    }
+    if (tid == 0) {
+        qsc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_q);
+        ksc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_k);
+    }
     if (tid < kD) {
         const float a = fmaxf(fmaxf(vred[0][tid], vred[1][tid]), fmaxf(vred[2][tid], vred[3][tid]));
         vpart[(static_cast<int64_t>(tile) * num_heads + h) * kD + tid] = a;
@@ -194,7 +234,7 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
 }
 
 // v_scale[s, h, c] (and the channel amax) from the tile partials of segment s. Block: 32 columns x
-// 32 tile slices; grid (B, H * 128 / 32).
+// 32 tile slices, eight loads in flight per thread; grid (B, H * 128 / 32).
 __global__ __launch_bounds__(1024) void vscale_kernel(const float* __restrict__ vpart,
                                                       const int32_t* __restrict__ tb, int num_heads,
                                                       float* __restrict__ vsc, float* __restrict__ vamax) {
@@ -203,52 +243,66 @@ __global__ __launch_bounds__(1024) void vscale_kernel(const float* __restrict__ 
     const int col = threadIdx.x & 31, slice = threadIdx.x >> 5;
     const int64_t cols = static_cast<int64_t>(num_heads) * kD;
     const int64_t c = static_cast<int64_t>(blockIdx.y) * 32 + col;
-    float m = 0.f;
-    for (int j = tb[seg] + slice; j < tb[seg + 1]; j += 32) m = fmaxf(m, vpart[j * cols + c]);
-    red[slice][col] = m;
+    const int end = tb[seg + 1];
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int j = tb[seg] + slice;
+    for (; j + 7 * 32 < end; j += 8 * 32) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m[u] = fmaxf(m[u], vpart[(j + 32 * u) * cols + c]);
+    }
+    for (; j < end; j += 32) m[0] = fmaxf(m[0], vpart[j * cols + c]);
+    float mm = fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+    red[slice][col] = mm;
     __syncthreads();
     if (slice == 0) {
-        for (int i = 1; i < 32; ++i) m = fmaxf(m, red[i][col]);
-        vsc[seg * cols + c] = fp8_scale_of(m);
-        vamax[seg * cols + c] = m;
+        for (int i = 1; i < 32; ++i) mm = fmaxf(mm, red[i][col]);
+        vsc[seg * cols + c] = fp8_scale_of(mm);
+        vamax[seg * cols + c] = mm;
     }
 }
 
-// One workgroup per (key tile, head): V codes, transposed and permuted
-// through LDS, written as one contiguous 8 KB block.
-__global__ __launch_bounds__(256) void quant_v_kernel(
+// One wave per (key tile, head), head-fastest: V codes of the tile,
+// transposed and key-permuted, straight to HBM. Lane 16 u + dc (u = 2 b + g)
+// owns the 16-byte chunk 2 g + b (positions 16 (2 g + b) .. + 15) of channel
+// rows 8 dc .. 8 dc + 7; those positions hold keys 32 b + 8 i + 4 g + e
+// (i, e in 0..3, position 16 (2 g + b) + 4 i + e), so the lane reads channels
+// 8 dc .. 8 dc + 7 of those 16 keys and writes eight 16-byte chunks.
+__global__ __launch_bounds__(64) void quant_v_kernel(
     const uint16_t* __restrict__ v, int64_t vs, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ tb, int num_seqs, int num_heads, int64_t num_tiles,
     const float* __restrict__ vamax, uint8_t* __restrict__ v8t) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kD * kTB];
-    const int tile = blockIdx.x, h = blockIdx.y;
+    const int tile = static_cast<int>(blockIdx.x / static_cast<unsigned>(num_heads));
+    const int h = static_cast<int>(blockIdx.x - static_cast<unsigned>(tile) * num_heads);
     int seg, t0, rows;
     tile_origin(cu, tb, num_seqs, tile, seg, t0, rows);
-    const int tid = threadIdx.x;
-    float x[4][8];
-    load_tile(v, vs, t0, rows, h, x);
-    const int dc = tid & 15;
-    float den[8];
+    const int lane = threadIdx.x, dc = lane & 15, u = lane >> 4, g = u & 1, b = u >> 1;
+    uint4 x[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        den[j] = fp8_den_of(vamax[(static_cast<int64_t>(seg) * num_heads + h) * kD + 8 * dc + j]);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int key = (tid >> 4) + 16 * i;
-        const int b = key >> 5, r = key & 31;
-        const int pos = 32 * ((r >> 2) & 1) + 16 * b + 4 * (r >> 3) + (r & 3);
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-            const uint32_t w = e4m3x2(kE4M3Max * x[i][j] / den[j], kE4M3Max * x[i][j + 1] / den[j + 1]);
-            lds[(8 * dc + j) * kTB + pos] = static_cast<uint8_t>(w & 0xff);
-            lds[(8 * dc + j + 1) * kTB + pos] = static_cast<uint8_t>(w >> 8);
+        for (int e = 0; e < 4; ++e) {
+            const int key = 32 * b + 8 * i + 4 * g + e;
+            x[4 * i + e] = make_uint4(0, 0, 0, 0);
+            if (key < rows) x[4 * i + e] = load_stream16(v + (t0 + key) * vs + h * kD + 8 * dc);
         }
+    const float4* am4 = reinterpret_cast<const float4*>(vamax + (static_cast<int64_t>(seg) * num_heads + h) * kD + 8 * dc);
+    const float4 a0 = am4[0], a1 = am4[1];
+    const float am[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    uint8_t* dst = v8t + ((static_cast<int64_t>(h) * num_tiles + tile) * kD + 8 * dc) * kTB + 16 * (2 * g + b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const Fp8Mul m = fp8_mul_of(am[j]);
+        uint4 w;
+        uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t c = e4m3x2<false>(fp8_prep(chunk_val(x[4 * i], j), m),
+                                             fp8_prep(chunk_val(x[4 * i + 1], j), m), 0u);
+            wp[i] = e4m3x2<true>(fp8_prep(chunk_val(x[4 * i + 2], j), m),
+                                 fp8_prep(chunk_val(x[4 * i + 3], j), m), c);
+        }
+        *reinterpret_cast<uint4*>(dst + j * kTB) = w;   // plain: L2 joins the 64-byte halves of each line
     }
-    __syncthreads();
-    uint8_t* dst = v8t + ((static_cast<int64_t>(h) * num_tiles + tile) * kD) * kTB;
-    const u32x4* src = reinterpret_cast<const u32x4*>(lds);
-    reinterpret_cast<u32x4*>(dst)[tid] = src[tid];
-    reinterpret_cast<u32x4*>(dst)[tid + 256] = src[tid + 256];
 }
 
 }  // namespace
@@ -271,19 +325,21 @@ hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint1
                                uint8_t* v8t, float* qsc, float* ksc, float* vsc, void* workspace,
                                hipStream_t stream) {
     if (num_seqs <= 0 || num_tiles <= 0) return hipSuccess;
+    if (num_tiles * num_heads > 0xffffffffll) return hipErrorInvalidValue;   // 1-D grid of (tile, head)
     int32_t* tb = static_cast<int32_t*>(workspace);
     const size_t tb_bytes = ((static_cast<size_t>(num_seqs) + 1) * sizeof(int32_t) + 255) & ~size_t(255);
     const size_t va_bytes = (static_cast<size_t>(num_seqs) * num_heads * kD * sizeof(float) + 255) & ~size_t(255);
     float* vamax = reinterpret_cast<float*>(static_cast<char*>(workspace) + tb_bytes);
     float* vpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + tb_bytes + va_bytes);
     hipLaunchKernelGGL(tile64_scan_kernel, dim3(1), dim3(1024), 0, stream, cu, num_seqs, tb);
-    hipLaunchKernelGGL(quant_qk_kernel, dim3(static_cast<unsigned>(num_tiles), num_heads), dim3(256), 0, stream,
+    const unsigned items = static_cast<unsigned>(num_tiles * num_heads);
+    hipLaunchKernelGGL(quant_qk_kernel, dim3(items), dim3(256), 0, stream,
                        q, k, v, qs, ks, vs, cu, tb, num_seqs, num_heads, num_tiles, q8, k8, qsc, ksc,
                        vpart);
     hipLaunchKernelGGL(vscale_kernel, dim3(num_seqs, num_heads * kD / 32), dim3(1024), 0, stream,
                        vpart, tb, num_heads, vsc, vamax);
-    hipLaunchKernelGGL(quant_v_kernel, dim3(static_cast<unsigned>(num_tiles), num_heads), dim3(256), 0,
-                       stream, v, vs, cu, tb, num_seqs, num_heads, num_tiles, vamax, v8t);
+    hipLaunchKernelGGL(quant_v_kernel, dim3(items), dim3(64), 0, stream, v, vs, cu, tb, num_seqs,
+                       num_heads, num_tiles, vamax, v8t);
     return hipGetLastError();
 }
 

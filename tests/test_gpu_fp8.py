@@ -64,13 +64,8 @@ def _scaled_inputs(lens, heads, seed):
     return cu, out
 
 
-@pytest.mark.parametrize("lens", [[100, 0, 64, 257, 1], [65], [0, 3, 0]])
-def test_fp8_quantize_codes_and_scales_bit_exact(dev, ops, lens):
-    heads = 3
-    announce(f"fp8 quantise lens={lens} H={heads}")
-    cu, (q, k, v) = _scaled_inputs(lens, heads, 301)
-    res = ops.fp8_quantize(to_dev_bf16(q, dev), to_dev_bf16(k, dev), to_dev_bf16(v, dev),
-                           to_dev_i32(cu, dev), cu)
+def _assert_quantize_matches(ops, res, q, k, v, cu, lens, heads):
+    """Codes and scales of h3_fp8_quantize equal the oracle's bit for bit."""
     qc, qs = oracle.quantize_qk_blocks(q.f32, cu, 64)
     kc, ks = oracle.quantize_qk_blocks(k.f32, cu, 64)
     vc, vs = oracle.quantize_v_channels(v.f32, cu)
@@ -94,6 +89,77 @@ def test_fp8_quantize_codes_and_scales_bit_exact(dev, ops, lens):
             assert np.array_equal(v8[:, tile], want_v), (s, t0)
             tile += 1
     assert tile == k8.shape[1] == ops.fp8_num_tiles(cu)
+
+
+@pytest.mark.parametrize("lens", [[100, 0, 64, 257, 1], [65], [0, 3, 0]])
+def test_fp8_quantize_codes_and_scales_bit_exact(dev, ops, lens):
+    heads = 3
+    announce(f"fp8 quantise lens={lens} H={heads}")
+    cu, (q, k, v) = _scaled_inputs(lens, heads, 301)
+    res = ops.fp8_quantize(to_dev_bf16(q, dev), to_dev_bf16(k, dev), to_dev_bf16(v, dev),
+                           to_dev_i32(cu, dev), cu)
+    _assert_quantize_matches(ops, res, q, k, v, cu, lens, heads)
+
+
+def _e4m3_midpoints() -> np.ndarray:
+    vals = [m * 2.0 ** -9 for m in range(8)]
+    vals += [(1 + m / 8) * 2.0 ** e for e in range(-6, 9) for m in range(8)]
+    grid = np.array([x for x in vals if x <= 448.0])
+    return (grid[:-1] + grid[1:]) / 2
+
+
+def _pattern(kind, rows, rng) -> np.ndarray:
+    """[rows, 128] float32 values that are exact bf16 numbers.
+    ties(a): +-m a / 448 for e4m3 midpoints m, with one +-a in every column, so
+    every block and channel has amax a and many quotients 448 x / a are exact
+    midpoints; 24.5 makes 448 / a inexact in fp32, 24.5 * 2^-70 takes the
+    pre-scaled path for tiny blocks. subnormal: bf16 subnormals only."""
+    tie_amax = {"ties448": 448.0, "ties24": 24.5, "tiny": 24.5 * 2.0 ** -70}
+    if kind in tie_amax:
+        amax = tie_amax[kind]
+        x = rng.choice(_e4m3_midpoints(), size=(rows, D)) * amax / 448.0
+        x[rng.integers(0, rows, size=D), np.arange(D)] = amax
+        x *= rng.choice([-1.0, 1.0], size=(rows, D))
+        return x.astype(np.float32)
+    if kind == "subnormal":
+        bits = (rng.integers(1, 128, size=(rows, D)).astype(np.uint32) << 16)
+        bits |= rng.integers(0, 2, size=(rows, D)).astype(np.uint32) << 31
+        return bits.view(np.float32)
+    if kind == "zero":
+        return np.zeros((rows, D), np.float32)
+    x = rng.standard_normal((rows, D)) * np.power(10.0, rng.uniform(-2, 2, size=(rows, 1)))
+    return h3synth.Bf16Array.from_f32(x.astype(np.float32)).f32
+
+
+def test_fp8_quantize_ties_tiny_subnormal_and_zero_blocks(dev, ops):
+    """Blocks and channels built so that the code decision meets its edge
+    cases: exact rounding midpoints (ties to even) with exact and inexact
+    448 / amax, blocks with amax below 2^-64, bf16 subnormals, all-zero
+    blocks and channels, and a ragged last tile."""
+    lens = [64, 64, 64, 100, 1]
+    heads = 2
+    kinds = [("ties448", "ties24"), ("tiny", "subnormal"), ("zero", "random"),
+             ("random", "random"), ("random", "ties24")]
+    announce(f"fp8 quantise edge blocks lens={lens} H={heads}")
+    cu = h3synth.cu_from_lengths(lens)
+    n = int(cu[-1])
+    rng = np.random.default_rng(303)
+    arrays = []
+    for t in range(3):
+        a = np.zeros((n, heads, D), np.float32)
+        for s, (k0, k1) in enumerate(kinds):
+            r0, r1 = int(cu[s]), int(cu[s + 1])
+            a[r0:r1, 0] = _pattern(k0, r1 - r0, rng)
+            a[r0:r1, 1] = _pattern(k1, r1 - r0, rng)
+        if t == 2:
+            a[int(cu[3]):int(cu[4]), 0, 5:9] = 0.0          # zero V channels in one segment
+        b = h3synth.Bf16Array.from_f32(a)
+        assert np.array_equal(b.f32, a)                     # every value is a bf16 number
+        arrays.append(b)
+    q, k, v = arrays
+    res = ops.fp8_quantize(to_dev_bf16(q, dev), to_dev_bf16(k, dev), to_dev_bf16(v, dev),
+                           to_dev_i32(cu, dev), cu)
+    _assert_quantize_matches(ops, res, q, k, v, cu, lens, heads)
 
 
 def _relf(a, b) -> float:
