@@ -186,21 +186,59 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         __syncthreads();
     }
 
-    // ---- epilogue: acc[bi][bj] register 4 q + e holds output row
-    // m = m0 + 128 wm + 32 bj + l32, W-tile row 64 wn + 32 bi + 8 q + 4 g + e ----
+    // ---- epilogue through LDS. acc[bi][bj] register 4 q + e holds output
+    // row 128 wm + 32 bj + l32 of the tile and W-tile row 64 wn + 32 bi +
+    // 8 q + 4 g + e, so a lane owns one row and a wave store would write 8
+    // bytes into each of 32 rows (one L2 write request per 16 bytes). Each
+    // wave instead stages its own 128 x 64 outputs in 16 KB of the (now
+    // free) stage buffers, 16-byte chunks of row r XOR-swizzled by r / 2,
+    // and reads them back row-contiguous, so 8 (or 4) lanes write a row's
+    // 128 (64) bytes together with 16-byte stores. The staging is
+    // wave-local: only this wave's LDS accesses need ordering.
+    char* ep = smem + wave * (2 * kStageBytes / kWaves);
+    const bool vec16 = ((reinterpret_cast<uintptr_t>(Y) | reinterpret_cast<uintptr_t>(res)) & 15) == 0;
+    auto lds_fence = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+    auto store8 = [&](uint16_t* dst, uint4 v) __attribute__((always_inline)) {
+        if (vec16) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+            reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+        }
+    };
+    const int64_t mw = m0 + 128 * wm;        // first row of this wave's outputs
+    if (EPI == kEpiStore) {
+        // 128 rows x 64 bf16 (128 B) per wave
 #pragma unroll
-    for (int bj = 0; bj < kWM; ++bj) {
-        const int64_t m = m0 + 128 * wm + 32 * bj + l32;
-        if (m >= M) continue;
-        int seg = 0;
-        if (EPI == kEpiGatedResidual && num_seqs > 1) seg = find_segment(cu, num_seqs, m);
-        if (EPI == kEpiSwiGLU) {
-            // bi = 0 is the gate block, bi = 1 the up block of output columns
-            // n0 + 32 wn + [0, 32)
+        for (int bj = 0; bj < kWM; ++bj) {
+            const int r = 32 * bj + l32;
+#pragma unroll
+            for (int bi = 0; bi < kWN; ++bi)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = 4 * bi + q;
+                    u32x2 w;
+                    w.x = pack_bf16x2(acc[bi][bj][4 * q], acc[bi][bj][4 * q + 1]);
+                    w.y = pack_bf16x2(acc[bi][bj][4 * q + 2], acc[bi][bj][4 * q + 3]);
+                    *reinterpret_cast<u32x2*>(ep + r * 128 + 16 * (c ^ ((r >> 1) & 7)) + 8 * g) = w;
+                }
+        }
+        lds_fence();
+        const int64_t n = n0 + 64 * wn + 8 * (lane & 7);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = 8 * j + (lane >> 3);
+            const uint4 v = *reinterpret_cast<const uint4*>(ep + r * 128 + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+            if (mw + r < M && n < N) store8(Y + (mw + r) * N + n, v);
+        }
+    } else if (EPI == kEpiSwiGLU) {
+        // bi = 0 is the gate block, bi = 1 the up block of output columns
+        // n0 + 32 wn + [0, 32): 128 rows x 32 bf16 (64 B) per wave
+#pragma unroll
+        for (int bj = 0; bj < kWM; ++bj) {
+            const int r = 32 * bj + l32;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + 32 * wn + 8 * q + 4 * g;
-                if (n >= N) continue;                // N % 4 == 0: groups are all in or out
                 float o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -211,31 +249,72 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
                 u32x2 w;
                 w.x = pack_bf16x2(o[0], o[1]);
                 w.y = pack_bf16x2(o[2], o[3]);
-                *reinterpret_cast<u32x2*>(Y + m * N + n) = w;
+                *reinterpret_cast<u32x2*>(ep + r * 64 + 16 * (q ^ ((r >> 2) & 3)) + 8 * g) = w;
             }
-        } else {
+        }
+        lds_fence();
+        const int64_t n = n0 + 32 * wn + 8 * (lane & 3);
 #pragma unroll
-            for (int bi = 0; bi < kWN; ++bi) {
+        for (int j = 0; j < 8; ++j) {
+            const int r = 16 * j + (lane >> 2);
+            const uint4 v = *reinterpret_cast<const uint4*>(ep + r * 64 + 16 * ((lane & 3) ^ ((r >> 2) & 3)));
+            if (mw + r < M && n < N) store8(Y + (mw + r) * N + n, v);
+        }
+    } else {
+        // y = res + gate[seg] * acc, rounded once: fp32 staging, one 32-column
+        // block (bi) at a time, 128 rows x 32 fp32 (128 B) per wave
+        int segs[kWM];
+#pragma unroll
+        for (int bj = 0; bj < kWM; ++bj) {
+            const int64_t m = mw + 32 * bj + l32;
+            segs[bj] = (num_seqs > 1 && m < M) ? find_segment(cu, num_seqs, m) : 0;
+        }
+#pragma unroll
+        for (int bi = 0; bi < kWN; ++bi) {
+            if (bi > 0) lds_fence();       // previous block's reads are done before it is overwritten
+#pragma unroll
+            for (int bj = 0; bj < kWM; ++bj) {
+                const int r = 32 * bj + l32;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int64_t n = n0 + 64 * wn + 32 * bi + 8 * q + 4 * g;
-                    if (n >= N) continue;
-                    float o[4];
-                    if (EPI == kEpiStore) {
+                    const int c = 2 * q + g;
+                    f32x4 v = {acc[bi][bj][4 * q], acc[bi][bj][4 * q + 1], acc[bi][bj][4 * q + 2],
+                               acc[bi][bj][4 * q + 3]};
+                    *reinterpret_cast<f32x4*>(ep + r * 128 + 16 * (c ^ ((r >> 1) & 7))) = v;
+                }
+            }
+            lds_fence();
+            const int64_t n = n0 + 64 * wn + 32 * bi + 8 * (lane & 3);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) o[e] = acc[bi][bj][4 * q + e];
+            for (int j = 0; j < 8; ++j) {
+                const int r = 16 * j + (lane >> 2);
+                // rows 16 j .. 16 j + 15 lie in 32-row block j / 2
+                const int seg = num_seqs > 1 ? __shfl(segs[j >> 1], r & 31, 64) : 0;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(ep + r * 128 + 16 * ((2 * (lane & 3)) ^ ((r >> 1) & 7)));
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(ep + r * 128 + 16 * ((2 * (lane & 3) + 1) ^ ((r >> 1) & 7)));
+                const int64_t m = mw + r;
+                if (m < M && n < N) {
+                    uint4 rv;
+                    if (vec16) {
+                        rv = *reinterpret_cast<const uint4*>(res + m * N + n);
                     } else {
-                        const u32x2 rv = *reinterpret_cast<const u32x2*>(res + m * N + n);
-                        const f32x4 gt = *reinterpret_cast<const f32x4*>(gate + seg * gate_stride + n);
-                        const float rr[4] = {__uint_as_float(rv.x << 16), __uint_as_float(rv.x & 0xffff0000u),
-                                             __uint_as_float(rv.y << 16), __uint_as_float(rv.y & 0xffff0000u)};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) o[e] = fmaf(gt[e], acc[bi][bj][4 * q + e], rr[e]);
+                        const uint2 r0 = reinterpret_cast<const uint2*>(res + m * N + n)[0];
+                        const uint2 r1 = reinterpret_cast<const uint2*>(res + m * N + n)[1];
+                        rv = make_uint4(r0.x, r0.y, r1.x, r1.y);
                     }
-                    u32x2 w;
-                    w.x = pack_bf16x2(o[0], o[1]);
-                    w.y = pack_bf16x2(o[2], o[3]);
-                    *reinterpret_cast<u32x2*>(Y + m * N + n) = w;
+                    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gate + seg * gate_stride + n);
+                    const f32x4 g1 = *reinterpret_cast<const f32x4*>(gate + seg * gate_stride + n + 4);
+                    const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+                    const float a8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const float g8[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+                    uint32_t ow[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float x0 = fmaf(g8[2 * p], a8[2 * p], __uint_as_float(rw[p] << 16));
+                        const float x1 = fmaf(g8[2 * p + 1], a8[2 * p + 1], __uint_as_float(rw[p] & 0xffff0000u));
+                        ow[p] = pack_bf16x2(x0, x1);
+                    }
+                    store8(Y + m * N + n, make_uint4(ow[0], ow[1], ow[2], ow[3]));
                 }
             }
         }

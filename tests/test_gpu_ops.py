@@ -144,3 +144,27 @@ def test_gated_residual_in_place(dev, ops):
                               to_dev_i32(cu, dev), cu, out=r)
     ref = res.f32 + a.f32.astype(np.float64) @ w.f32.astype(np.float64).T
     compare(to_np(r), ref, "gated residual in place")
+
+
+def test_gated_residual_8_byte_aligned_views(dev, ops):
+    """res and y 8-byte but not 16-byte aligned (the epilogue's 8-byte path),
+    ragged in both tile dimensions."""
+    import torch
+    announce("gated residual, 8-byte aligned res / y views")
+    cu = h3synth.cu_from_lengths([170, 131])
+    m, n, k = 301, 264, 128
+    a, w, res = _bf((m, k), 63), _bf((n, k), 64, 0.05), _bf((m, n), 65)
+    gate = np.random.default_rng(66).standard_normal((2, n)).astype(np.float32)
+    r_big = torch.zeros(m * n + 4, dtype=torch.bfloat16, device=dev)
+    r = r_big[4:].view(m, n)
+    r.copy_(to_dev_bf16(res, dev))
+    y_big = torch.zeros(m * n + 4, dtype=torch.bfloat16, device=dev)
+    y = y_big[4:].view(m, n)
+    assert r.data_ptr() % 16 == 8 and y.data_ptr() % 16 == 8
+    ops.linear_gated_residual(to_dev_bf16(a, dev), to_dev_bf16(w, dev), r,
+                              torch.from_numpy(gate).to(dev), to_dev_i32(cu, dev), cu, out=y)
+    seg = oracle.segment_ids(cu)
+    ref = oracle.gated_residual_ref(res.f32, gate, a.f32.astype(np.float64)
+                                    @ w.f32.astype(np.float64).T, seg)
+    compare(to_np(y), ref, "gated residual 8-byte views")
+    assert float(y_big[:4].float().abs().sum()) == 0.0      # nothing written before y
