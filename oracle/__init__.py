@@ -9,7 +9,9 @@ invariants, special cases or brute force):
   segment_ids, tile_offsets, schedule_ref, rmsnorm, rope_3d,
   qk_norm_rope_ref, attn_varlen_ref, modulation_ref, adaln_modulate_ref,
   silu, swiglu_ref, gated_residual_ref, dit_block_ref, dit_block_rows_ref,
-  e4m3_round, fp8_attn_emulated_ref, bf16_round (storage emulation).
+  e4m3_round, fp8_attn_emulated_ref, bf16_round (storage emulation),
+  mx_scale_exponents, mx_quantize, mx_dequantize, mx_fake_quant, mx_linear_ref
+  (MXFP8 linears, OCP MX v1.0 reading).
 
 Parity unpinned: agreement of the block structure with the real model's
 block (the pages give operator names only, no equations or weights).
@@ -20,11 +22,14 @@ from .h3_oracle import (MOD_CHUNKS, adaln_modulate_ref, bf16_round, attn_varlen_
                         segment_ids, silu, split_modulation, swiglu_ref, tile_offsets)
 from .fp8_attention import (e4m3_round, fp8_attn_emulated_ref, quantize_qk_blocks,
                             quantize_v_channels)
+from .mx_linear import (mx_dequantize, mx_fake_quant, mx_linear_ref, mx_quantize,
+                        mx_scale_exponents)
 
 __all__ = [
     "MOD_CHUNKS", "adaln_modulate_ref", "bf16_round", "attn_varlen_ref", "check_cu_seqlens", "dit_block_ref",
     "dit_block_rows_ref", "gated_residual_ref", "modulation_ref", "qk_norm_rope_ref",
     "rel_frobenius", "rmsnorm", "rope_3d", "schedule_ref", "segment_ids", "silu",
     "split_modulation", "swiglu_ref", "tile_offsets", "e4m3_round", "fp8_attn_emulated_ref",
-    "quantize_qk_blocks", "quantize_v_channels",
+    "quantize_qk_blocks", "quantize_v_channels", "mx_dequantize", "mx_fake_quant", "mx_linear_ref",
+    "mx_quantize", "mx_scale_exponents",
 ]

@@ -38,7 +38,7 @@ module takes the plainest reading (all of them listed with the design notes):
 from __future__ import annotations
 
 import math
-from typing import Dict, Optional, Sequence
+from typing import Callable, Dict, Optional, Sequence
 
 import numpy as np
 
@@ -269,13 +269,21 @@ def _split_heads(qkv: np.ndarray, heads: int, head_dim: int):
 def dit_block_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], grid,
                   heads: int, head_dim: int, rope_split: Sequence[int],
                   rope_theta: float = 10000.0, eps: float = 1e-6,
-                  emulate_bf16_storage: bool = False) -> Dict[str, np.ndarray]:
+                  emulate_bf16_storage: bool = False,
+                  linear_quant: Optional[Callable] = None) -> Dict[str, np.ndarray]:
     """One block over the whole packed sequence; returns every intermediate.
 
     With emulate_bf16_storage, every intermediate that the device path stores
     between kernels is rounded to bf16 (h, qkv, q/k after norm + RoPE, o, x1,
     h2, a, x2) and mod to float32; all arithmetic in between stays float64.
     This models the storage precision of the path, not its exact value.
+
+    linear_quant (e.g. mx_linear.mx_fake_quant) replaces every operand of
+    the four block linears by its quantised value: the weights, and the
+    activations h, o, h2, a where they enter a linear. h, h2 and a are
+    quantised from their unrounded values (the producing kernels quantise
+    in registers), o from its stored value. The returned h, o, h2, a are the
+    values the linears consumed.
 
     h   = RMSNorm(x)(1+scale1)+shift1
     qkv = h W_qkv^T                   (q | k | v, each head-major [H*D])
@@ -287,6 +295,9 @@ def dit_block_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], gr
     x2  = x1 + gate2 * (a W_down^T)
     """
     st = bf16_round if emulate_bf16_storage else _identity
+    lq = linear_quant
+    act = (lambda z: lq(z)) if lq else st          # activation entering a linear
+    wt = (lambda nm: lq(_f64(weights[nm]))) if lq else (lambda nm: _f64(weights[nm]))
     x = _f64(x)
     n, c = x.shape
     seg = segment_ids(cu)
@@ -294,17 +305,19 @@ def dit_block_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], gr
     if emulate_bf16_storage:
         mod = mod.astype(np.float32).astype(_F)
     m = split_modulation(mod, c)
-    h = st(adaln_modulate_ref(x, m["shift1"], m["scale1"], seg, eps))
-    qkv = st(h @ _f64(weights["w_qkv"]).T)
+    h = act(adaln_modulate_ref(x, m["shift1"], m["scale1"], seg, eps))
+    qkv = st(h @ wt("w_qkv").T)
     q, k, v = _split_heads(qkv, heads, head_dim)
     qr, kr = qk_norm_rope_ref(q, k, weights["q_norm"], weights["k_norm"], grid, rope_split,
                               rope_theta, eps)
     qr, kr = st(qr), st(kr)
     o = st(attn_varlen_ref(qr, kr, v, cu).reshape(n, c))
-    x1 = st(gated_residual_ref(x, m["gate1"], o @ _f64(weights["w_o"]).T, seg))
-    h2 = st(adaln_modulate_ref(x1, m["shift2"], m["scale2"], seg, eps))
-    a = st(swiglu_ref(h2, weights["w_gate"], weights["w_up"]))
-    x2 = st(gated_residual_ref(x1, m["gate2"], a @ _f64(weights["w_down"]).T, seg))
+    if lq:
+        o = lq(o)
+    x1 = st(gated_residual_ref(x, m["gate1"], o @ wt("w_o").T, seg))
+    h2 = act(adaln_modulate_ref(x1, m["shift2"], m["scale2"], seg, eps))
+    a = act(swiglu_ref(h2, wt("w_gate"), wt("w_up")))
+    x2 = st(gated_residual_ref(x1, m["gate2"], a @ wt("w_down").T, seg))
     return {"mod": mod, "h": h, "qkv": qkv, "q": qr.reshape(n, c), "k": kr.reshape(n, c),
             "v": v.reshape(n, c), "o": o, "x1": x1, "h2": h2, "a": a, "x2": x2}
 
@@ -313,9 +326,11 @@ def dit_block_rows_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int
                        heads: int, head_dim: int, rope_split: Sequence[int], rows,
                        rope_theta: float = 10000.0, eps: float = 1e-6,
                        token_chunk: int = 4096,
-                       emulate_bf16_storage: bool = False) -> Dict[str, np.ndarray]:
+                       emulate_bf16_storage: bool = False,
+                       linear_quant: Optional[Callable] = None) -> Dict[str, np.ndarray]:
     """The same block for the sampled token indices `rows` only (exact, or
-    with the storage emulation of dit_block_ref).
+    with the storage emulation and linear quantisation of dit_block_ref;
+    both quantisations act along K, per row, so sampling rows is exact).
 
     Keys and values of every token of the segments that hold a sampled row
     are computed (a sampled row attends to its whole segment); everything
@@ -323,6 +338,9 @@ def dit_block_rows_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int
     leading rows. Memory is bounded by processing tokens in chunks.
     """
     st = bf16_round if emulate_bf16_storage else _identity
+    lq = linear_quant
+    act = (lambda z: lq(z)) if lq else st
+    wt = (lambda w: lq(w)) if lq else (lambda w: w)
     cu = check_cu_seqlens(cu)
     x32 = np.asarray(x)
     n, c = x32.shape
@@ -333,12 +351,12 @@ def dit_block_rows_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int
     if emulate_bf16_storage:
         mod = mod.astype(np.float32).astype(_F)
     m = split_modulation(mod, c)
-    w_qkv = _f64(weights["w_qkv"])
+    w_qkv = wt(_f64(weights["w_qkv"]))
     w_q, w_k, w_v = w_qkv[0:c], w_qkv[c:2 * c], w_qkv[2 * c:3 * c]
     wq_t, wk_t, wv_t = w_q.T.copy(), w_k.T.copy(), w_v.T.copy()
 
     def project(tok):
-        return st(adaln_modulate_ref(x32[tok], m["shift1"], m["scale1"], seg[tok], eps))
+        return act(adaln_modulate_ref(x32[tok], m["shift1"], m["scale1"], seg[tok], eps))
 
     out_o = np.zeros((rows.size, heads, head_dim), dtype=_F)
     for s in np.unique(seg[rows]) if rows.size else []:
@@ -366,14 +384,16 @@ def dit_block_rows_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int
         out_o[sel] = attn_varlen_ref(q_full, kk, vv, local_cu, rows=tok - a)
 
     o = st(out_o.reshape(rows.size, c))
+    if lq:
+        o = lq(o)
     segr = seg[rows]
     xr = _f64(x32[rows])
-    h = st(adaln_modulate_ref(xr, m["shift1"], m["scale1"], segr, eps))
-    x1 = st(gated_residual_ref(xr, m["gate1"], o @ _f64(weights["w_o"]).T, segr))
-    h2 = st(adaln_modulate_ref(x1, m["shift2"], m["scale2"], segr, eps))
-    act = st(swiglu_ref(h2, weights["w_gate"], weights["w_up"]))
-    x2 = st(gated_residual_ref(x1, m["gate2"], act @ _f64(weights["w_down"]).T, segr))
-    return {"mod": mod, "h": h, "o": o, "x1": x1, "h2": h2, "a": act, "x2": x2}
+    h = act(adaln_modulate_ref(xr, m["shift1"], m["scale1"], segr, eps))
+    x1 = st(gated_residual_ref(xr, m["gate1"], o @ wt(_f64(weights["w_o"])).T, segr))
+    h2 = act(adaln_modulate_ref(x1, m["shift2"], m["scale2"], segr, eps))
+    a = act(swiglu_ref(h2, wt(_f64(weights["w_gate"])), wt(_f64(weights["w_up"]))))
+    x2 = st(gated_residual_ref(x1, m["gate2"], a @ wt(_f64(weights["w_down"])).T, segr))
+    return {"mod": mod, "h": h, "o": o, "x1": x1, "h2": h2, "a": a, "x2": x2}
 
 
 def rel_frobenius(got, ref) -> float:
