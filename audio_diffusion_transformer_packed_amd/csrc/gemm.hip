@@ -33,6 +33,28 @@
 //  * workgroup ids are remapped so each XCD (ids are dealt round-robin over
 //    the 8 XCDs) gets a contiguous run of tiles, grouped 4 row-panels at a
 //    time, so concurrently running tiles share A and W panels in that XCD's L2.
+//
+// MXFP8 operands (the same kernel with MX = true; "MiniMax H3 on Ascend
+// 950PR / 950DT", section "Recommended lossy configuration": the transformer
+// runs with MXFP8 online quantization; the format follows the OCP MX v1.0
+// specification): a and W hold E4M3 codes, row-major [rows, K], with one
+// E8M0 scale per 32 consecutive K elements of a row, stored K-step-major:
+// the scale of row r, block j at byte ((j / 4) rows_total + r) 4 + j % 4, so
+// the four scales of a row for one 128-element K step are one aligned dword
+// and 32 consecutive rows' dwords are 128 contiguous bytes. A K step is 128
+// elements (128 bytes per row, the same LDS tiles and DMA as bf16's 64) and
+// runs v_mfma_scale_f32_32x32x64_f8f6f4, which applies the scales inside the
+// matrix core. Its operand layout (measured): lane (l, g) (l = lane % 32,
+// g = lane / 32) holds 32 bytes of row l; the first 16 bytes of lanes (l, 0)
+// and (l, 1) form one 32-element scale block, scaled by the byte selected in
+// lane (l, 0)'s scale register, and their last 16 bytes the second block,
+// scaled from lane (l, 1). So lane (l, g) reads K elements 16 g + [0, 16)
+// and 32 + 16 g + [0, 16) of each 64-element chunk, and its scale register is
+// the row's K-step dword shifted right by 8 g, so that byte 2c holds block
+// 2c + g of chunk c. The SwiGLU epilogue then writes its output as MXFP8
+// (codes and scales in the same layouts), ready for the down projection.
+#include <type_traits>
+
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -41,13 +63,13 @@ namespace {
 
 constexpr int kBM = 256;          // activation rows per tile
 constexpr int kBN = 256;          // W rows per tile (output columns, or gate+up pairs)
-constexpr int kBK = 64;
+constexpr int kStepBytes = 128;   // bytes of a row per K step (64 bf16 or 128 fp8)
 constexpr int kWaves = 8;         // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWN = 2;            // 32-row W blocks per wave (64 output columns, or one gate+up pair)
 constexpr int kWM = 4;            // 32-row activation blocks per wave (128 rows)
 constexpr int kDmaPerWave = kBM / 8 / kWaves;   // 1 KB DMA instructions per wave and operand
-constexpr int kTileBytes = kBM * kBK * 2;      // 32 KB per operand tile
+constexpr int kTileBytes = kBM * kStepBytes;   // 32 KB per operand tile
 constexpr int kStageBytes = 2 * kTileBytes;    // W tile then activation tile
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
@@ -65,6 +87,45 @@ __device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
         16, voff, soff, 0, 0);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 4 bytes per lane from buffer offset voff + soff into LDS at lds_dst + 4 i.
+__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int soff,
+                                         void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_dst)),
+        4, voff, soff, 0, 0);
+}
+
+// Scaled fp8 MFMA; OP selects the byte of each lane's scale register.
+template <int OP>
+__device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OP, sa, OP, sb);
+}
+
+__device__ __forceinline__ i32x8 cat16(uint4 x, uint4 y) {
+    return i32x8{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w),
+                 static_cast<int>(y.x), static_cast<int>(y.y), static_cast<int>(y.z), static_cast<int>(y.w)};
+}
+
+struct GemmArgs {
+    const void* a;            // [M, K] bf16, or E4M3 codes
+    const void* w;            // [N, K]
+    const void* w2;           // [N, K] up matrix (SwiGLU)
+    const uint8_t* a_sc;      // MX scales of a, w, w2 (K-step-major)
+    const uint8_t* w_sc;
+    const uint8_t* w2_sc;
+    void* y;                  // [M, N] bf16, or E4M3 codes (SwiGLU with MX)
+    uint8_t* y_sc;            // MX scales of y (SwiGLU with MX)
+    int64_t M, N, K;
+    const uint16_t* res;      // gated residual
+    const float* gate;
+    int64_t gate_stride;
+    const int32_t* cu;
+    int num_seqs;
+    int mtiles, ntiles;
+};
+
 // Tile id -> (row panel, column panel), XCD-aware and grouped.
 __device__ __forceinline__ void tile_coords(int bid, int nblocks, int mt, int nt, int& tm, int& tn) {
     // contiguous run per XCD (block b runs on XCD b % 8); XCD x owns
@@ -80,16 +141,24 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int mt, int nt
     tn = w / gm;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-    const uint16_t* __restrict__ W2, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
-    const uint16_t* __restrict__ res, const float* __restrict__ gate, int64_t gate_stride,
-    const int32_t* __restrict__ cu, int num_seqs, int mtiles, int ntiles) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+template <int EPI, bool MX>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * (kStageBytes + (MX ? 2048 : 0))];
+    const char* __restrict__ A = static_cast<const char*>(p.a);
+    const char* __restrict__ W = static_cast<const char*>(p.w);
+    const char* __restrict__ W2 = static_cast<const char*>(p.w2);
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const uint16_t* __restrict__ res = p.res;
+    const float* __restrict__ gate = p.gate;
+    const int64_t gate_stride = p.gate_stride;
+    const int32_t* __restrict__ cu = p.cu;
+    const int num_seqs = p.num_seqs, mtiles = p.mtiles, ntiles = p.ntiles;
+    uint16_t* __restrict__ Y = static_cast<uint16_t*>(p.y);
+    constexpr int kElem = MX ? 1 : 2;                  // bytes per operand element
+    const int64_t row_bytes = K * kElem;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
@@ -112,40 +181,82 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const int rl = lane >> 3;
     const int64_t a_rows = min<int64_t>(kBM, M - m0);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(A + m0 * K), 0, static_cast<int>(a_rows * K * 2), kBufferWord3);
+        const_cast<char*>(A + m0 * row_bytes), 0, static_cast<int>(a_rows * row_bytes), kBufferWord3);
     constexpr int W_ROWS = EPI == kEpiSwiGLU ? kBN / 2 : kBN;   // W rows per operand matrix
     const int64_t w_rows = min<int64_t>(W_ROWS, N - n0);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(W + n0 * K), 0, static_cast<int>(w_rows * K * 2), kBufferWord3);
+        const_cast<char*>(W + n0 * row_bytes), 0, static_cast<int>(w_rows * row_bytes), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>((EPI == kEpiSwiGLU ? W2 : W) + n0 * K), 0,
-        static_cast<int>(w_rows * K * 2), kBufferWord3);
+        const_cast<char*>((EPI == kEpiSwiGLU ? W2 : W) + n0 * row_bytes), 0,
+        static_cast<int>(w_rows * row_bytes), kBufferWord3);
     uint32_t aoff[kDmaPerWave], woff[kDmaPerWave];
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
         const int r = 8 * kDmaPerWave * wave + 8 * i + rl;     // tile row
         const int chunk = (lane & 7) ^ ((r >> 1) & 7);
-        aoff[i] = static_cast<uint32_t>((r * K + 8 * chunk) * 2);
+        aoff[i] = static_cast<uint32_t>(r * row_bytes + 16 * chunk);
         if (EPI == kEpiSwiGLU) {
             // W-tile row r = 128 wnp + 32 bj + j: bj even -> gate (W), odd -> up
             // (W2), for output column n0 + 64 wnp + 32 (bj / 2) + j; a wave's
             // rows share one bj (r / 32 = wave), so the matrix is wave-uniform
             const int wnp = r >> 7, bj = (r >> 5) & 3, j = r & 31;
-            woff[i] = static_cast<uint32_t>(((64 * wnp + 32 * (bj >> 1) + j) * K + 8 * chunk) * 2);
+            woff[i] = static_cast<uint32_t>((64 * wnp + 32 * (bj >> 1) + j) * row_bytes + 16 * chunk);
         } else {
-            woff[i] = static_cast<uint32_t>((r * K + 8 * chunk) * 2);
+            woff[i] = static_cast<uint32_t>(r * row_bytes + 16 * chunk);
         }
     }
 
-    auto issue = [&](int stage, int64_t k0) __attribute__((always_inline)) {
-        char* base = smem + stage * kStageBytes;
-        const int kb = static_cast<int>(k0 * 2);
-        const bool up = EPI == kEpiSwiGLU && (wave & 1);
+    // MX scales ride with the tiles: per K step the 256 activation rows'
+    // dwords (1 KB, contiguous in the K-step-major layout) and the 256 W
+    // rows' dwords (for SwiGLU 128 gate rows then 128 up rows) are DMA'd
+    // into 2 KB after the two tiles of the stage, by waves 0 and 1. Scale
+    // rows past the matrix read past-the-end zeros or the next K step's
+    // first rows; their data rows load as zeros and are never stored.
+    const int64_t ks_total = row_bytes / kStepBytes;
+    const int sa_bytes = MX ? static_cast<int>((ks_total * M - m0) * 4) : 0;
+    const int sw_bytes = MX ? static_cast<int>((ks_total * N - n0) * 4) : 0;
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.a_sc) + (MX ? m0 * 4 : 0), 0, sa_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsw1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.w_sc) + (MX ? n0 * 4 : 0), 0, sw_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsw2 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(EPI == kEpiSwiGLU ? p.w2_sc : p.w_sc) + (MX ? n0 * 4 : 0), 0, sw_bytes,
+        kBufferWord3);
+    constexpr int kScaleBytes = MX ? 2048 : 0;
+    constexpr int kStage = kStageBytes + kScaleBytes;
+
+    // per-wave constant sources (selected once, so they stay in scalar registers)
+    const bool up = EPI == kEpiSwiGLU && (wave & 1);
+    const __amdgpu_buffer_rsrc_t rwx = up ? rw2 : rw;
+    // MX scales: every wave moves 256 B per K step (4 per lane, no branch):
+    // waves 0-3 the W rows' dwords (SwiGLU: waves 0-1 gate rows, 2-3 up
+    // rows), waves 4-7 the activation rows'
+    const bool wpart = wave < 4;
+    const __amdgpu_buffer_rsrc_t rsx = wpart ? ((EPI == kEpiSwiGLU && wave >= 2) ? rsw2 : rsw1) : rsa;
+    const uint32_t sc_voff = 4 * (64 * (EPI == kEpiSwiGLU && wpart ? (wave & 1) : (wave & 3)) + lane);
+    const int64_t sc_rows = wpart ? N : M;
+
+    auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
+        char* base = smem + stage * kStage;
+        const int kb = static_cast<int>(kt * kStepBytes);
 #pragma unroll
         for (int i = 0; i < kDmaPerWave; ++i) {
-            buf_dma16(up ? rw2 : rw, woff[i], kb, base + (kDmaPerWave * wave + i) * 1024);
+            buf_dma16(rwx, woff[i], kb, base + (kDmaPerWave * wave + i) * 1024);
             buf_dma16(ra, aoff[i], kb, base + kTileBytes + (kDmaPerWave * wave + i) * 1024);
         }
+        if constexpr (MX)
+            buf_dma4(rsx, sc_voff, static_cast<int>(kt * sc_rows * 4), base + kStageBytes + 256 * wave);
+    };
+    // this lane's scale dwords in a stage (shifted by 8 g, see the header)
+    uint32_t asc[kWM], wsc[kWN];
+    auto take_scales = [&](int stage) __attribute__((always_inline)) {
+        const uint32_t* sw = reinterpret_cast<const uint32_t*>(smem + stage * kStage + kStageBytes);
+        const uint32_t* sa = sw + 256;
+#pragma unroll
+        for (int b = 0; b < kWM; ++b) asc[b] = sa[128 * wm + 32 * b + l32] >> (8 * g);
+#pragma unroll
+        for (int b = 0; b < kWN; ++b)
+            wsc[b] = sw[EPI == kEpiSwiGLU ? 128 * b + 32 * wn + l32 : 64 * wn + 32 * b + l32] >> (8 * g);
     };
 
     f32x16 acc[kWN][kWM];
@@ -160,27 +271,58 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const int wrow0 = (64 * wn + l32) * 128;
     const int arow0 = (128 * wm + l32) * 128;
 
-    const int64_t ksteps = K / kBK;
+    const int64_t ksteps = ks_total;
     issue(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int64_t kt = 0; kt < ksteps; ++kt) {
         const int stage = static_cast<int>(kt & 1);
-        if (kt + 1 < ksteps) issue(stage ^ 1, (kt + 1) * kBK);
-        const char* wt = smem + stage * kStageBytes;
+        if (MX) take_scales(stage);
+        if (kt + 1 < ksteps) issue(stage ^ 1, kt + 1);
+        const char* wt = smem + stage * kStage;
         const char* at = wt + kTileBytes;
+        if constexpr (MX) {
+            // two 64-element chunks c: lane reads 16-byte chunks 4c + g and
+            // 4c + 2 + g. The fragments are read as bf16x8 (reinterpreted as
+            // fp8 bytes): read as uint4 the compiler could not tell them from
+            // the in-flight DMA's LDS writes and waited for the DMA first.
 #pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            const int off = 16 * ((2 * ks + g) ^ rsw);
-            bf16x8 wf[kWN], af[kWM];
+            for (int c = 0; c < 2; ++c) {
+                const int o0 = 16 * ((4 * c + g) ^ rsw), o1 = 16 * ((4 * c + 2 + g) ^ rsw);
+                bf16x8 w0[kWN], w1[kWN], a0[kWM], a1[kWM];
 #pragma unroll
-            for (int b = 0; b < kWN; ++b) wf[b] = *reinterpret_cast<const bf16x8*>(wt + wrow0 + b * 32 * 128 + off);
+                for (int b = 0; b < kWN; ++b) w0[b] = *reinterpret_cast<const bf16x8*>(wt + wrow0 + b * 32 * 128 + o0);
 #pragma unroll
-            for (int b = 0; b < kWM; ++b) af[b] = *reinterpret_cast<const bf16x8*>(at + arow0 + b * 32 * 128 + off);
+                for (int b = 0; b < kWN; ++b) w1[b] = *reinterpret_cast<const bf16x8*>(wt + wrow0 + b * 32 * 128 + o1);
 #pragma unroll
-            for (int bi = 0; bi < kWN; ++bi)
+                for (int b = 0; b < kWM; ++b) a0[b] = *reinterpret_cast<const bf16x8*>(at + arow0 + b * 32 * 128 + o0);
 #pragma unroll
-                for (int bj = 0; bj < kWM; ++bj) acc[bi][bj] = mfma32x32x16(wf[bi], af[bj], acc[bi][bj]);
+                for (int b = 0; b < kWM; ++b) a1[b] = *reinterpret_cast<const bf16x8*>(at + arow0 + b * 32 * 128 + o1);
+#pragma unroll
+                for (int bi = 0; bi < kWN; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < kWM; ++bj) {
+                        const i32x8 wa = cat16(__builtin_bit_cast(uint4, w0[bi]), __builtin_bit_cast(uint4, w1[bi]));
+                        const i32x8 aa = cat16(__builtin_bit_cast(uint4, a0[bj]), __builtin_bit_cast(uint4, a1[bj]));
+                        const int sw = static_cast<int>(wsc[bi]), sa = static_cast<int>(asc[bj]);
+                        acc[bi][bj] = c == 0 ? mfma_mx<0>(wa, aa, acc[bi][bj], sw, sa)
+                                             : mfma_mx<2>(wa, aa, acc[bi][bj], sw, sa);
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = 16 * ((2 * ks + g) ^ rsw);
+                bf16x8 wf[kWN], af[kWM];
+#pragma unroll
+                for (int b = 0; b < kWN; ++b) wf[b] = *reinterpret_cast<const bf16x8*>(wt + wrow0 + b * 32 * 128 + off);
+#pragma unroll
+                for (int b = 0; b < kWM; ++b) af[b] = *reinterpret_cast<const bf16x8*>(at + arow0 + b * 32 * 128 + off);
+#pragma unroll
+                for (int bi = 0; bi < kWN; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < kWM; ++bj) acc[bi][bj] = mfma32x32x16(wf[bi], af[bj], acc[bi][bj]);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -196,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     // 128 (64) bytes together with 16-byte stores. The staging is
     // wave-local: only this wave's LDS accesses need ordering.
     char* ep = smem + wave * (2 * kStageBytes / kWaves);
-    const bool vec16 = ((reinterpret_cast<uintptr_t>(Y) | reinterpret_cast<uintptr_t>(res)) & 15) == 0;
+    const bool vec16 = ((reinterpret_cast<uintptr_t>(p.y) | reinterpret_cast<uintptr_t>(res)) & 15) == 0;
     auto lds_fence = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
     auto store8 = [&](uint16_t* dst, uint4 v) __attribute__((always_inline)) {
         if (vec16) {
@@ -230,6 +372,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             const int r = 8 * j + (lane >> 3);
             const uint4 v = *reinterpret_cast<const uint4*>(ep + r * 128 + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
             if (mw + r < M && n < N) store8(Y + (mw + r) * N + n, v);
+        }
+    } else if (EPI == kEpiSwiGLU && MX) {
+        // bi = 0 is the gate block, bi = 1 the up block of output columns
+        // n0 + 32 wn + [0, 32), exactly one MX block per row: fp32 staging
+        // (128 rows x 32 fp32 per wave), then 4 lanes per row take the
+        // block's amax, scale byte and E4M3 codes (8 per lane)
+#pragma unroll
+        for (int bj = 0; bj < kWM; ++bj) {
+            const int r = 32 * bj + l32;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float gv = acc[0][bj][4 * q + e];
+                    const float uv = acc[1][bj][4 * q + e];
+                    o[e] = gv / (1.0f + __expf(-gv)) * uv;
+                }
+                *reinterpret_cast<f32x4*>(ep + r * 128 + 16 * ((2 * q + g) ^ ((r >> 1) & 7))) = o;
+            }
+        }
+        lds_fence();
+        uint8_t* Y8 = static_cast<uint8_t*>(p.y);
+        const int64_t n = n0 + 32 * wn + 8 * (lane & 3);
+        const int64_t blk = (n0 + 32 * wn) >> 5;           // MX block of this wave's columns
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 16 * j + (lane >> 2);
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(ep + r * 128 + 16 * ((2 * (lane & 3)) ^ ((r >> 1) & 7)));
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(ep + r * 128 + 16 * ((2 * (lane & 3) + 1) ^ ((r >> 1) & 7)));
+            float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            float am = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+            am = fmaxf(am, __shfl_xor(am, 1, 64));
+            am = fmaxf(am, __shfl_xor(am, 2, 64));
+            const uint32_t sb = mx_scale_byte(am);
+            const float inv = mx_inv_scale(sb);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] *= inv;
+            const uint2 codes = mx_codes8(v);
+            const int64_t m = mw + r;
+            if (m < M && n < N) {
+                *reinterpret_cast<uint2*>(Y8 + m * N + n) = codes;
+                if ((lane & 3) == 0) p.y_sc[((blk >> 2) * M + m) * 4 + (blk & 3)] = static_cast<uint8_t>(sb);
+            }
         }
     } else if (EPI == kEpiSwiGLU) {
         // bi = 0 is the gate block, bi = 1 the up block of output columns
@@ -321,32 +509,51 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     }
 }
 
+template <bool MX>
+hipError_t launch_gemm_args(int epilogue, GemmArgs& p, hipStream_t stream) {
+    if (p.M == 0) return hipSuccess;
+    const int out_n = epilogue == kEpiSwiGLU ? kBN / 2 : kBN;
+    p.mtiles = static_cast<int>((p.M + kBM - 1) / kBM);
+    p.ntiles = static_cast<int>((p.N + out_n - 1) / out_n);
+    const dim3 grid(static_cast<unsigned>(p.mtiles * p.ntiles));
+    switch (epilogue) {
+        case kEpiStore:
+            hipLaunchKernelGGL((gemm_kernel<kEpiStore, MX>), grid, dim3(kThreads), 0, stream, p);
+            break;
+        case kEpiSwiGLU:
+            hipLaunchKernelGGL((gemm_kernel<kEpiSwiGLU, MX>), grid, dim3(kThreads), 0, stream, p);
+            break;
+        default:
+            hipLaunchKernelGGL((gemm_kernel<kEpiGatedResidual, MX>), grid, dim3(kThreads), 0, stream, p);
+            break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int epilogue, const uint16_t* a, const uint16_t* w, const uint16_t* w2,
                        uint16_t* y, int64_t m, int64_t n, int64_t k, const uint16_t* res,
                        const float* gate, int64_t gate_stride, const int32_t* cu,
                        int num_seqs, hipStream_t stream) {
-    if (m == 0) return hipSuccess;
-    const int out_n = epilogue == kEpiSwiGLU ? kBN / 2 : kBN;
-    const int mt = static_cast<int>((m + kBM - 1) / kBM);
-    const int nt = static_cast<int>((n + out_n - 1) / out_n);
-    const dim3 grid(static_cast<unsigned>(mt * nt));
-    switch (epilogue) {
-        case kEpiStore:
-            hipLaunchKernelGGL(gemm_kernel<kEpiStore>, grid, dim3(kThreads), 0, stream, a, w, w2,
-                               y, m, n, k, res, gate, gate_stride, cu, num_seqs, mt, nt);
-            break;
-        case kEpiSwiGLU:
-            hipLaunchKernelGGL(gemm_kernel<kEpiSwiGLU>, grid, dim3(kThreads), 0, stream, a, w, w2,
-                               y, m, n, k, res, gate, gate_stride, cu, num_seqs, mt, nt);
-            break;
-        default:
-            hipLaunchKernelGGL(gemm_kernel<kEpiGatedResidual>, grid, dim3(kThreads), 0, stream, a,
-                               w, w2, y, m, n, k, res, gate, gate_stride, cu, num_seqs, mt, nt);
-            break;
-    }
-    return hipGetLastError();
+    GemmArgs p{};
+    p.a = a; p.w = w; p.w2 = w2; p.y = y;
+    p.M = m; p.N = n; p.K = k;
+    p.res = res; p.gate = gate; p.gate_stride = gate_stride; p.cu = cu; p.num_seqs = num_seqs;
+    return launch_gemm_args<false>(epilogue, p, stream);
+}
+
+hipError_t launch_gemm_mx(int epilogue, const uint8_t* a, const uint8_t* a_sc, const uint8_t* w,
+                          const uint8_t* w_sc, const uint8_t* w2, const uint8_t* w2_sc, void* y,
+                          uint8_t* y_sc, int64_t m, int64_t n, int64_t k, const uint16_t* res,
+                          const float* gate, int64_t gate_stride, const int32_t* cu, int num_seqs,
+                          hipStream_t stream) {
+    GemmArgs p{};
+    p.a = a; p.a_sc = a_sc; p.w = w; p.w_sc = w_sc; p.w2 = w2; p.w2_sc = w2_sc;
+    p.y = y; p.y_sc = y_sc;
+    p.M = m; p.N = n; p.K = k;
+    p.res = res; p.gate = gate; p.gate_stride = gate_stride; p.cu = cu; p.num_seqs = num_seqs;
+    return launch_gemm_args<true>(epilogue, p, stream);
 }
 
 }  // namespace h3

@@ -86,4 +86,35 @@ __device__ __forceinline__ int find_segment(const int32_t* __restrict__ cu, int 
     return lo;
 }
 
+
+// ---- MXFP8 (OCP MX v1.0: 32-element blocks, E8M0 scale, E4M3 elements) ----
+// E8M0 byte of a block's scale 2^(floor(log2 amax) - 8) from its fp32 amax,
+// never below 2^-127: the exponent field minus 8, clamped at 0 (zero and
+// fp32-subnormal amax give byte 0).
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+    const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xff);
+    return static_cast<uint32_t>(max(e - 8, 0));
+}
+// 1 / scale for that byte, 2^(127 - byte), built from its bits.
+__device__ __forceinline__ float mx_inv_scale(uint32_t byte) {
+    return __uint_as_float((254u - byte) << 23);
+}
+// E4M3 codes (byte i = value i) of eight values already divided by the
+// scale: saturated to +-448, then round to nearest even.
+__device__ __forceinline__ uint2 mx_codes8(const float (&v)[8]) {
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(v[i], -448.0f), 448.0f);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], w1, true);
+    return make_uint2(static_cast<uint32_t>(w0), static_cast<uint32_t>(w1));
+}
+// Byte offset of the scale of row r, block j in the K-step-major layout
+// (the four scales of a row for one 128-element K step form one dword).
+__device__ __forceinline__ int64_t mx_scale_offset(int64_t r, int64_t j, int64_t rows) {
+    return ((j >> 2) * rows + r) * 4 + (j & 3);
+}
+
 }  // namespace h3

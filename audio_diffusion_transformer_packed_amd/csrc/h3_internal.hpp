@@ -61,5 +61,15 @@ hipError_t launch_gemm(int epilogue, const uint16_t* a, const uint16_t* w, const
                        uint16_t* y, int64_t m, int64_t n, int64_t k, const uint16_t* res,
                        const float* gate, int64_t gate_stride, const int32_t* cu,
                        int num_seqs, hipStream_t stream);
+// MXFP8 operands: E4M3 codes row-major [rows, k], E8M0 scales K-step-major
+// (row r, block j at byte ((j / 4) rows + r) 4 + j % 4); y is bf16, or MXFP8
+// (codes + y_sc) for the SwiGLU epilogue. k % 128 == 0.
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t ld, int64_t rows, int64_t k, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream);
+hipError_t launch_gemm_mx(int epilogue, const uint8_t* a, const uint8_t* a_sc, const uint8_t* w,
+                          const uint8_t* w_sc, const uint8_t* w2, const uint8_t* w2_sc, void* y,
+                          uint8_t* y_sc, int64_t m, int64_t n, int64_t k, const uint16_t* res,
+                          const float* gate, int64_t gate_stride, const int32_t* cu, int num_seqs,
+                          hipStream_t stream);
 
 }  // namespace h3

@@ -507,6 +507,119 @@ H3_API h3_status h3_linear_gated_residual_bf16(const void* a, const void* w, con
     return ok();
 }
 
+H3_API h3_status h3_mx_quantize_bf16(const void* x, int64_t x_row_stride, int64_t rows, int64_t k,
+                                     void* codes, void* scales, void* hip_stream) {
+    if (rows < 0 || k <= 0) return fail(H3_ERR_INVALID_ARGUMENT, "rows=%lld k=%lld", (long long)rows, (long long)k);
+    if (k % 128) return fail(H3_ERR_UNSUPPORTED, "k=%lld must be a multiple of 128", (long long)k);
+    if (x_row_stride < k || x_row_stride % 8)
+        return fail(H3_ERR_INVALID_ARGUMENT, "x_row_stride must be >= k and a multiple of 8");
+    if (rows == 0) return ok();
+    if (rows > (static_cast<int64_t>(1) << 40) / k) return fail(H3_ERR_UNSUPPORTED, "rows * k too large");
+    if (!x || !codes || !scales) return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes)) & 15 ||
+        reinterpret_cast<uintptr_t>(scales) & 3)
+        return fail(H3_ERR_UNSUPPORTED, "x and codes must be 16-byte, scales 4-byte aligned");
+    hipError_t e = h3::launch_mx_quantize(static_cast<const uint16_t*>(x), x_row_stride, rows, k,
+                                          static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                                          static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "mx quantize launch");
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// MX GEMM operands: k a multiple of 128, codes 16-byte and scales 4-byte
+// aligned, and every scale array's byte count within a signed 32-bit range
+// (the kernel addresses it with 32-bit buffer offsets).
+h3_status check_mx_gemm(int64_t m, int64_t n, int64_t k, int64_t n_mult) {
+    h3_status st = check_gemm_shape(m, n, k, n_mult);
+    if (st != H3_OK) return st;
+    if (k % 128) return fail(H3_ERR_UNSUPPORTED, "k=%lld must be a multiple of 128 (MX)", (long long)k);
+    if (std::max(m, n) > INT32_MAX / (k / 32))
+        return fail(H3_ERR_UNSUPPORTED, "m or n times k/32 exceeds 2^31 (MX scale arrays)");
+    return ok();
+}
+
+bool mx_aligned(const void* codes, const void* scales) {
+    return !((reinterpret_cast<uintptr_t>(codes) & 15) || (reinterpret_cast<uintptr_t>(scales) & 3));
+}
+
+}  // namespace
+
+extern "C" {
+
+H3_API h3_status h3_linear_mxfp8(const void* a, const void* a_scales, const void* w,
+                                 const void* w_scales, void* y, int64_t m, int64_t n, int64_t k,
+                                 void* hip_stream) {
+    h3_status st = check_mx_gemm(m, n, k, 8);
+    if (st != H3_OK) return st;
+    if (m == 0) return ok();
+    if (!a || !a_scales || !w || !w_scales || !y) return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!mx_aligned(a, a_scales) || !mx_aligned(w, w_scales) || reinterpret_cast<uintptr_t>(y) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "codes 16-byte, scales 4-byte and y 8-byte aligned");
+    hipError_t e = h3::launch_gemm_mx(h3::kEpiStore, static_cast<const uint8_t*>(a),
+                                      static_cast<const uint8_t*>(a_scales), static_cast<const uint8_t*>(w),
+                                      static_cast<const uint8_t*>(w_scales), nullptr, nullptr, y, nullptr,
+                                      m, n, k, nullptr, nullptr, 0, nullptr, 1,
+                                      static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "mx gemm launch");
+    return ok();
+}
+
+H3_API h3_status h3_linear_swiglu_mxfp8(const void* a, const void* a_scales, const void* w_gate,
+                                        const void* w_gate_scales, const void* w_up,
+                                        const void* w_up_scales, void* y, void* y_scales, int64_t m,
+                                        int64_t n, int64_t k, void* hip_stream) {
+    h3_status st = check_mx_gemm(m, n, k, 128);
+    if (st != H3_OK) return st;
+    if (m == 0) return ok();
+    if (!a || !a_scales || !w_gate || !w_gate_scales || !w_up || !w_up_scales || !y || !y_scales)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (m > INT32_MAX / (n / 32)) return fail(H3_ERR_UNSUPPORTED, "m * n / 32 exceeds 2^31");
+    if (!mx_aligned(a, a_scales) || !mx_aligned(w_gate, w_gate_scales) || !mx_aligned(w_up, w_up_scales) ||
+        !mx_aligned(y, y_scales))
+        return fail(H3_ERR_UNSUPPORTED, "codes 16-byte and scales 4-byte aligned");
+    hipError_t e = h3::launch_gemm_mx(h3::kEpiSwiGLU, static_cast<const uint8_t*>(a),
+                                      static_cast<const uint8_t*>(a_scales), static_cast<const uint8_t*>(w_gate),
+                                      static_cast<const uint8_t*>(w_gate_scales),
+                                      static_cast<const uint8_t*>(w_up), static_cast<const uint8_t*>(w_up_scales),
+                                      y, static_cast<uint8_t*>(y_scales), m, n, k, nullptr, nullptr, 0,
+                                      nullptr, 1, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "mx gemm launch");
+    return ok();
+}
+
+H3_API h3_status h3_linear_gated_residual_mxfp8(const void* a, const void* a_scales, const void* w,
+                                                const void* w_scales, const void* res,
+                                                const float* gate, int64_t gate_row_stride, void* y,
+                                                int64_t m, int64_t n, int64_t k,
+                                                const int32_t* cu_seqlens_dev,
+                                                const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                void* hip_stream) {
+    h3_status st = check_mx_gemm(m, n, k, 8);
+    if (st != H3_OK) return st;
+    if (m > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "m too large");
+    st = check_cu(cu_seqlens_host, num_seqs, static_cast<int32_t>(m));
+    if (st != H3_OK) return st;
+    if (m == 0) return ok();
+    if (!a || !a_scales || !w || !w_scales || !res || !gate || !y || !cu_seqlens_dev)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (gate_row_stride < n) return fail(H3_ERR_INVALID_ARGUMENT, "gate_row_stride < n");
+    if (gate_row_stride & 3) return fail(H3_ERR_UNSUPPORTED, "gate_row_stride must be a multiple of 4");
+    if (!mx_aligned(a, a_scales) || !mx_aligned(w, w_scales) || reinterpret_cast<uintptr_t>(gate) & 15 ||
+        (reinterpret_cast<uintptr_t>(res) | reinterpret_cast<uintptr_t>(y)) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "codes/gate 16-byte, scales 4-byte, res/y 8-byte aligned");
+    hipError_t e = h3::launch_gemm_mx(h3::kEpiGatedResidual, static_cast<const uint8_t*>(a),
+                                      static_cast<const uint8_t*>(a_scales), static_cast<const uint8_t*>(w),
+                                      static_cast<const uint8_t*>(w_scales), nullptr, nullptr, y, nullptr,
+                                      m, n, k, static_cast<const uint16_t*>(res), gate, gate_row_stride,
+                                      cu_seqlens_dev, num_seqs, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "mx gemm launch");
+    return ok();
+}
+
 }  // extern "C"
 
 namespace {

@@ -314,6 +314,103 @@ def linear_gated_residual(a: torch.Tensor, w: torch.Tensor, res: torch.Tensor,
 
 
 # --------------------------------------------------------------------------
+# MXFP8 (layouts in h3dit.h: codes [rows, k] uint8, scales K-step-major)
+# --------------------------------------------------------------------------
+
+class MX:
+    """An MXFP8 matrix: `codes` uint8 [rows, k] (E4M3) and `scales` uint8
+    [rows * k / 32] (E8M0, K-step-major)."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor):
+        if codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or codes.dim() != 2:
+            raise TypeError("MX codes must be uint8 [rows, k] and scales uint8")
+        rows, k = codes.shape
+        if k % 128 or scales.numel() != rows * k // 32 or not codes.is_contiguous():
+            raise ValueError("MX: k must be a multiple of 128, codes contiguous, scales rows*k/32 bytes")
+        self.codes, self.scales = codes, scales
+
+    @property
+    def shape(self):
+        return tuple(self.codes.shape)
+
+    @staticmethod
+    def empty(rows: int, k: int, device) -> "MX":
+        return MX(torch.empty((rows, k), dtype=torch.uint8, device=device),
+                  torch.empty(rows * k // 32, dtype=torch.uint8, device=device))
+
+
+def mx_quantize(x: torch.Tensor, out: Optional[MX] = None) -> MX:
+    """MXFP8 codes and scales of bf16 x [rows, k] (rows may be strided)."""
+    _need(x, "x", BF16)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [rows, k] with contiguous rows")
+    rows, k = x.shape
+    out = MX.empty(rows, k, x.device) if out is None else out
+    if out.shape != (rows, k):
+        raise ValueError("out has the wrong shape")
+    check(lib().h3_mx_quantize_bf16(_ptr(x), x.stride(0), rows, k, _ptr(out.codes), _ptr(out.scales),
+                                    _stream(x.device)))
+    return out
+
+
+def _mx_args(a: MX, ws) -> torch.device:
+    dev = a.codes.device
+    for t in [a] + list(ws):
+        if not isinstance(t, MX):
+            raise TypeError("MX operands expected")
+        if t.codes.device != dev:
+            raise ValueError("operands on different devices")
+        if t.shape[1] != a.shape[1]:
+            raise ValueError("operands must share k")
+    return dev
+
+
+def linear_mx(a: MX, w: MX) -> torch.Tensor:
+    """y = dq(a) dq(w)^T in bf16."""
+    dev = _mx_args(a, [w])
+    m, k = a.shape
+    n = w.shape[0]
+    y = torch.empty((m, n), dtype=BF16, device=dev)
+    check(lib().h3_linear_mxfp8(_ptr(a.codes), _ptr(a.scales), _ptr(w.codes), _ptr(w.scales), _ptr(y),
+                                m, n, k, _stream(dev)))
+    return y
+
+
+def linear_swiglu_mx(a: MX, w_gate: MX, w_up: MX, out: Optional[MX] = None) -> MX:
+    """MX(silu(dq(a) dq(w_gate)^T) * (dq(a) dq(w_up)^T))."""
+    dev = _mx_args(a, [w_gate, w_up])
+    m, k = a.shape
+    n = w_gate.shape[0]
+    if w_up.shape != w_gate.shape:
+        raise ValueError("w_gate and w_up must have the same shape")
+    y = MX.empty(m, n, dev) if out is None else out
+    check(lib().h3_linear_swiglu_mxfp8(_ptr(a.codes), _ptr(a.scales), _ptr(w_gate.codes),
+                                       _ptr(w_gate.scales), _ptr(w_up.codes), _ptr(w_up.scales),
+                                       _ptr(y.codes), _ptr(y.scales), m, n, k, _stream(dev)))
+    return y
+
+
+def linear_gated_residual_mx(a: MX, w: MX, res: torch.Tensor, gate: torch.Tensor,
+                             cu_seqlens: torch.Tensor, cu_host,
+                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dev = _mx_args(a, [w])
+    _need(res, "res", BF16, dev)
+    _need(gate, "gate", torch.float32, dev)
+    m, k = a.shape
+    n = w.shape[0]
+    if gate.stride(1) != 1:
+        raise ValueError("gate rows must be contiguous")
+    y = torch.empty((m, n), dtype=BF16, device=dev) if out is None else out
+    cu = _host_cu(cu_host)
+    check(lib().h3_linear_gated_residual_mxfp8(_ptr(a.codes), _ptr(a.scales), _ptr(w.codes),
+                                               _ptr(w.scales), _ptr(res.contiguous()), _ptr(gate),
+                                               gate.stride(0), _ptr(y), m, n, k, _ptr(cu_seqlens),
+                                               cu.ctypes.data_as(C.c_void_p), cu.size - 1,
+                                               _stream(dev)))
+    return y
+
+
+# --------------------------------------------------------------------------
 # The block
 # --------------------------------------------------------------------------
 

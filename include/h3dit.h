@@ -276,6 +276,57 @@ H3_API h3_status h3_linear_gated_residual_bf16(const void* a, const void* w, con
                                                int32_t num_seqs, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * MXFP8 linears ([H3-950PR] "Recommended lossy configuration": the
+ * transformer runs with MXFP8 online quantization; [FastH3-EN] "Scaling
+ * beyond the FastH3 profile", quantization-paths bullet: online FP8 for the
+ * linears). The pages do not give the format; this follows the public OCP
+ * Microscaling (MX) v1.0 specification, MXFP8 with E4M3 elements:
+ *   - blocks of 32 consecutive elements along k share one E8M0 scale
+ *     (byte e means 2^(e - 127)); the scale of a block is
+ *     2^(floor(log2 amax) - 8), never below 2^-127 (byte 0 for all-zero
+ *     blocks);
+ *   - elements are E4M3(x / scale), round to nearest even, saturating at
+ *     +-448; the value of an element is scale * code.
+ * An MX matrix [rows, k] is two buffers: codes, uint8 [rows, k] row-major,
+ * and scales in K-step-major order, the scale of row r and block j
+ * (elements 32j .. 32j+31) at byte ((j / 4) * rows + r) * 4 + j % 4
+ * (rows * k / 32 bytes; the four scales of a row for one 128-element K step
+ * form one aligned dword). k is a multiple of 128; codes are 16-byte and
+ * scales 4-byte aligned; rows * k / 32 < 2^31.
+ *
+ *   h3_mx_quantize_bf16: bf16 x [rows, k] (row stride x_row_stride elements,
+ *       >= k and a multiple of 8, x 16-byte aligned) -> MX codes + scales.
+ *       Exact: equal to the definition above for every bf16 input.
+ *   h3_linear_mxfp8: y = dq(a) . dq(W)^T, y bf16 [m, n] (8-byte aligned),
+ *       a MX [m, k], W MX [n, k]; n a multiple of 8. fp32 accumulation in
+ *       the matrix core, one bf16 rounding.
+ *   h3_linear_swiglu_mxfp8: y = MX(silu(dq(a) . dq(W_gate)^T) * (dq(a) .
+ *       dq(W_up)^T)): the product is quantised from fp32 (no bf16 step) into
+ *       MX codes y [m, n] and y_scales (rows = m); n a multiple of 128.
+ *   h3_linear_gated_residual_mxfp8: y = res + gate[seg(t)] * (dq(a) .
+ *       dq(W)^T), as h3_linear_gated_residual_bf16 (res, y bf16 8-byte
+ *       aligned; gate 16-byte aligned).
+ * Errors as for the bf16 linears; all buffers are the caller's, nothing is
+ * allocated and every launch goes on hip_stream.
+ * ---------------------------------------------------------------------- */
+H3_API h3_status h3_mx_quantize_bf16(const void* x, int64_t x_row_stride, int64_t rows, int64_t k,
+                                     void* codes, void* scales, void* hip_stream);
+H3_API h3_status h3_linear_mxfp8(const void* a, const void* a_scales, const void* w,
+                                 const void* w_scales, void* y, int64_t m, int64_t n, int64_t k,
+                                 void* hip_stream);
+H3_API h3_status h3_linear_swiglu_mxfp8(const void* a, const void* a_scales, const void* w_gate,
+                                        const void* w_gate_scales, const void* w_up,
+                                        const void* w_up_scales, void* y, void* y_scales, int64_t m,
+                                        int64_t n, int64_t k, void* hip_stream);
+H3_API h3_status h3_linear_gated_residual_mxfp8(const void* a, const void* a_scales, const void* w,
+                                                const void* w_scales, const void* res,
+                                                const float* gate, int64_t gate_row_stride, void* y,
+                                                int64_t m, int64_t n, int64_t k,
+                                                const int32_t* cu_seqlens_dev,
+                                                const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * One DiT block over the packed sequence (all of the above, in order):
  *   mod = cond W_mod^T                      -> shift1 scale1 gate1 shift2 scale2 gate2
  *   h   = RMSNorm(x)(1 + scale1) + shift1
