@@ -28,9 +28,11 @@ EXPORTS = (
     "h3_attn_varlen_workspace_size", "h3_attn_varlen_num_items", "h3_attn_varlen",
     "h3_fp8_num_tiles", "h3_fp8_quantize_workspace_size", "h3_fp8_quantize",
     "h3_qk_rmsnorm_rope", "h3_modulation", "h3_adaln_rmsnorm_modulate", "h3_linear_bf16",
-    "h3_linear_swiglu_bf16", "h3_linear_gated_residual_bf16", "h3_mx_quantize_bf16",
+    "h3_linear_swiglu_bf16", "h3_linear_gated_residual_bf16", "h3_adaln_rmsnorm_modulate_mxfp8",
+    "h3_mx_quantize_bf16",
     "h3_linear_mxfp8", "h3_linear_swiglu_mxfp8", "h3_linear_gated_residual_mxfp8",
-    "h3_dit_block_workspace_size", "h3_dit_block_forward",
+    "h3_dit_block_workspace_size", "h3_dit_block_forward", "h3_dit_block_mx_workspace_size",
+    "h3_dit_block_forward_mxfp8",
 )
 
 
@@ -49,6 +51,15 @@ class DitDims(C.Structure):
 class DitWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in
                 ("w_mod", "w_qkv", "w_o", "q_norm", "k_norm", "w_gate", "w_up", "w_down")]
+
+
+class MxMatrix(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p)]
+
+
+class DitMxWeights(C.Structure):
+    _fields_ = [("w_mod", C.c_void_p), ("q_norm", C.c_void_p), ("k_norm", C.c_void_p)] + \
+               [(n, MxMatrix) for n in ("w_qkv", "w_o", "w_gate", "w_up", "w_down")]
 
 
 class DitTaps(C.Structure):
@@ -89,6 +100,8 @@ def _declare(lib):
         "h3_linear_swiglu_bf16": (C.c_int, [P, P, P, P, I64, I64, I64, P]),
         "h3_linear_gated_residual_bf16": (C.c_int, [P, P, P, P, I64, P, I64, I64, I64, P, P, I32,
                                                     P]),
+        "h3_adaln_rmsnorm_modulate_mxfp8": (C.c_int, [P, P, P, P, P, I64, P, P, I32, I32, I32, F32,
+                                                      P]),
         "h3_mx_quantize_bf16": (C.c_int, [P, I64, I64, I64, P, P, P]),
         "h3_linear_mxfp8": (C.c_int, [P, P, P, P, P, I64, I64, I64, P]),
         "h3_linear_swiglu_mxfp8": (C.c_int, [P, P, P, P, P, P, P, P, I64, I64, I64, P]),
@@ -96,6 +109,8 @@ def _declare(lib):
                                                      I32, P]),
         "h3_dit_block_workspace_size": (SZ, [P, I32, I32]),
         "h3_dit_block_forward": (C.c_int, [P, P, P, P, P, P, P, I32, I32, P, P, P, SZ, P]),
+        "h3_dit_block_mx_workspace_size": (SZ, [P, I32, I32]),
+        "h3_dit_block_forward_mxfp8": (C.c_int, [P, P, P, P, P, P, P, I32, I32, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -79,11 +79,15 @@ __global__ __launch_bounds__(kThreads) void modulation_kernel(
 constexpr int kRowsPerWave = 2;
 constexpr int kAdalnWaves = 4;
 
-template <int NCH>
+// With MX the output is MXFP8 instead of bf16 (codes into h, E8M0 scales
+// into hsc, K-step-major with total_tokens rows; "MiniMax H3 on Ascend 950PR
+// / 950DT", MXFP8 online quantization): a 32-element block is the 4 chunks
+// of 4 consecutive lanes, quantised from the fp32 values.
+template <int NCH, bool MX>
 __global__ __launch_bounds__(64 * kAdalnWaves) void adaln_kernel(
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ h, const float* __restrict__ shift,
-    const float* __restrict__ scale, int64_t mod_stride, const int32_t* __restrict__ cu,
-    int num_seqs, int total_tokens, float eps) {
+    const uint16_t* __restrict__ x, void* __restrict__ hout, uint8_t* __restrict__ hsc,
+    const float* __restrict__ shift, const float* __restrict__ scale, int64_t mod_stride,
+    const int32_t* __restrict__ cu, int num_seqs, int total_tokens, float eps) {
     constexpr int hidden = NCH * 512;
     constexpr bool kCacheMod = NCH <= 8;
     const int lane = threadIdx.x & 63;
@@ -139,14 +143,28 @@ __global__ __launch_bounds__(64 * kAdalnWaves) void adaln_kernel(
             } else {
                 load_mod(seg, i, sh, sc);
             }
-            Chunk16 out;
+            float o[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a = fmaf(bf2f(xc[r][i].h[2 * e]) * rinv, sc[2 * e], sh[2 * e]);
-                const float b = fmaf(bf2f(xc[r][i].h[2 * e + 1]) * rinv, sc[2 * e + 1], sh[2 * e + 1]);
-                out.w[e] = pack_bf16x2(a, b);
+            for (int e = 0; e < 8; ++e) o[e] = fmaf(bf2f(xc[r][i].h[e]) * rinv, sc[e], sh[e]);
+            if constexpr (MX) {
+                float am = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(o[e]));
+                am = fmaxf(am, __shfl_xor(am, 1, 64));
+                am = fmaxf(am, __shfl_xor(am, 2, 64));
+                const uint32_t sb = mx_scale_byte(am);
+                const float inv = mx_inv_scale(sb);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] *= inv;
+                const int ch = i * 64 + lane;
+                *reinterpret_cast<uint2*>(static_cast<uint8_t*>(hout) + t * hidden + ch * 8) = mx_codes8(o);
+                if ((lane & 3) == 0) hsc[mx_scale_offset(t, ch >> 2, total_tokens)] = static_cast<uint8_t>(sb);
+            } else {
+                Chunk16 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out.w[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+                store_stream16(static_cast<uint16_t*>(hout) + t * hidden + (i * 64 + lane) * 8, out.u);
             }
-            store_stream16(h + t * hidden + (i * 64 + lane) * 8, out.u);
         }
     }
 }
@@ -172,12 +190,12 @@ hipError_t launch_modulation_nch(int nch, dim3 grid, hipStream_t stream, Args...
     return hipGetLastError();
 }
 
-template <typename... Args>
+template <bool MX, typename... Args>
 hipError_t launch_adaln_nch(int nch, dim3 grid, hipStream_t stream, Args... args) {
     switch (nch) {
 #define H3_ADALN_CASE(N)                                                                       \
     case N:                                                                                  \
-        hipLaunchKernelGGL(adaln_kernel<N>, grid, dim3(64 * kAdalnWaves), 0, stream, args...); \
+        hipLaunchKernelGGL((adaln_kernel<N, MX>), grid, dim3(64 * kAdalnWaves), 0, stream, args...); \
         break;
         H3_ADALN_CASE(1) H3_ADALN_CASE(2) H3_ADALN_CASE(3) H3_ADALN_CASE(4)
         H3_ADALN_CASE(5) H3_ADALN_CASE(6) H3_ADALN_CASE(7) H3_ADALN_CASE(8)
@@ -209,8 +227,20 @@ hipError_t launch_adaln(const uint16_t* x, uint16_t* h, const float* shift, cons
     if (hidden % 512 != 0 || hidden > 8192) return hipErrorInvalidValue;
     constexpr int rows_per_block = kRowsPerWave * kAdalnWaves;
     const dim3 grid((total_tokens + rows_per_block - 1) / rows_per_block);
-    return launch_adaln_nch(hidden / 512, grid, stream, x, h, shift, scale, mod_stride, cu,
-                            num_seqs, total_tokens, eps);
+    return launch_adaln_nch<false>(hidden / 512, grid, stream, x, static_cast<void*>(h),
+                                   static_cast<uint8_t*>(nullptr), shift, scale, mod_stride, cu,
+                                   num_seqs, total_tokens, eps);
+}
+
+hipError_t launch_adaln_mx(const uint16_t* x, uint8_t* h8, uint8_t* h_sc, const float* shift,
+                           const float* scale, int64_t mod_stride, const int32_t* cu, int num_seqs,
+                           int total_tokens, int hidden, float eps, hipStream_t stream) {
+    if (total_tokens == 0) return hipSuccess;
+    if (hidden % 512 != 0 || hidden > 8192) return hipErrorInvalidValue;
+    constexpr int rows_per_block = kRowsPerWave * kAdalnWaves;
+    const dim3 grid((total_tokens + rows_per_block - 1) / rows_per_block);
+    return launch_adaln_nch<true>(hidden / 512, grid, stream, x, static_cast<void*>(h8), h_sc, shift,
+                                  scale, mod_stride, cu, num_seqs, total_tokens, eps);
 }
 
 }  // namespace h3

@@ -64,6 +64,9 @@ hipError_t launch_gemm(int epilogue, const uint16_t* a, const uint16_t* w, const
 // MXFP8 operands: E4M3 codes row-major [rows, k], E8M0 scales K-step-major
 // (row r, block j at byte ((j / 4) rows + r) 4 + j % 4); y is bf16, or MXFP8
 // (codes + y_sc) for the SwiGLU epilogue. k % 128 == 0.
+hipError_t launch_adaln_mx(const uint16_t* x, uint8_t* h8, uint8_t* h_sc, const float* shift,
+                           const float* scale, int64_t mod_stride, const int32_t* cu, int num_seqs,
+                           int total_tokens, int hidden, float eps, hipStream_t stream);
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t ld, int64_t rows, int64_t k, uint8_t* codes,
                               uint8_t* scales, hipStream_t stream);
 hipError_t launch_gemm_mx(int epilogue, const uint8_t* a, const uint8_t* a_sc, const uint8_t* w,

@@ -442,6 +442,37 @@ H3_API h3_status h3_adaln_rmsnorm_modulate(const void* x, void* h_out, const flo
     return ok();
 }
 
+H3_API h3_status h3_adaln_rmsnorm_modulate_mxfp8(const void* x, void* h_codes, void* h_scales,
+                                                 const float* shift, const float* scale,
+                                                 int64_t mod_row_stride,
+                                                 const int32_t* cu_seqlens_dev,
+                                                 const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                 int32_t total_tokens, int32_t hidden, float eps,
+                                                 void* hip_stream) {
+    h3_status st = check_cu(cu_seqlens_host, num_seqs, total_tokens);
+    if (st != H3_OK) return st;
+    if (hidden <= 0 || hidden % 512 || hidden > 8192)
+        return fail(H3_ERR_UNSUPPORTED, "hidden=%d must be a multiple of 512 in [512, 8192]", hidden);
+    if (!(eps >= 0.f) || isinf(eps)) return fail(H3_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    if (total_tokens == 0) return ok();
+    if (!x || !h_codes || !h_scales || !shift || !scale || !cu_seqlens_dev)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (mod_row_stride < hidden || (mod_row_stride & 3))
+        return fail(H3_ERR_INVALID_ARGUMENT, "mod_row_stride must be >= hidden and a multiple of 4");
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(h_codes) |
+         reinterpret_cast<uintptr_t>(shift) | reinterpret_cast<uintptr_t>(scale)) & 15 ||
+        reinterpret_cast<uintptr_t>(h_scales) & 3)
+        return fail(H3_ERR_UNSUPPORTED, "x/codes/shift/scale 16-byte and scales 4-byte aligned");
+    if (static_cast<int64_t>(total_tokens) * hidden / 32 > INT32_MAX)
+        return fail(H3_ERR_UNSUPPORTED, "MX scale array exceeds 2^31 bytes");
+    hipError_t e = h3::launch_adaln_mx(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(h_codes),
+                                       static_cast<uint8_t*>(h_scales), shift, scale, mod_row_stride,
+                                       cu_seqlens_dev, num_seqs, total_tokens, hidden, eps,
+                                       static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "adaln launch");
+    return ok();
+}
+
 H3_API h3_status h3_linear_bf16(const void* a, const void* w, void* y, int64_t m, int64_t n,
                                 int64_t k, void* hip_stream) {
     h3_status st = check_gemm_shape(m, n, k, 8);
@@ -769,6 +800,148 @@ H3_API h3_status h3_dit_block_forward(const void* x, void* x_out, const void* co
     H3_TRY(h3::launch_gemm(h3::kEpiGatedResidual, abuf, static_cast<const uint16_t*>(w.w_down),
                            nullptr, yb, n, c, ffn, x1, mod + 5 * c, ms, cu_seqlens_dev,
                            num_seqs, stream), "down gemm");
+#undef H3_TRY
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+struct BlockPlanMX {
+    size_t mod, h8, hs, qkv, o, o8, os, x1, a8, as, attn, total;
+};
+
+BlockPlanMX block_plan_mx(const h3_dit_dims* d, int32_t num_seqs, int32_t total_tokens) {
+    BlockPlanMX p;
+    const size_t n = static_cast<size_t>(total_tokens), c = static_cast<size_t>(d->hidden);
+    const size_t f = static_cast<size_t>(d->ffn_dim);
+    p.mod = align_up(static_cast<size_t>(num_seqs) * 6 * c * sizeof(float));
+    p.h8 = align_up(n * c);              // h, then h2 (MX codes)
+    p.hs = align_up(n * c / 32);
+    p.qkv = align_up(n * 3 * c * 2);
+    p.o = align_up(n * c * 2);
+    p.o8 = align_up(n * c);
+    p.os = align_up(n * c / 32);
+    p.x1 = align_up(n * c * 2);
+    p.a8 = align_up(n * f);
+    p.as = align_up(n * f / 32);
+    p.attn = attn_plan(num_seqs, total_tokens, d->num_heads, d->head_dim, H3_ATTN_BF16).total;
+    p.total = p.mod + p.h8 + p.hs + p.qkv + p.o + p.o8 + p.os + p.x1 + p.a8 + p.as + p.attn;
+    return p;
+}
+
+h3_status check_dims_mx(const h3_dit_dims* d, int32_t total_tokens) {
+    h3_status st = check_dims(d);
+    if (st != H3_OK) return st;
+    if (d->ffn_dim % 128) return fail(H3_ERR_UNSUPPORTED, "ffn_dim=%d must be a multiple of 128 (MX)", d->ffn_dim);
+    const int64_t widest = std::max<int64_t>(3 * static_cast<int64_t>(d->hidden), d->ffn_dim);
+    if (static_cast<int64_t>(total_tokens) * widest / 32 > INT32_MAX ||
+        widest * std::max(d->hidden, d->ffn_dim) / 32 > INT32_MAX)
+        return fail(H3_ERR_UNSUPPORTED, "MX scale arrays exceed 2^31 bytes");
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+H3_API size_t h3_dit_block_mx_workspace_size(const h3_dit_dims* dims, int32_t num_seqs,
+                                             int32_t total_tokens) {
+    if (dims == nullptr || num_seqs < 0 || total_tokens < 0) return 0;
+    if (check_dims_mx(dims, total_tokens) != H3_OK) return 0;
+    return block_plan_mx(dims, num_seqs, total_tokens).total;
+}
+
+H3_API h3_status h3_dit_block_forward_mxfp8(const void* x, void* x_out, const void* cond,
+                                            const h3_dit_mx_weights* weights,
+                                            const h3_dit_dims* dims,
+                                            const int32_t* cu_seqlens_dev,
+                                            const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                            int32_t total_tokens, const int32_t* rope_grid,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* hip_stream) {
+    h3_status st = check_dims_mx(dims, total_tokens);
+    if (st != H3_OK) return st;
+    st = check_cu(cu_seqlens_host, num_seqs, total_tokens);
+    if (st != H3_OK) return st;
+    if (total_tokens == 0) return ok();
+    if (!x || !x_out || !cond || !weights || !cu_seqlens_dev || !rope_grid)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    const h3_dit_mx_weights& w = *weights;
+    const h3_mx_matrix* mats[5] = {&w.w_qkv, &w.w_o, &w.w_gate, &w.w_up, &w.w_down};
+    if (!w.w_mod || !w.q_norm || !w.k_norm) return fail(H3_ERR_INVALID_ARGUMENT, "NULL weight pointer");
+    for (const h3_mx_matrix* m : mats) {
+        if (!m->codes || !m->scales) return fail(H3_ERR_INVALID_ARGUMENT, "NULL MX weight pointer");
+        if (!mx_aligned(m->codes, m->scales))
+            return fail(H3_ERR_UNSUPPORTED, "MX weight codes 16-byte and scales 4-byte aligned");
+    }
+    if (x == x_out) return fail(H3_ERR_INVALID_ARGUMENT, "x and x_out may not alias");
+    const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(x_out) |
+                         reinterpret_cast<uintptr_t>(cond) | reinterpret_cast<uintptr_t>(w.w_mod) |
+                         reinterpret_cast<uintptr_t>(w.q_norm) | reinterpret_cast<uintptr_t>(w.k_norm);
+    if (al & 15) return fail(H3_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+    const BlockPlanMX p = block_plan_mx(dims, num_seqs, total_tokens);
+    if (workspace_bytes < p.total || workspace == nullptr)
+        return fail(H3_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, p.total);
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+        return fail(H3_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    char* ws = static_cast<char*>(workspace);
+    auto carve = [&](size_t bytes) { char* r = ws; ws += bytes; return r; };
+    float* mod = reinterpret_cast<float*>(carve(p.mod));
+    uint8_t* h8 = reinterpret_cast<uint8_t*>(carve(p.h8));
+    uint8_t* hs = reinterpret_cast<uint8_t*>(carve(p.hs));
+    uint16_t* qkv = reinterpret_cast<uint16_t*>(carve(p.qkv));
+    uint16_t* obuf = reinterpret_cast<uint16_t*>(carve(p.o));
+    uint8_t* o8 = reinterpret_cast<uint8_t*>(carve(p.o8));
+    uint8_t* os = reinterpret_cast<uint8_t*>(carve(p.os));
+    uint16_t* x1 = reinterpret_cast<uint16_t*>(carve(p.x1));
+    uint8_t* a8 = reinterpret_cast<uint8_t*>(carve(p.a8));
+    uint8_t* as = reinterpret_cast<uint8_t*>(carve(p.as));
+    void* attn_ws = carve(p.attn);
+
+    const int64_t n = total_tokens, c = dims->hidden, ffn = dims->ffn_dim;
+    const int64_t ms = 6 * c;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    uint16_t* yb = static_cast<uint16_t*>(x_out);
+    auto u8 = [](const void* ptr) { return static_cast<const uint8_t*>(ptr); };
+    hipError_t e;
+#define H3_TRY(call, what)                          \
+    e = (call);                                     \
+    if (e != hipSuccess) return hip_fail(e, what);
+
+    H3_TRY(h3::launch_modulation(static_cast<const uint16_t*>(cond),
+                                 static_cast<const uint16_t*>(w.w_mod), mod, num_seqs,
+                                 static_cast<int>(c), stream), "modulation");
+    H3_TRY(h3::launch_adaln_mx(xb, h8, hs, mod + 0 * c, mod + 1 * c, ms, cu_seqlens_dev, num_seqs,
+                               total_tokens, static_cast<int>(c), dims->eps, stream), "adaln 1");
+    H3_TRY(h3::launch_gemm_mx(h3::kEpiStore, h8, hs, u8(w.w_qkv.codes), u8(w.w_qkv.scales), nullptr,
+                              nullptr, qkv, nullptr, n, 3 * c, c, nullptr, nullptr, 0, nullptr, 1,
+                              stream), "qkv gemm");
+    H3_TRY(h3::launch_qk_norm_rope(qkv, qkv + c, 3 * c, 3 * c,
+                                   static_cast<const uint16_t*>(w.q_norm),
+                                   static_cast<const uint16_t*>(w.k_norm), rope_grid,
+                                   total_tokens, dims->num_heads, dims->head_dim,
+                                   dims->rope_split, dims->rope_theta, dims->eps, stream),
+           "qk norm rope");
+    h3_status ast = run_attention(qkv, qkv + c, qkv + 2 * c, obuf, 3 * c, 3 * c, 3 * c, c,
+                                  cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                                  dims->num_heads, dims->head_dim, nullptr, attn_ws, stream);
+    if (ast != H3_OK) return ast;
+    H3_TRY(h3::launch_mx_quantize(obuf, c, n, c, o8, os, stream), "o quantize");
+    H3_TRY(h3::launch_gemm_mx(h3::kEpiGatedResidual, o8, os, u8(w.w_o.codes), u8(w.w_o.scales), nullptr,
+                              nullptr, x1, nullptr, n, c, c, xb, mod + 2 * c, ms, cu_seqlens_dev,
+                              num_seqs, stream), "out-proj gemm");
+    H3_TRY(h3::launch_adaln_mx(x1, h8, hs, mod + 3 * c, mod + 4 * c, ms, cu_seqlens_dev, num_seqs,
+                               total_tokens, static_cast<int>(c), dims->eps, stream), "adaln 2");
+    H3_TRY(h3::launch_gemm_mx(h3::kEpiSwiGLU, h8, hs, u8(w.w_gate.codes), u8(w.w_gate.scales),
+                              u8(w.w_up.codes), u8(w.w_up.scales), a8, as, n, ffn, c, nullptr,
+                              nullptr, 0, nullptr, 1, stream), "gate/up gemm");
+    H3_TRY(h3::launch_gemm_mx(h3::kEpiGatedResidual, a8, as, u8(w.w_down.codes), u8(w.w_down.scales),
+                              nullptr, nullptr, yb, nullptr, n, c, ffn, x1, mod + 5 * c, ms,
+                              cu_seqlens_dev, num_seqs, stream), "down gemm");
 #undef H3_TRY
     return ok();
 }

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import _lib as L
-from ._lib import AttnOpts, DitDims, DitTaps, DitWeights, check, lib
+from ._lib import AttnOpts, DitDims, DitMxWeights, DitTaps, DitWeights, MxMatrix, check, lib
 
 BF16 = torch.bfloat16
 
@@ -353,6 +353,29 @@ def mx_quantize(x: torch.Tensor, out: Optional[MX] = None) -> MX:
     return out
 
 
+def adaln_rmsnorm_modulate_mx(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor,
+                              cu_seqlens: torch.Tensor, cu_host, eps: float = 1e-6,
+                              out: Optional[MX] = None) -> MX:
+    """MX(RMSNorm(x) * (1 + scale[seg]) + shift[seg]), quantised from fp32."""
+    dev = x.device
+    _need(x, "x", BF16, dev)
+    _need(shift, "shift", torch.float32, dev)
+    _need(scale, "scale", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    n, c = x.shape
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if shift.stride(1) != 1 or scale.stride(1) != 1 or shift.stride(0) != scale.stride(0):
+        raise ValueError("shift/scale rows must be contiguous with one common row stride")
+    out = MX.empty(n, c, dev) if out is None else out
+    cu = _host_cu(cu_host)
+    check(lib().h3_adaln_rmsnorm_modulate_mxfp8(_ptr(x), _ptr(out.codes), _ptr(out.scales), _ptr(shift),
+                                                _ptr(scale), shift.stride(0), _ptr(cu_seqlens),
+                                                cu.ctypes.data_as(C.c_void_p), cu.size - 1, n, c,
+                                                float(eps), _stream(dev)))
+    return out
+
+
 def _mx_args(a: MX, ws) -> torch.device:
     dev = a.codes.device
     for t in [a] + list(ws):
@@ -474,3 +497,53 @@ class DitBlock:
                 "x1": torch.empty((n, c), dtype=BF16, device=device),
                 "h2": torch.empty((n, c), dtype=BF16, device=device),
                 "a": torch.empty((n, self.ffn), dtype=BF16, device=device)}
+
+
+MX_WEIGHT_NAMES = ("w_qkv", "w_o", "w_gate", "w_up", "w_down")
+
+
+class DitBlockMX:
+    """The block with MXFP8 linears: the five linear weights are quantised
+    once here (h3_mx_quantize_bf16); forward() calls h3_dit_block_forward_mxfp8."""
+
+    def __init__(self, weights: Dict[str, torch.Tensor], heads: int, head_dim: int,
+                 ffn_dim: int, rope_split: Sequence[int], rope_theta: float = 10000.0,
+                 eps: float = 1e-6):
+        hidden = heads * head_dim
+        for nm in WEIGHT_NAMES:
+            _need(weights[nm], nm, BF16)
+            if not weights[nm].is_contiguous():
+                raise ValueError(f"{nm} must be contiguous")
+        self.bf16 = {nm: weights[nm] for nm in ("w_mod", "q_norm", "k_norm")}
+        self.mx = {nm: mx_quantize(weights[nm]) for nm in MX_WEIGHT_NAMES}
+        self.dims = DitDims(hidden, heads, head_dim, ffn_dim, (C.c_int32 * 3)(*rope_split),
+                            float(rope_theta), float(eps))
+        mats = [MxMatrix(self.mx[nm].codes.data_ptr(), self.mx[nm].scales.data_ptr())
+                for nm in MX_WEIGHT_NAMES]
+        self.c_weights = DitMxWeights(self.bf16["w_mod"].data_ptr(), self.bf16["q_norm"].data_ptr(),
+                                      self.bf16["k_norm"].data_ptr(), *mats)
+        self.hidden, self.ffn = hidden, ffn_dim
+
+    def workspace_bytes(self, num_seqs: int, total_tokens: int) -> int:
+        return lib().h3_dit_block_mx_workspace_size(C.byref(self.dims), num_seqs, total_tokens)
+
+    def forward(self, x: torch.Tensor, cond: torch.Tensor, cu_seqlens: torch.Tensor, cu_host,
+                rope_grid: torch.Tensor, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        dev = x.device
+        _need(x, "x", BF16, dev)
+        _need(cond, "cond", BF16, dev)
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        _need(rope_grid, "rope_grid", torch.int32, dev)
+        if not (x.is_contiguous() and cond.is_contiguous() and rope_grid.is_contiguous()):
+            raise ValueError("x, cond and rope_grid must be contiguous")
+        cu = _host_cu(cu_host)
+        b, n = cu.size - 1, x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        ws = _workspace(self.workspace_bytes(b, n), dev, workspace)
+        check(lib().h3_dit_block_forward_mxfp8(_ptr(x), _ptr(out), _ptr(cond), C.byref(self.c_weights),
+                                               C.byref(self.dims), _ptr(cu_seqlens),
+                                               cu.ctypes.data_as(C.c_void_p), b, n, _ptr(rope_grid),
+                                               _ptr(ws), ws.numel(), _stream(dev)))
+        return out

@@ -158,6 +158,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-mx", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this hot path runs on one GPU; --gpus must be 1 "
@@ -333,6 +334,67 @@ def main():
                "skip_threshold": 8.0}
         rec("fp8_quantize", tq, nbytes=q_bytes)
 
+    # The same block with MXFP8 (OCP MX, E4M3) linears: weights quantised once
+    # before timing; a step quantises its activations inside the step.
+    mxr = None
+    if not args.no_mx:
+        log("timing mxfp8 block")
+        blk_mx = ops.DitBlockMX(weights, wl.heads, wl.head_dim, wl.ffn, split)
+        ws_mx = torch.empty(blk_mx.workspace_bytes(b, n), dtype=torch.uint8, device=dev)
+        out_mx = torch.empty_like(x)
+        step_mx = lambda: blk_mx.forward(x, cond, cu_d, cu, grid_d, out=out_mx, workspace=ws_mx)
+        for _ in range(args.warmup):
+            step_mx()
+        ms_mx = timer(step_mx, args.steps)
+        mods = {}
+        if not args.no_stages:
+            mod = taps["mod"]
+            wmx = blk_mx.mx
+            h_mx = ops.adaln_rmsnorm_modulate_mx(x, mod[:, 0:c], mod[:, c:2 * c], cu_d, cu)
+            o_mx = ops.mx_quantize(taps["o"])
+            h2_mx = ops.adaln_rmsnorm_modulate_mx(taps["x1"], mod[:, 3 * c:4 * c], mod[:, 4 * c:5 * c],
+                                                  cu_d, cu)
+            a_mx = ops.linear_swiglu_mx(h2_mx, wmx["w_gate"], wmx["w_up"])
+            x1_mx = torch.empty_like(x)
+            x2_mx = torch.empty_like(x)
+
+            def mxrec(name, t, flops=None, nbytes=None):
+                e = {"ms": round(t["median"], 4), "p10_ms": round(t["p10"], 4), "p90_ms": round(t["p90"], 4),
+                     "launches": t["n"], "mall_flushed": t["flush"]}
+                if flops is not None:
+                    tf = flops / (t["median"] * 1e-3) / 1e12
+                    e["tflops"] = round(tf, 2)
+                    e["frac_fp8_peak"] = round(tf / PEAK_FP8_TFLOPS, 4)
+                if nbytes is not None:
+                    gbs = nbytes / (t["median"] * 1e-3) / 1e9
+                    e["gbs"] = round(gbs, 1)
+                    e["frac_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+                mods[name] = e
+            it = stage_iters
+            mxrec("adaln_mx", sampler(lambda: ops.adaln_rmsnorm_modulate_mx(
+                x, mod[:, 0:c], mod[:, c:2 * c], cu_d, cu, out=h_mx), it, True),
+                nbytes=n * c * 2 + n * c + n * c // 32)
+            mxrec("qkv_gemm_mx", sampler(lambda: ops.linear_mx(h_mx, wmx["w_qkv"]), it, False),
+                  flops=2.0 * n * c * 3 * c)
+            mxrec("o_quantize_mx", sampler(lambda: ops.mx_quantize(taps["o"], out=o_mx), it, True),
+                  nbytes=n * c * 2 + n * c + n * c // 32)
+            mxrec("out_proj_gated_residual_mx", sampler(lambda: ops.linear_gated_residual_mx(
+                o_mx, wmx["w_o"], x, mod[:, 2 * c:3 * c], cu_d, cu, out=x1_mx), it, False),
+                flops=2.0 * n * c * c)
+            mxrec("swiglu_gemm_mx", sampler(lambda: ops.linear_swiglu_mx(h2_mx, wmx["w_gate"], wmx["w_up"],
+                                                                         out=a_mx), it, False),
+                  flops=2.0 * n * c * 2 * wl.ffn)
+            mxrec("down_gated_residual_mx", sampler(lambda: ops.linear_gated_residual_mx(
+                a_mx, wmx["w_down"], taps["x1"], mod[:, 5 * c:6 * c], cu_d, cu, out=x2_mx), it, False),
+                flops=2.0 * n * wl.ffn * c)
+            del h_mx, o_mx, h2_mx, a_mx, x1_mx, x2_mx
+        mxr = {"workload": f"{wl.name} with MXFP8 (OCP MX v1.0, E4M3, 32-element K blocks) linears",
+               "block_ms": round(ms_mx, 4),
+               "block_tflops": round((f_attn + f_gemm) / (ms_mx * 1e-3) / 1e12, 2),
+               "speedup_vs_bf16_block": round(ms_step / ms_mx, 4),
+               "stages": mods}
+        del blk_mx, ws_mx, out_mx
+
     traffic = load_traffic()
     result = {
         "metric": METRIC,
@@ -362,6 +424,7 @@ def main():
                      "traffic": traffic},
         "stages": stages,
         "fp8_attention": fp8,
+        "mxfp8_linears": mxr,
         "timed_wall_s": round(t_wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -309,6 +309,17 @@ H3_API h3_status h3_linear_gated_residual_bf16(const void* a, const void* w, con
  * Errors as for the bf16 linears; all buffers are the caller's, nothing is
  * allocated and every launch goes on hip_stream.
  * ---------------------------------------------------------------------- */
+/* The AdaLN RMSNorm + modulate of h3_adaln_rmsnorm_modulate with MXFP8
+ * output: h is quantised from its fp32 values (no bf16 step) into codes
+ * [total_tokens, hidden] and scales (rows = total_tokens). Arguments and
+ * errors otherwise as there; codes 16-byte, scales 4-byte aligned. */
+H3_API h3_status h3_adaln_rmsnorm_modulate_mxfp8(const void* x, void* h_codes, void* h_scales,
+                                                 const float* shift, const float* scale,
+                                                 int64_t mod_row_stride,
+                                                 const int32_t* cu_seqlens_dev,
+                                                 const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                 int32_t total_tokens, int32_t hidden, float eps,
+                                                 void* hip_stream);
 H3_API h3_status h3_mx_quantize_bf16(const void* x, int64_t x_row_stride, int64_t rows, int64_t k,
                                      void* codes, void* scales, void* hip_stream);
 H3_API h3_status h3_linear_mxfp8(const void* a, const void* a_scales, const void* w,
@@ -372,6 +383,38 @@ H3_API h3_status h3_dit_block_forward(const void* x, void* x_out, const void* co
                                       int32_t total_tokens, const int32_t* rope_grid,
                                       const h3_dit_taps* taps, void* workspace,
                                       size_t workspace_bytes, void* hip_stream);
+
+
+/* ------------------------------------------------------------------------
+ * The same block with MXFP8 linears ([H3-950PR] "Recommended lossy
+ * configuration", MXFP8 online quantization of the transformer; format as
+ * for h3_linear_mxfp8): the four linears take MX weights (quantised once by
+ * the caller with h3_mx_quantize_bf16) and MX activations produced in the
+ * previous kernel: h and h2 by the AdaLN kernel from its fp32 values, o by
+ * h3_mx_quantize_bf16 from the bf16 attention output, a by the SwiGLU
+ * epilogue from fp32. qkv, x1 and x_out stay bf16; the modulation GEMV,
+ * norms, RoPE and attention are the bf16 path's. ffn_dim a multiple of 128;
+ * total_tokens * max(3 hidden, ffn_dim) / 32 < 2^31. Needs a workspace of
+ * h3_dit_block_mx_workspace_size(...) bytes (256-byte aligned).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    const void* codes;   /* E4M3 [rows, k] */
+    const void* scales;  /* E8M0, K-step-major (see the MXFP8 linears) */
+} h3_mx_matrix;
+typedef struct {
+    const void *w_mod, *q_norm, *k_norm;               /* bf16, as in h3_dit_weights */
+    h3_mx_matrix w_qkv, w_o, w_gate, w_up, w_down;     /* MX, [out, in] */
+} h3_dit_mx_weights;
+H3_API size_t h3_dit_block_mx_workspace_size(const h3_dit_dims* dims, int32_t num_seqs,
+                                             int32_t total_tokens);
+H3_API h3_status h3_dit_block_forward_mxfp8(const void* x, void* x_out, const void* cond,
+                                            const h3_dit_mx_weights* weights,
+                                            const h3_dit_dims* dims,
+                                            const int32_t* cu_seqlens_dev,
+                                            const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                            int32_t total_tokens, const int32_t* rope_grid,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -159,3 +159,35 @@ def test_linear_mx_deterministic(dev, ops):
     y1 = ops.linear_mx(am, wm)
     y2 = ops.linear_mx(am, wm)
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("c", [512, 3072])
+def test_adaln_mx_multi_segment(dev, ops, c):
+    """AdaLN with MX output against MX(the float64 AdaLN): the kernel
+    quantises its fp32 values, so a code may sit one E4M3 step off where the
+    value is within fp32 rounding (2^-18 relative, generous) of a midpoint."""
+    import torch
+    announce(f"adaln mx C={c}")
+    lens = [300, 0, 65, 129]
+    cu = h3synth.cu_from_lengths(lens)
+    n = int(cu[-1])
+    rng = np.random.default_rng(450 + c)
+    x = h3synth.Bf16Array.from_f32(rng.standard_normal((n, c)).astype(np.float32))
+    mod = (rng.standard_normal((len(lens), 6 * c)) * 0.5).astype(np.float32)
+    mod_t = torch.from_numpy(mod).to(dev)
+    h = ops.adaln_rmsnorm_modulate_mx(to_dev_bf16(x, dev), mod_t[:, 0:c], mod_t[:, c:2 * c],
+                                      to_dev_i32(cu, dev), cu, 1e-6)
+    p, e = _mx_values(h)
+    seg = oracle.segment_ids(cu)
+    pre = oracle.adaln_modulate_ref(x.f32, mod[:, 0:c], mod[:, c:2 * c], seg, 1e-6)
+    pr, er = oracle.mx_quantize(pre)
+    assert np.mean(e != er) < 1e-3 and np.all(np.abs(e - er) <= 1)
+    scale = np.power(2.0, e.astype(np.float64)).repeat(32, axis=1)
+    got = p * scale
+    v = np.abs(pre) / scale
+    half = 0.5 * np.power(2.0, np.maximum(np.floor(np.log2(np.maximum(v, 2.0 ** -30))), -6) - 3) * scale
+    sat = v > 448
+    over = np.abs(got - pre) - (half * (1 + 1e-9) + 2.0 ** -18 * np.abs(pre))
+    assert np.all(over[~sat] <= 0), float(over[~sat].max())
+    assert np.all(np.abs(got[sat]) == 448 * scale[sat])
+    assert np.mean(got == oracle.mx_dequantize(pr, er)) > 0.999
