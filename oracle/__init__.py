@@ -11,7 +11,8 @@ invariants, special cases or brute force):
   silu, swiglu_ref, gated_residual_ref, dit_block_ref, dit_block_rows_ref,
   e4m3_round, fp8_attn_emulated_ref, bf16_round (storage emulation),
   mx_scale_exponents, mx_quantize, mx_dequantize, mx_fake_quant, mx_linear_ref
-  (MXFP8 linears, OCP MX v1.0 reading).
+  (MXFP8 linears, OCP MX v1.0 reading), frames_to_uint8_values,
+  frames_to_uint8_bthwc (decoded-frame compaction).
 
 Parity unpinned: agreement of the block structure with the real model's
 block (the pages give operator names only, no equations or weights).
@@ -24,6 +25,7 @@ from .fp8_attention import (e4m3_round, fp8_attn_emulated_ref, quantize_qk_block
                             quantize_v_channels)
 from .mx_linear import (mx_dequantize, mx_fake_quant, mx_linear_ref, mx_quantize,
                         mx_scale_exponents)
+from .output_compaction import frames_to_uint8_bthwc, frames_to_uint8_values
 
 __all__ = [
     "MOD_CHUNKS", "adaln_modulate_ref", "bf16_round", "attn_varlen_ref", "check_cu_seqlens", "dit_block_ref",
@@ -31,5 +33,5 @@ __all__ = [
     "rel_frobenius", "rmsnorm", "rope_3d", "schedule_ref", "segment_ids", "silu",
     "split_modulation", "swiglu_ref", "tile_offsets", "e4m3_round", "fp8_attn_emulated_ref",
     "quantize_qk_blocks", "quantize_v_channels", "mx_dequantize", "mx_fake_quant", "mx_linear_ref",
-    "mx_quantize", "mx_scale_exponents",
+    "mx_quantize", "mx_scale_exponents", "frames_to_uint8_bthwc", "frames_to_uint8_values",
 ]
