@@ -28,7 +28,8 @@ EXPORTS = (
     "h3_attn_varlen_workspace_size", "h3_attn_varlen_num_items", "h3_attn_varlen",
     "h3_fp8_num_tiles", "h3_fp8_quantize_workspace_size", "h3_fp8_quantize",
     "h3_qk_rmsnorm_rope", "h3_modulation", "h3_adaln_rmsnorm_modulate", "h3_linear_bf16",
-    "h3_linear_swiglu_bf16", "h3_linear_gated_residual_bf16", "h3_adaln_rmsnorm_modulate_mxfp8",
+    "h3_linear_swiglu_bf16", "h3_linear_gated_residual_bf16", "h3_frames_to_uint8_bthwc",
+    "h3_adaln_rmsnorm_modulate_mxfp8",
     "h3_mx_quantize_bf16",
     "h3_linear_mxfp8", "h3_linear_swiglu_mxfp8", "h3_linear_gated_residual_mxfp8",
     "h3_dit_block_workspace_size", "h3_dit_block_forward", "h3_dit_block_mx_workspace_size",
@@ -100,6 +101,7 @@ def _declare(lib):
         "h3_linear_swiglu_bf16": (C.c_int, [P, P, P, P, I64, I64, I64, P]),
         "h3_linear_gated_residual_bf16": (C.c_int, [P, P, P, P, I64, P, I64, I64, I64, P, P, I32,
                                                     P]),
+        "h3_frames_to_uint8_bthwc": (C.c_int, [P, P, I64, I64, I64, I64, I64, P]),
         "h3_adaln_rmsnorm_modulate_mxfp8": (C.c_int, [P, P, P, P, P, I64, P, P, I32, I32, I32, F32,
                                                       P]),
         "h3_mx_quantize_bf16": (C.c_int, [P, I64, I64, I64, P, P, P]),

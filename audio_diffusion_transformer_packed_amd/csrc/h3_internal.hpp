@@ -67,6 +67,8 @@ hipError_t launch_gemm(int epilogue, const uint16_t* a, const uint16_t* w, const
 hipError_t launch_adaln_mx(const uint16_t* x, uint8_t* h8, uint8_t* h_sc, const float* shift,
                            const float* scale, int64_t mod_stride, const int32_t* cu, int num_seqs,
                            int total_tokens, int hidden, float eps, hipStream_t stream);
+hipError_t launch_frames_to_u8(const float* x, uint8_t* out, int64_t b, int c, int64_t pixels,
+                               hipStream_t stream);
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t ld, int64_t rows, int64_t k, uint8_t* codes,
                               uint8_t* scales, hipStream_t stream);
 hipError_t launch_gemm_mx(int epilogue, const uint8_t* a, const uint8_t* a_sc, const uint8_t* w,

@@ -538,6 +538,25 @@ H3_API h3_status h3_linear_gated_residual_bf16(const void* a, const void* w, con
     return ok();
 }
 
+H3_API h3_status h3_frames_to_uint8_bthwc(const float* x, void* out, int64_t batch, int64_t channels,
+                                          int64_t frames, int64_t height, int64_t width,
+                                          void* hip_stream) {
+    if (batch < 0 || channels < 0 || frames < 0 || height < 0 || width < 0)
+        return fail(H3_ERR_INVALID_ARGUMENT, "negative dimension");
+    if (channels > 64) return fail(H3_ERR_UNSUPPORTED, "channels=%lld > 64", (long long)channels);
+    if (batch == 0 || channels == 0 || frames == 0 || height == 0 || width == 0) return ok();
+    const int64_t lim = static_cast<int64_t>(1) << 40;
+    if (frames > lim / height || frames * height > lim / width ||
+        frames * height * width > lim / (batch * channels))
+        return fail(H3_ERR_UNSUPPORTED, "too many elements");
+    if (!x || !out) return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (reinterpret_cast<uintptr_t>(x) & 3) return fail(H3_ERR_INVALID_ARGUMENT, "x must be 4-byte aligned");
+    hipError_t e = h3::launch_frames_to_u8(x, static_cast<uint8_t*>(out), batch, static_cast<int>(channels),
+                                           frames * height * width, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "frames launch");
+    return ok();
+}
+
 H3_API h3_status h3_mx_quantize_bf16(const void* x, int64_t x_row_stride, int64_t rows, int64_t k,
                                      void* codes, void* scales, void* hip_stream) {
     if (rows < 0 || k <= 0) return fail(H3_ERR_INVALID_ARGUMENT, "rows=%lld k=%lld", (long long)rows, (long long)k);

@@ -313,6 +313,20 @@ def linear_gated_residual(a: torch.Tensor, w: torch.Tensor, res: torch.Tensor,
     return y
 
 
+def frames_to_uint8_bthwc(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 decoded frames [B, C, T, H, W] -> uint8 [B, T, H, W, C]."""
+    _need(x, "x", torch.float32)
+    if x.dim() != 5 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, C, T, H, W] tensor")
+    b, c, t, h, w = x.shape
+    if out is None:
+        out = torch.empty((b, t, h, w, c), dtype=torch.uint8, device=x.device)
+    if out.dtype != torch.uint8 or tuple(out.shape) != (b, t, h, w, c) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 [B, T, H, W, C] tensor")
+    check(lib().h3_frames_to_uint8_bthwc(_ptr(x), _ptr(out), b, c, t, h, w, _stream(x.device)))
+    return out
+
+
 # --------------------------------------------------------------------------
 # MXFP8 (layouts in h3dit.h: codes [rows, k] uint8, scales K-step-major)
 # --------------------------------------------------------------------------

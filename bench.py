@@ -294,6 +294,19 @@ def main():
         rec(f"attention_bf16_per_rank_h{h_rank}", sampler(rank_attn, stage_iters, False),
             flops=attention_flops(wl.lengths, h_rank, wl.head_dim))
 
+    # Decoded-frame compaction (FP32 BCTHW -> uint8 BTHWC) at the 10 s clip's
+    # 243 frames of 1344 x 768 RGB: 3.0 GB read, 0.75 GB written. Synthetic
+    # frames uniform in [-1.1, 1.1] from a seeded torch generator.
+    if not args.no_stages:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(inp.seed)
+        frames = torch.rand((1, 3, 243, 768, 1344), generator=gen, device=dev) * 2.2 - 1.1
+        frames_u8 = torch.empty((1, 243, 768, 1344, 3), dtype=torch.uint8, device=dev)
+        rec("frames_to_uint8_bthwc",
+            sampler(lambda: ops.frames_to_uint8_bthwc(frames, out=frames_u8), stage_iters, True),
+            nbytes=frames.numel() * 5)
+        del frames, frames_u8
+
     fp8 = None
     if not args.no_fp8:
         log("timing fp8 attention")

@@ -276,6 +276,24 @@ H3_API h3_status h3_linear_gated_residual_bf16(const void* a, const void* w, con
                                                int32_t num_seqs, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Decoded frames to contiguous uint8 ([FastH3-ZH] "紧凑输出与并行 MP4 构建";
+ * [FastH3-EN] system-wide optimizations, GPU output preparation bullet: the
+ * decoder's FP32 BCTHW frames are converted once on the GPU to uint8
+ * BTHWC). The pages give no value range or rounding; the map taken is the
+ * decoded-video convention for [-1, 1], evaluated in fp32 in this order:
+ *   out[b, t, h, w, c] = round_half_even(255 * clamp(x[b, c, t, h, w] * 0.5
+ *                        + 0.5, 0, 1)),   NaN -> 0.
+ * x: fp32 [batch, channels, frames, height, width] contiguous, 4-byte
+ * aligned; out: uint8 [batch, frames, height, width, channels] contiguous.
+ * channels <= 64; fastest when x and out are 16-byte aligned, channels <= 4
+ * and frames * height * width is a multiple of 16. Zero-sized dims are a
+ * no-op.
+ * ---------------------------------------------------------------------- */
+H3_API h3_status h3_frames_to_uint8_bthwc(const float* x, void* out, int64_t batch, int64_t channels,
+                                          int64_t frames, int64_t height, int64_t width,
+                                          void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * MXFP8 linears ([H3-950PR] "Recommended lossy configuration": the
  * transformer runs with MXFP8 online quantization; [FastH3-EN] "Scaling
  * beyond the FastH3 profile", quantization-paths bullet: online FP8 for the
