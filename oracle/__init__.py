@@ -12,7 +12,9 @@ invariants, special cases or brute force):
   e4m3_round, fp8_attn_emulated_ref, bf16_round (storage emulation),
   mx_scale_exponents, mx_quantize, mx_dequantize, mx_fake_quant, mx_linear_ref
   (MXFP8 linears, OCP MX v1.0 reading), frames_to_uint8_values,
-  frames_to_uint8_bthwc (decoded-frame compaction).
+  frames_to_uint8_bthwc (decoded-frame compaction), int8_quantize_qk_blocks,
+  keep_count, select_kv_blocks, bsa_attn_emulated_ref, dense_fallback
+  (block-sparse attention with INT8 Q/K and FP8 V).
 
 Parity unpinned: agreement of the block structure with the real model's
 block (the pages give operator names only, no equations or weights).
@@ -26,6 +28,8 @@ from .fp8_attention import (e4m3_round, fp8_attn_emulated_ref, quantize_qk_block
 from .mx_linear import (mx_dequantize, mx_fake_quant, mx_linear_ref, mx_quantize,
                         mx_scale_exponents)
 from .output_compaction import frames_to_uint8_bthwc, frames_to_uint8_values
+from .block_sparse_attention import (bsa_attn_emulated_ref, dense_fallback, int8_quantize_qk_blocks,
+                                     keep_count, select_kv_blocks)
 
 __all__ = [
     "MOD_CHUNKS", "adaln_modulate_ref", "bf16_round", "attn_varlen_ref", "check_cu_seqlens", "dit_block_ref",
@@ -34,4 +38,5 @@ __all__ = [
     "split_modulation", "swiglu_ref", "tile_offsets", "e4m3_round", "fp8_attn_emulated_ref",
     "quantize_qk_blocks", "quantize_v_channels", "mx_dequantize", "mx_fake_quant", "mx_linear_ref",
     "mx_quantize", "mx_scale_exponents", "frames_to_uint8_bthwc", "frames_to_uint8_values",
+    "bsa_attn_emulated_ref", "dense_fallback", "int8_quantize_qk_blocks", "keep_count", "select_kv_blocks",
 ]
