@@ -27,7 +27,8 @@ EXPORTS = (
     "h3_varlen_bookkeeping_workspace_size", "h3_varlen_bookkeeping",
     "h3_attn_varlen_workspace_size", "h3_attn_varlen_num_items", "h3_attn_varlen",
     "h3_fp8_num_tiles", "h3_fp8_quantize_workspace_size", "h3_fp8_quantize",
-    "h3_qk_rmsnorm_rope", "h3_modulation", "h3_adaln_rmsnorm_modulate", "h3_linear_bf16",
+    "h3_attn_block_sparse_list_stride", "h3_attn_block_sparse_workspace_size",
+    "h3_attn_block_sparse", "h3_qk_rmsnorm_rope", "h3_modulation", "h3_adaln_rmsnorm_modulate", "h3_linear_bf16",
     "h3_linear_swiglu_bf16", "h3_linear_gated_residual_bf16", "h3_frames_to_uint8_bthwc",
     "h3_adaln_rmsnorm_modulate_mxfp8",
     "h3_mx_quantize_bf16",
@@ -94,6 +95,10 @@ def _declare(lib):
         "h3_fp8_quantize_workspace_size": (SZ, [I32, I32, I32]),
         "h3_fp8_quantize": (C.c_int, [P, P, P, I64, I64, I64, P, P, I32, I32, I32, I32, P, P, P, P,
                                       P, P, P, SZ, P]),
+        "h3_attn_block_sparse_list_stride": (C.c_int, [P, I32, F32, P]),
+        "h3_attn_block_sparse_workspace_size": (SZ, [I32, I32, I32, I32, F32]),
+        "h3_attn_block_sparse": (C.c_int, [P, P, P, P, I64, I64, I64, I64, P, P, I32, I32, I32, I32,
+                                           F32, F32, P, P, SZ, P]),
         "h3_qk_rmsnorm_rope": (C.c_int, [P, P, I64, I64, P, P, P, I32, I32, I32, P, F32, F32, P]),
         "h3_modulation": (C.c_int, [P, P, P, I32, I32, P]),
         "h3_adaln_rmsnorm_modulate": (C.c_int, [P, P, P, P, I64, P, P, I32, I32, I32, F32, P]),

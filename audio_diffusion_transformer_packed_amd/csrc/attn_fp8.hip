@@ -45,6 +45,8 @@ constexpr int kVT = kD * kBN;              // bytes of a V^T tile
 constexpr float kLog2_448 = 8.807354922057604f;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -75,13 +77,25 @@ __device__ __forceinline__ i32x8 read32(const char* p0, const char* p1) {
                  static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z), static_cast<int>(b.w)};
 }
 
+__device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// BSA: the block-sparse variant. Q and K hold INT8 codes and S^T runs on
+// v_mfma_i32_32x32x32_i8 (two per fp8 k-step: the lane's first and second
+// 16 bytes; the A and B lanes hold the same head-dim positions, so the sum
+// covers every position once); the work item visits only the kept key
+// blocks of its query block, lists[(head, first 64-row block)][0 .. keep),
+// in ascending order; no skip rule.
+template <bool BSA>
 __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
     const float* __restrict__ qsc, const float* __restrict__ ksc, const float* __restrict__ vsc,
     uint16_t* __restrict__ o, int64_t os, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ tb, const int4* __restrict__ items, int num_seqs,
     int total_tokens, int num_heads, int64_t num_tiles, float scale_log2, int skip,
-    float thr_log2, int32_t* __restrict__ skip_counts) {
+    float thr_log2, int32_t* __restrict__ skip_counts, const int32_t* __restrict__ lists,
+    int64_t list_stride, int sp_permille) {
     // K stage 0, K stage 1, V stage 0, V stage 1
     __shared__ __attribute__((aligned(1024))) char smem[2 * kKT + 2 * kVT];
     __shared__ int32_t wskip[kWaves];
@@ -106,6 +120,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const int ntiles = (len + kBN - 1) / kBN;
     const int keys_left = len - (ntiles - 1) * kBN;
     const int tbs = __builtin_amdgcn_readfirstlane(tb[seg]);
+    int nsel = ntiles;                  // key tiles this work item visits
+    const int32_t* lst = lists;
+    if constexpr (BSA) {
+        nsel = max(1, ntiles - static_cast<int>((static_cast<int64_t>(ntiles) * sp_permille) / 1000));
+        lst = lists + (static_cast<int64_t>(head) * num_tiles + tbs + (q0 - kv0) / kBN) * list_stride;
+    }
+    // key tile of step u: the u-th kept block (clamped into the segment, so
+    // no list content can address outside it), or tile u
+    auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
+        if constexpr (BSA) return min(max(__builtin_amdgcn_readfirstlane(lst[u]), 0), ntiles - 1);
+        else return u;
+    };
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -164,13 +190,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(v8t + (static_cast<int64_t>(head) * num_tiles + tbs) * kVT), 0,
         ntiles * kVT, kBufferWord3);
-    auto dma_k = [&](int tile) __attribute__((always_inline)) {
-        char* dst = smem + (tile & 1) * kKT + 2048 * wg;
+    // step u's tiles go to stage u & 1
+    auto dma_k = [&](int u) __attribute__((always_inline)) {
+        char* dst = smem + (u & 1) * kKT + 2048 * wg;
+        const int tile = tile_at(u);
         buf_dma16(rk, ksrc0, tile * kKT, dst);
         buf_dma16(rk, ksrc1, tile * kKT, dst + 1024);
     };
-    auto dma_v = [&](int tile) __attribute__((always_inline)) {
-        char* dst = smem + 2 * kKT + (tile & 1) * kVT + 2048 * wg;
+    auto dma_v = [&](int u) __attribute__((always_inline)) {
+        char* dst = smem + 2 * kKT + (u & 1) * kVT + 2048 * wg;
+        const int tile = tile_at(u);
         buf_dma16(rv, vsrc0, tile * kVT, dst);
         buf_dma16(rv, vsrc1, tile * kVT, dst + 1024);
     };
@@ -200,15 +229,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     // from V stage (u-1) & 1 (u >= 1, tile not skipped)
     auto mfma_block = [&](int u) __attribute__((always_inline)) {
         if (!wave_active) return;
-        if (u < ntiles) {
+        if (u < nsel) {
             const char* kl = smem + (u & 1) * kKT;
-            sc[0] = f32x16{};
-            sc[1] = f32x16{};
+            if constexpr (BSA) {
+                i32x16 si[2] = {i32x16{}, i32x16{}};
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        const i32x8 kf = read32(kl + 4096 * b + kro[c][0], kl + 4096 * b + kro[c][1]);
+                        si[b] = mfma_i8(kf.lo, qf[c].lo, si[b]);
+                        si[b] = mfma_i8(kf.hi, qf[c].hi, si[b]);
+                    }
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
-                    sc[b] = mfma_fp8(read32(kl + 4096 * b + kro[c][0], kl + 4096 * b + kro[c][1]), qf[c], sc[b]);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sc[b][r] = static_cast<float>(si[b][r]);
+            } else {
+                sc[0] = f32x16{};
+                sc[1] = f32x16{};
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        sc[b] = mfma_fp8(read32(kl + 4096 * b + kro[c][0], kl + 4096 * b + kro[c][1]), qf[c], sc[b]);
+            }
         }
         if (u >= 1 && pv_pending) {
             const char* vl = smem + 2 * kKT + ((u - 1) & 1) * kVT;
@@ -220,8 +265,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     // softmax block S(u): tile max, skip rule, rescale, P of tile u
     auto softmax_block = [&](int u) __attribute__((always_inline)) {
         if (!wave_active) return;
-        const float sk = ksc[static_cast<int64_t>(tbs + u) * num_heads + head];
-        if (u + 1 == ntiles && keys_left < kBN) {
+        const int tile = tile_at(u);
+        const float sk = ksc[static_cast<int64_t>(tbs + tile) * num_heads + head];
+        if (tile + 1 == ntiles && keys_left < kBN) {
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -273,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     };
 
     // ---- prologue: K(0) in LDS, every wave one 1 KB block ----
-    buf_dma16(rk, ksrc_of(wave), 0, smem + 1024 * wave);
+    buf_dma16(rk, ksrc_of(wave), tile_at(0) * kKT, smem + 1024 * wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -291,12 +337,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     // the group waits for its DMA at the end of its M(u+1), before barrier 2u+4.
     auto issue_dma = [&](int u) __attribute__((always_inline)) {
         if (!g0) {
-            if (u + 2 < ntiles) dma_k(u + 2);
-            if (u + 1 < ntiles) dma_v(u + 1);
+            if (u + 2 < nsel) dma_k(u + 2);
+            if (u + 1 < nsel) dma_v(u + 1);
         }
     };
     if (!g0) {
-        if (1 < ntiles) dma_k(1);
+        if (1 < nsel) dma_k(1);
         dma_v(0);
         bar();
     }
@@ -306,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     issue_dma(0);
     softmax_block(0);
     bar();
-    for (int u = 1; u < ntiles; ++u) {
+    for (int u = 1; u < nsel; ++u) {
         mfma_block(u);
         dma_wait();
         bar();
@@ -314,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
         softmax_block(u);
         bar();
     }
-    mfma_block(ntiles);
+    mfma_block(nsel);
     if (g0) bar();
 
     // ---- O = acc s_v / l; lane holds channels 32 db + 8 r4 + 4 g + [0, 4) ----
@@ -370,7 +416,66 @@ Fp8Scratch fp8_scratch_layout(int num_seqs, int total_tokens, int num_heads) {
     return s;
 }
 
+// Block-sparse scratch: the fp8 layout (Q/K codes INT8 there), then the
+// code sums and the kept-block lists.
+struct BsaScratch {
+    Fp8Scratch f;
+    size_t qsum, ksum, lists, total;
+};
+
+BsaScratch bsa_scratch_layout(int num_seqs, int total_tokens, int num_heads, int64_t list_stride) {
+    BsaScratch b;
+    b.f = fp8_scratch_layout(num_seqs, total_tokens, num_heads);
+    const size_t t = fp8_tiles_upper_bound(num_seqs, total_tokens);
+    const size_t sums = up256(t * num_heads * kD * sizeof(int32_t));
+    size_t off = b.f.total;
+    b.qsum = off;  off += sums;
+    b.ksum = off;  off += sums;
+    b.lists = off; off += up256(t * num_heads * static_cast<size_t>(list_stride) * sizeof(int32_t));
+    b.total = off;
+    return b;
+}
+
 }  // namespace
+
+size_t bsa_scratch_bytes(int num_seqs, int total_tokens, int num_heads, int64_t list_stride) {
+    return bsa_scratch_layout(num_seqs, total_tokens, num_heads, list_stride).total;
+}
+
+hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                           int64_t qs, int64_t ks, int64_t vs, int64_t os, const int32_t* cu,
+                           const int32_t* cu_host, const int32_t* items, int64_t num_items,
+                           int num_seqs, int total_tokens, int num_heads, float softmax_scale,
+                           int sp_permille, int64_t list_stride, int32_t* lists_out, void* scratch,
+                           hipStream_t stream) {
+    if (num_items <= 0 || num_seqs <= 0) return hipSuccess;
+    int64_t tiles = 0;
+    for (int s = 0; s < num_seqs; ++s) tiles += (cu_host[s + 1] - cu_host[s] + kBN - 1) / kBN;
+    const BsaScratch L = bsa_scratch_layout(num_seqs, total_tokens, num_heads, list_stride);
+    char* base = static_cast<char*>(scratch);
+    uint8_t* q8 = reinterpret_cast<uint8_t*>(base + L.f.q8);
+    uint8_t* k8 = reinterpret_cast<uint8_t*>(base + L.f.k8);
+    uint8_t* v8t = reinterpret_cast<uint8_t*>(base + L.f.v8t);
+    float* qsc = reinterpret_cast<float*>(base + L.f.qsc);
+    float* ksc = reinterpret_cast<float*>(base + L.f.ksc);
+    float* vsc = reinterpret_cast<float*>(base + L.f.vsc);
+    int32_t* qsum = reinterpret_cast<int32_t*>(base + L.qsum);
+    int32_t* ksum = reinterpret_cast<int32_t*>(base + L.ksum);
+    int32_t* lists = lists_out ? lists_out : reinterpret_cast<int32_t*>(base + L.lists);
+    void* ws = base + L.f.ws;
+    hipError_t e = launch_fp8_quantize(q, k, v, qs, ks, vs, cu, num_seqs, num_heads, tiles, q8, k8,
+                                       v8t, qsc, ksc, vsc, ws, stream, qsum, ksum);
+    if (e != hipSuccess) return e;
+    const int32_t* tb = static_cast<const int32_t*>(ws);   // tile prefix sums from the quantise pass
+    e = launch_bsa_select(qsum, ksum, qsc, ksc, cu, tb, items, num_items, num_seqs, total_tokens,
+                          num_heads, tiles, sp_permille, list_stride, lists, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(static_cast<unsigned>(num_items)), dim3(kThreads), 0,
+                       stream, q8, k8, v8t, qsc, ksc, vsc, o, os, cu, tb,
+                       reinterpret_cast<const int4*>(items), num_seqs, total_tokens, num_heads,
+                       tiles, softmax_scale * kLog2e, 0, 0.f, nullptr, lists, list_stride, sp_permille);
+    return hipGetLastError();
+}
 
 bool fp8_attention_available() { return true; }
 
@@ -402,10 +507,11 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t*
                                        v8t, qsc, ksc, vsc, ws, stream);
     if (e != hipSuccess) return e;
     const int32_t* tb = static_cast<const int32_t*>(ws);   // tile prefix sums from the quantise pass
-    hipLaunchKernelGGL(attn_fp8_kernel, dim3(static_cast<unsigned>(num_items)), dim3(kThreads), 0,
+    hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3(static_cast<unsigned>(num_items)), dim3(kThreads), 0,
                        stream, q8, k8, v8t, qsc, ksc, vsc, o, os, cu, tb,
                        reinterpret_cast<const int4*>(items), num_seqs, total_tokens, num_heads,
-                       tiles, softmax_scale * kLog2e, skip, skip_threshold * kLog2e, skip_counts);
+                       tiles, softmax_scale * kLog2e, skip, skip_threshold * kLog2e, skip_counts,
+                       nullptr, int64_t{0}, 0);
     return hipGetLastError();
 }
 

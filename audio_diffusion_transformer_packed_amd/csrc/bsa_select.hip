@@ -1,0 +1,164 @@
+// Key-block selection of the block-sparse attention path ("MiniMax H3 on
+// Ascend 950PR / 950DT", section "Recommended lossy configuration (Ascend
+// 950PR / 950DT)": EQBSA block-sparse attention with Q/K in INT8 and V in
+// FP8 at sparsity 0.8; the page names the method and its sparsity only).
+//
+// Reading: query blocks are the 256-row attention work items, key blocks
+// the 64-key tiles, both aligned to the segment start. A query block keeps
+// keep(n) = max(1, n - floor(n p / 1000)) of its segment's n key blocks
+// (p = sparsity in thousandths): those with the highest logit between the
+// block means of the INT8 codes,
+//   score_j = ((sum over the query block's 64-row blocks b, ascending, of
+//               sq_b * I_bj) * sk_j) / n_j,
+// I_bj the exact integer dot product of the code sums of Q block b and key
+// block j, sq / sk the stored fp32 scales, n_j the keys in block j; each
+// operation one float64 rounding in this order (no contraction), equal
+// scores going to the lower block index. The kept indices are written in
+// ascending order, the order the attention kernel visits them.
+//
+// One workgroup of 256 threads per work item: the query block's code sums
+// (up to 4 x 128) go to LDS as doubles; each thread scores key blocks j =
+// tid, tid + 256, ..., reading the key block's 128 code sums (512 B, from
+// L2: every query block of the head reads the same sums); the (score, j)
+// pairs are sorted in LDS by a bitonic network, the first keep(n) marked,
+// and the marks compacted in ascending j by a workgroup scan.
+#include "h3_common.hpp"
+#include "h3_internal.hpp"
+
+namespace h3 {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBN = 64;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ bool before(double ka, int ia, double kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+__global__ __launch_bounds__(kThreads) void bsa_select_kernel(
+    const int32_t* __restrict__ qsum, const int32_t* __restrict__ ksum, const float* __restrict__ qsc,
+    const float* __restrict__ ksc, const int32_t* __restrict__ cu, const int32_t* __restrict__ tb,
+    const int4* __restrict__ items, int num_seqs, int total_tokens, int num_heads, int64_t num_tiles,
+    int sp_permille, int64_t list_stride, int32_t* __restrict__ lists) {
+#pragma clang fp contract(off)
+    __shared__ __attribute__((aligned(16))) double pq[4][kD];
+    __shared__ double key[kBsaMaxKeyBlocks];
+    __shared__ uint16_t idx[kBsaMaxKeyBlocks];
+    __shared__ uint8_t mark[kBsaMaxKeyBlocks];
+    __shared__ int32_t part[kThreads];
+
+    const int tid = threadIdx.x;
+    const int4 it = items[blockIdx.x];
+    const int head = it.x, seg = it.y, q0 = it.z, qlen = it.w;
+    if (seg < 0 || seg >= num_seqs || head < 0 || head >= num_heads) return;
+    const int kv0 = max(0, cu[seg]), kv1 = min(total_tokens, cu[seg + 1]);
+    if (qlen <= 0 || q0 < kv0 || q0 + qlen > kv1 || (q0 - kv0) % (4 * kBN) != 0) return;
+    const int len = kv1 - kv0;
+    const int n = (len + kBN - 1) / kBN;
+    if (n > kBsaMaxKeyBlocks) return;                 // rejected on the host
+    const int keep = max(1, n - static_cast<int>((static_cast<int64_t>(n) * sp_permille) / 1000));
+    const int tbs = tb[seg];
+    const int t0 = tbs + (q0 - kv0) / kBN;            // first 64-row block of the query block
+    const int nb = (qlen + kBN - 1) / kBN;
+
+    for (int i = tid; i < nb * kD; i += kThreads)
+        pq[i / kD][i % kD] = static_cast<double>(
+            qsum[(static_cast<int64_t>(t0 + i / kD) * num_heads + head) * kD + i % kD]);
+    double sq[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        sq[b] = b < nb ? static_cast<double>(qsc[static_cast<int64_t>(t0 + b) * num_heads + head]) : 0.0;
+    int npow = 1;
+    while (npow < n) npow <<= 1;
+    for (int j = tid; j < npow; j += kThreads) mark[j] = 0;
+    __syncthreads();
+
+    const int32_t* kbase = ksum + (static_cast<int64_t>(head) * num_tiles + tbs) * kD;
+    for (int j = tid; j < npow; j += kThreads) {
+        double score = -INFINITY;
+        if (j < n) {
+            const int4* kp = reinterpret_cast<const int4*>(kbase + static_cast<int64_t>(j) * kD);
+            // products and partial sums are integers below 2^53: exact in any order
+            double dot[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+            for (int c = 0; c < kD / 4; ++c) {
+                const int4 kv = kp[c];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const double2 p01 = *reinterpret_cast<const double2*>(&pq[b][4 * c]);
+                    const double2 p23 = *reinterpret_cast<const double2*>(&pq[b][4 * c + 2]);
+                    dot[b] = fma(p01.x, static_cast<double>(kv.x), dot[b]);
+                    dot[b] = fma(p01.y, static_cast<double>(kv.y), dot[b]);
+                    dot[b] = fma(p23.x, static_cast<double>(kv.z), dot[b]);
+                    dot[b] = fma(p23.y, static_cast<double>(kv.w), dot[b]);
+                }
+            }
+            double acc = 0.0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (b < nb) acc = acc + sq[b] * dot[b];
+            const int nj = min(kBN, len - kBN * j);
+            score = (acc * static_cast<double>(ksc[static_cast<int64_t>(tbs + j) * num_heads + head])) /
+                    static_cast<double>(nj);
+        }
+        key[j] = score;
+        idx[j] = static_cast<uint16_t>(j);          // pads (j >= n) sort after every real block
+    }
+    __syncthreads();
+
+    // bitonic sort of npow (score, index) pairs into "before" order
+    for (int size = 2; size <= npow; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < npow / 2; i += kThreads) {
+                const int lo = 2 * stride * (i / stride) + (i % stride);
+                const int hi = lo + stride;
+                const bool up = (lo & size) == 0;
+                const double klo = key[lo], khi = key[hi];
+                const int ilo = idx[lo], ihi = idx[hi];
+                if (before(khi, ihi, klo, ilo) == up) {
+                    key[lo] = khi;
+                    key[hi] = klo;
+                    idx[lo] = static_cast<uint16_t>(ihi);
+                    idx[hi] = static_cast<uint16_t>(ilo);
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int r = tid; r < keep; r += kThreads) mark[idx[r]] = 1;
+    __syncthreads();
+
+    // ascending compaction: thread tid owns blocks [tid * per, (tid + 1) * per)
+    const int per = (n + kThreads - 1) / kThreads;
+    const int j0 = min(n, tid * per), j1 = min(n, j0 + per);
+    int cnt = 0;
+    for (int j = j0; j < j1; ++j) cnt += mark[j];
+    part[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        const int add = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += add;
+        __syncthreads();
+    }
+    int pos = part[tid] - cnt;
+    int32_t* out = lists + (static_cast<int64_t>(head) * num_tiles + t0) * list_stride;
+    for (int j = j0; j < j1; ++j)
+        if (mark[j]) out[pos++] = j;
+}
+
+}  // namespace
+
+hipError_t launch_bsa_select(const int32_t* qsum, const int32_t* ksum, const float* qsc, const float* ksc,
+                             const int32_t* cu, const int32_t* tb, const int32_t* items, int64_t num_items,
+                             int num_seqs, int total_tokens, int num_heads, int64_t num_tiles,
+                             int sp_permille, int64_t list_stride, int32_t* lists, hipStream_t stream) {
+    if (num_items <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bsa_select_kernel, dim3(static_cast<unsigned>(num_items)), dim3(kThreads), 0, stream,
+                       qsum, ksum, qsc, ksc, cu, tb, reinterpret_cast<const int4*>(items), num_seqs,
+                       total_tokens, num_heads, num_tiles, sp_permille, list_stride, lists);
+    return hipGetLastError();
+}
+
+}  // namespace h3

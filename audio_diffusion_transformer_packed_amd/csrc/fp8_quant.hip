@@ -35,6 +35,11 @@
 //                           sits at position 32g + 16b + 4i + e, the order
 //                           in which the attention kernel's lanes hold P;
 //   q_scale, k_scale [T, H];  v_scale [B, H, 128].
+// With code sums requested (the block-sparse path) Q and K are INT8 instead:
+// scale = amax / 127 (1 when amax is 0), code = round-half-even(127 x /
+// amax) in [-127, 127], same layouts, plus per (tile, head) the per-channel
+// sums of the Q codes (qsum [T, H, 128]) and of the K codes (ksum [H, T,
+// 128]), the block means the block selection ranks by.
 // All HBM-bound: q, k, v are streamed once by quant_qk_kernel and v once
 // more by quant_v_kernel (V's scale needs the whole segment first), with
 // 16-byte nontemporal loads. Work items are ordered head-fastest, so the
@@ -158,16 +163,43 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ base, int
     }
 }
 
+// INT8 code of x in a block of maximum magnitude amax: round-half-even of
+// 127 x / amax. 127 x is exact for bf16 x and the IEEE division rounds the
+// quotient once: an exact half-integer quotient stays exact (and rounds to
+// even), any other is at least 2^-16 (relative) from one and stays on its
+// side. amax == 0 means every x of the block is 0.
+__device__ __forceinline__ int i8_code(float x, float amax) {
+    return amax > 0.f ? static_cast<int>(__builtin_rintf((127.0f * x) / amax)) : 0;
+}
+
+// INT8 codes of a bf16 chunk (byte j = value j), added to the per-channel
+// code sums s[0..7].
+__device__ __forceinline__ u32x2 i8_codes8(uint4 raw, float amax, int (&s)[8]) {
+    u32x2 out = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int c = i8_code(chunk_val(raw, j), amax);
+        s[j] += c;
+        out[j >> 2] |= (static_cast<uint32_t>(c) & 0xffu) << (8 * (j & 3));
+    }
+    return out;
+}
+
 // One workgroup per (key tile, head), head-fastest: Q and K codes + block
 // scales, and the tile's channel amax of V (reduced per segment afterwards).
+// I8: Q and K as INT8 (scale amax / 127) instead of e4m3, plus the tile's
+// per-channel code sums of Q (qsum [T, H, 128]) and K (ksum [H, T, 128]).
+template <bool I8>
 __global__ __launch_bounds__(256) void quant_qk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int64_t qs, int64_t ks, int64_t vs, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ tb, int num_seqs, int num_heads, int64_t num_tiles,
     uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, float* __restrict__ qsc,
-    float* __restrict__ ksc, float* __restrict__ vpart) {
+    float* __restrict__ ksc, float* __restrict__ vpart, int32_t* __restrict__ qsum,
+    int32_t* __restrict__ ksum) {
     __shared__ float red[2][4];
     __shared__ float vred[4][kD];
+    __shared__ int32_t isum[I8 ? 2 : 1][4][I8 ? kD : 1];
     const int tile = static_cast<int>(blockIdx.x / static_cast<unsigned>(num_heads));
     const int h = static_cast<int>(blockIdx.x - static_cast<unsigned>(tile) * num_heads);
     int seg, t0, rows;
@@ -211,21 +243,62 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
     __syncthreads();
     const float amax_q = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     const float amax_k = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-    const Fp8Mul mulq = fp8_mul_of(amax_q), mulk = fp8_mul_of(amax_k);
     uint8_t* kt = k8 + ((static_cast<int64_t>(h) * num_tiles + tile) * kTB) * kD;
+    if constexpr (I8) {
+        // rows past the segment end load as 0, so they add nothing to the sums
+        int sq[8] = {0, 0, 0, 0, 0, 0, 0, 0}, sk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;
-        const int tok = c >> 4, dc = c & 15;
-        if (tok < rows)
-            __builtin_nontemporal_store(codes8(xq[i], mulq),
-                                        reinterpret_cast<u32x2*>(q8 + (t0 + tok) * row_bytes + h * kD + 8 * dc));
-        // K rows past the segment end are 0
-        __builtin_nontemporal_store(codes8(xk[i], mulk), reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc));
-    }
-    if (tid == 0) {
-        qsc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_q);
-        ksc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_k);
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;
+            const int tok = c >> 4, dc = c & 15;
+            const u32x2 cq = i8_codes8(xq[i], amax_q, sq);
+            const u32x2 ck = i8_codes8(xk[i], amax_k, sk);
+            if (tok < rows)
+                __builtin_nontemporal_store(cq, reinterpret_cast<u32x2*>(q8 + (t0 + tok) * row_bytes + h * kD + 8 * dc));
+            __builtin_nontemporal_store(ck, reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc));
+        }
+        // channel chunk tid % 16 is shared with lanes tid ^ 16 and tid ^ 32
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            sq[j] += __shfl_xor(sq[j], 16, 64);
+            sq[j] += __shfl_xor(sq[j], 32, 64);
+            sk[j] += __shfl_xor(sk[j], 16, 64);
+            sk[j] += __shfl_xor(sk[j], 32, 64);
+        }
+        if ((tid & 63) < 16) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                isum[0][wave][8 * (tid & 15) + j] = sq[j];
+                isum[1][wave][8 * (tid & 15) + j] = sk[j];
+            }
+        }
+        __syncthreads();
+        const int which = tid >> 7, d = tid & 127;
+        const int32_t tot = isum[which][0][d] + isum[which][1][d] + isum[which][2][d] + isum[which][3][d];
+        if (which == 0)
+            qsum[(static_cast<int64_t>(tile) * num_heads + h) * kD + d] = tot;
+        else
+            ksum[(static_cast<int64_t>(h) * num_tiles + tile) * kD + d] = tot;
+        if (tid == 0) {
+            qsc[static_cast<int64_t>(tile) * num_heads + h] = amax_q > 0.f ? amax_q / 127.0f : 1.0f;
+            ksc[static_cast<int64_t>(tile) * num_heads + h] = amax_k > 0.f ? amax_k / 127.0f : 1.0f;
+        }
+    } else {
+        const Fp8Mul mulq = fp8_mul_of(amax_q), mulk = fp8_mul_of(amax_k);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;
+            const int tok = c >> 4, dc = c & 15;
+            if (tok < rows)
+                __builtin_nontemporal_store(codes8(xq[i], mulq),
+                                            reinterpret_cast<u32x2*>(q8 + (t0 + tok) * row_bytes + h * kD + 8 * dc));
+            // K rows past the segment end are 0
+            __builtin_nontemporal_store(codes8(xk[i], mulk), reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc));
+        }
+        if (tid == 0) {
+            qsc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_q);
+            ksc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_k);
+        }
     }
     if (tid < kD) {
         const float a = fmaxf(fmaxf(vred[0][tid], vred[1][tid]), fmaxf(vred[2][tid], vred[3][tid]));
@@ -323,7 +396,7 @@ hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint1
                                int64_t ks, int64_t vs, const int32_t* cu, int num_seqs,
                                int num_heads, int64_t num_tiles, uint8_t* q8, uint8_t* k8,
                                uint8_t* v8t, float* qsc, float* ksc, float* vsc, void* workspace,
-                               hipStream_t stream) {
+                               hipStream_t stream, int32_t* qsum, int32_t* ksum) {
     if (num_seqs <= 0 || num_tiles <= 0) return hipSuccess;
     if (num_tiles * num_heads > 0xffffffffll) return hipErrorInvalidValue;   // 1-D grid of (tile, head)
     int32_t* tb = static_cast<int32_t*>(workspace);
@@ -333,9 +406,12 @@ hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint1
     float* vpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + tb_bytes + va_bytes);
     hipLaunchKernelGGL(tile64_scan_kernel, dim3(1), dim3(1024), 0, stream, cu, num_seqs, tb);
     const unsigned items = static_cast<unsigned>(num_tiles * num_heads);
-    hipLaunchKernelGGL(quant_qk_kernel, dim3(items), dim3(256), 0, stream,
-                       q, k, v, qs, ks, vs, cu, tb, num_seqs, num_heads, num_tiles, q8, k8, qsc, ksc,
-                       vpart);
+    if (qsum != nullptr)
+        hipLaunchKernelGGL(quant_qk_kernel<true>, dim3(items), dim3(256), 0, stream, q, k, v, qs, ks, vs,
+                           cu, tb, num_seqs, num_heads, num_tiles, q8, k8, qsc, ksc, vpart, qsum, ksum);
+    else
+        hipLaunchKernelGGL(quant_qk_kernel<false>, dim3(items), dim3(256), 0, stream, q, k, v, qs, ks, vs,
+                           cu, tb, num_seqs, num_heads, num_tiles, q8, k8, qsc, ksc, vpart, qsum, ksum);
     hipLaunchKernelGGL(vscale_kernel, dim3(num_seqs, num_heads * kD / 32), dim3(1024), 0, stream,
                        vpart, tb, num_heads, vsc, vamax);
     hipLaunchKernelGGL(quant_v_kernel, dim3(items), dim3(64), 0, stream, v, vs, cu, tb, num_seqs,

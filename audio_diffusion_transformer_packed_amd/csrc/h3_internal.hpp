@@ -29,7 +29,7 @@ hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint1
                                int64_t ks, int64_t vs, const int32_t* cu, int num_seqs,
                                int num_heads, int64_t num_tiles, uint8_t* q8, uint8_t* k8,
                                uint8_t* v8t, float* qsc, float* ksc, float* vsc, void* workspace,
-                               hipStream_t stream);
+                               hipStream_t stream, int32_t* qsum = nullptr, int32_t* ksum = nullptr);
 
 // fp8 attention over the quantised codes (attn_fp8.hip)
 bool fp8_attention_available();
@@ -40,6 +40,22 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int64_t num_items, int num_seqs, int total_tokens, int num_heads,
                            int head_dim, float softmax_scale, int skip, float skip_threshold,
                            int32_t* skip_counts, void* scratch, hipStream_t stream);
+
+// Block-sparse attention, INT8 Q/K + FP8 V (bsa_select.hip, attn_fp8.hip).
+// Lists: int32 [H, T, list_stride], row (head, first 64-token block of a
+// 256-row query block) holds the kept key blocks of that query block.
+constexpr int kBsaMaxKeyBlocks = 4096;          // 64-key blocks per segment
+hipError_t launch_bsa_select(const int32_t* qsum, const int32_t* ksum, const float* qsc, const float* ksc,
+                             const int32_t* cu, const int32_t* tb, const int32_t* items, int64_t num_items,
+                             int num_seqs, int total_tokens, int num_heads, int64_t num_tiles,
+                             int sp_permille, int64_t list_stride, int32_t* lists, hipStream_t stream);
+size_t bsa_scratch_bytes(int num_seqs, int total_tokens, int num_heads, int64_t list_stride);
+hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                           int64_t qs, int64_t ks, int64_t vs, int64_t os, const int32_t* cu,
+                           const int32_t* cu_host, const int32_t* items, int64_t num_items,
+                           int num_seqs, int total_tokens, int num_heads, float softmax_scale,
+                           int sp_permille, int64_t list_stride, int32_t* lists_out, void* scratch,
+                           hipStream_t stream);
 
 // Q/K RMSNorm + 3D RoPE (qk_norm_rope.hip)
 hipError_t launch_qk_norm_rope(uint16_t* q, uint16_t* k, int64_t qs, int64_t ks,

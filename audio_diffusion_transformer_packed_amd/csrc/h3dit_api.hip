@@ -6,6 +6,8 @@
 // caller's stream without synchronising. The library's only state is the
 // thread-local error message.
 #include <math.h>
+
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -305,6 +307,113 @@ H3_API h3_status h3_attn_varlen(const void* q, const void* k, const void* v, voi
     return run_attention(q, k, v, out, q_tok_stride, k_tok_stride, v_tok_stride, o_tok_stride,
                          cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens, num_heads,
                          head_dim, opts, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+// ---- block-sparse attention, INT8 Q/K + FP8 V ----
+
+namespace {
+
+bool sparsity_ok(float sparsity) { return sparsity >= 0.f && sparsity < 1.f; }
+int sparsity_permille(float sparsity) {
+    return static_cast<int>(std::nearbyint(1000.0 * static_cast<double>(sparsity)));
+}
+int64_t bsa_keep(int64_t n, int permille) {
+    return n > 0 ? std::max<int64_t>(1, n - (n * permille) / 1000) : 0;
+}
+int64_t bsa_list_stride(const int32_t* cu, int32_t num_seqs, int permille) {
+    int64_t nmax = 0;
+    for (int32_t s = 0; s < num_seqs; ++s)
+        nmax = std::max<int64_t>(nmax, (cu[s + 1] - cu[s] + H3_FP8_QK_BLOCK - 1) / H3_FP8_QK_BLOCK);
+    return std::max<int64_t>(1, bsa_keep(nmax, permille));
+}
+// keep(n) does not decrease with n, so the longest possible segment bounds the stride
+int64_t bsa_list_stride_bound(int32_t total_tokens, int permille) {
+    return std::max<int64_t>(1, bsa_keep((static_cast<int64_t>(total_tokens) + H3_FP8_QK_BLOCK - 1) /
+                                             H3_FP8_QK_BLOCK, permille));
+}
+
+}  // namespace
+
+H3_API h3_status h3_attn_block_sparse_list_stride(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                  float sparsity, int64_t* stride_out) {
+    if (stride_out == nullptr) return fail(H3_ERR_INVALID_ARGUMENT, "stride_out is NULL");
+    if (cu_seqlens_host == nullptr || num_seqs < 0)
+        return fail(H3_ERR_INVALID_ARGUMENT, "bad cu_seqlens_host / num_seqs");
+    if (!sparsity_ok(sparsity)) return fail(H3_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1)");
+    h3_status st = check_cu(cu_seqlens_host, num_seqs, cu_seqlens_host[num_seqs]);
+    if (st != H3_OK) return st;
+    *stride_out = bsa_list_stride(cu_seqlens_host, num_seqs, sparsity_permille(sparsity));
+    return ok();
+}
+
+H3_API size_t h3_attn_block_sparse_workspace_size(int32_t num_seqs, int32_t total_tokens,
+                                                  int32_t num_heads, int32_t head_dim, float sparsity) {
+    if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || head_dim != 128 || !sparsity_ok(sparsity))
+        return 0;
+    const int64_t stride = bsa_list_stride_bound(total_tokens, sparsity_permille(sparsity));
+    return attn_plan(num_seqs, total_tokens, num_heads, head_dim, H3_ATTN_BF16).total +
+           align_up(h3::bsa_scratch_bytes(num_seqs, total_tokens, num_heads, stride));
+}
+
+H3_API h3_status h3_attn_block_sparse(const void* q, const void* k, const void* v, void* out,
+                                      int64_t q_tok_stride, int64_t k_tok_stride,
+                                      int64_t v_tok_stride, int64_t o_tok_stride,
+                                      const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                      int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                      int32_t head_dim, float softmax_scale, float sparsity,
+                                      int32_t* kv_block_lists, void* workspace,
+                                      size_t workspace_bytes, void* hip_stream) {
+    h3_status st = check_cu(cu_seqlens_host, num_seqs, total_tokens);
+    if (st != H3_OK) return st;
+    if (num_heads <= 0) return fail(H3_ERR_INVALID_ARGUMENT, "num_heads=%d <= 0", num_heads);
+    if (head_dim != 128)
+        return fail(H3_ERR_UNSUPPORTED, "block-sparse attention needs head_dim 128 (got %d)", head_dim);
+    if (!sparsity_ok(sparsity)) return fail(H3_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1)");
+    if (!(softmax_scale >= 0.f) || std::isinf(softmax_scale))
+        return fail(H3_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+    for (int32_t s = 0; s < num_seqs; ++s)
+        if (cu_seqlens_host[s + 1] - cu_seqlens_host[s] > h3::kBsaMaxKeyBlocks * H3_FP8_QK_BLOCK)
+            return fail(H3_ERR_UNSUPPORTED, "segment %d has %d tokens; block-sparse attention takes at most %d",
+                        s, cu_seqlens_host[s + 1] - cu_seqlens_host[s], h3::kBsaMaxKeyBlocks * H3_FP8_QK_BLOCK);
+    if (total_tokens == 0) return ok();
+    if (!q || !k || !v || !out || !cu_seqlens_dev)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
+    const int64_t row = static_cast<int64_t>(num_heads) * head_dim;
+    if (q_tok_stride < row || k_tok_stride < row || v_tok_stride < row || o_tok_stride < row)
+        return fail(H3_ERR_INVALID_ARGUMENT, "token strides must be >= num_heads * head_dim = %lld",
+                    (long long)row);
+    if ((q_tok_stride | k_tok_stride | v_tok_stride | o_tok_stride) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+         reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out)) & 15)
+        return fail(H3_ERR_UNSUPPORTED, "q/k/v/out must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(kv_block_lists) & 3)
+        return fail(H3_ERR_INVALID_ARGUMENT, "kv_block_lists must be 4-byte aligned");
+    const size_t need = h3_attn_block_sparse_workspace_size(num_seqs, total_tokens, num_heads, head_dim, sparsity);
+    if (workspace_bytes < need || workspace == nullptr)
+        return fail(H3_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+        return fail(H3_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const int permille = sparsity_permille(sparsity);
+    const AttnPlan plan = attn_plan(num_seqs, total_tokens, num_heads, head_dim, H3_ATTN_BF16);
+    const int64_t n_items = count_items(cu_seqlens_host, num_seqs, num_heads, H3_ATTN_BLOCK_M);
+    if (n_items == 0) return ok();
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* items = reinterpret_cast<int32_t*>(ws);
+    hipError_t e = h3::launch_bookkeeping(cu_seqlens_dev, num_seqs, total_tokens, num_heads,
+                                          H3_ATTN_BLOCK_M, nullptr, nullptr, items, plan.items_cap,
+                                          ws + plan.items_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "bookkeeping launch");
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+    e = h3::launch_attn_bsa(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), q_tok_stride,
+                            k_tok_stride, v_tok_stride, o_tok_stride, cu_seqlens_dev, cu_seqlens_host,
+                            items, n_items, num_seqs, total_tokens, num_heads, scale, permille,
+                            bsa_list_stride(cu_seqlens_host, num_seqs, permille), kv_block_lists,
+                            ws + plan.total, stream);
+    if (e != hipSuccess) return hip_fail(e, "block-sparse attention launch");
+    return ok();
 }
 
 H3_API h3_status h3_fp8_num_tiles(const int32_t* cu_seqlens_host, int32_t num_seqs,

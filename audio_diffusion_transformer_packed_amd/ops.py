@@ -196,6 +196,57 @@ def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: 
     return out
 
 
+def attn_block_sparse_list_stride(cu_host, sparsity: float) -> int:
+    """Entries per list row of attn_block_sparse's kept-block lists."""
+    cu = _host_cu(cu_host)
+    stride = C.c_int64(0)
+    check(lib().h3_attn_block_sparse_list_stride(cu.ctypes.data_as(C.c_void_p), cu.size - 1,
+                                                 float(sparsity), C.byref(stride)))
+    return stride.value
+
+
+def attn_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                      cu_host, sparsity: float = 0.8, softmax_scale: float = 0.0,
+                      out: Optional[torch.Tensor] = None, kv_block_lists: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-sparse varlen attention, INT8 Q/K + FP8 V (h3_attn_block_sparse);
+    q, k, v, out [N, H, 128] bf16. kv_block_lists, if given, is int32
+    [H, T, attn_block_sparse_list_stride(cu_host, sparsity)] and receives
+    the kept key blocks of each (head, 256-row query block)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, BF16, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    n, heads, d = q.shape
+    if out is None:
+        out = torch.empty((n, heads, d), dtype=BF16, device=dev)
+    _need(out, "out", BF16, dev)
+    strides = [_token_view(t, nm, heads, d) for nm, t in (("q", q), ("k", k), ("v", v), ("out", out))]
+    cu = _host_cu(cu_host)
+    if kv_block_lists is not None:
+        _need(kv_block_lists, "kv_block_lists", torch.int32, dev)
+        want = (heads, fp8_num_tiles(cu), attn_block_sparse_list_stride(cu, sparsity))
+        if tuple(kv_block_lists.shape) != want or not kv_block_lists.is_contiguous():
+            raise ValueError(f"kv_block_lists must be a contiguous int32 tensor of shape {want}")
+    nbytes = lib().h3_attn_block_sparse_workspace_size(cu.size - 1, n, heads, d, float(sparsity))
+    ws = _workspace(nbytes, dev, workspace)
+    check(lib().h3_attn_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), *strides, _ptr(cu_seqlens),
+                                     cu.ctypes.data_as(C.c_void_p), cu.size - 1, n, heads, d,
+                                     float(softmax_scale), float(sparsity),
+                                     None if kv_block_lists is None else _ptr(kv_block_lists),
+                                     _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def dense_attention_step(step: int, num_steps: int, start_steps: int, end_steps: int) -> bool:
+    """Whether denoising step `step` (0-based) runs dense attention under the
+    block-sparse configuration: the first start_steps and the last end_steps
+    of num_steps do (the dense-fallback window, counts not indices)."""
+    if not 0 <= step < num_steps or start_steps < 0 or end_steps < 0:
+        raise ValueError("step, start_steps or end_steps out of range")
+    return step < start_steps or step >= num_steps - end_steps
+
+
 # --------------------------------------------------------------------------
 # Per-block fused operators
 # --------------------------------------------------------------------------

@@ -201,6 +201,60 @@ H3_API h3_status h3_fp8_quantize(const void* q, const void* k, const void* v,
                                  size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Block-sparse varlen attention with INT8 Q/K and FP8 V ("MiniMax H3 on
+ * Ascend 950PR / 950DT", section "Recommended lossy configuration (Ascend
+ * 950PR / 950DT)": EQBSA, block-sparse attention with Q and K in INT8 and V
+ * in FP8, sparsity 0.8; section "Tuning the EQBSA dense-fallback window":
+ * whole denoising steps at the start and end run dense attention instead,
+ * which is the caller's choice per call).
+ *
+ * The page gives the method's name, precisions and sparsity only; this
+ * implements one reading of the rest:
+ *  - Q and K: INT8, one scale per (head, 64-token block aligned to the
+ *    segment start), scale = fp32(amax / 127) (1 if amax == 0), code =
+ *    round-half-even(127 x / amax). V: e4m3 per (segment, head, channel) as
+ *    in the fp8 path of h3_attn_varlen.
+ *  - Query blocks of 256 rows and key blocks of 64 keys, aligned to the
+ *    segment start. A query block keeps keep(n) = max(1, n - floor(n p /
+ *    1000)) of its segment's n key blocks, p = round(1000 sparsity): those
+ *    with the highest score_j = ((sum over its 64-row blocks b, ascending,
+ *    of sq_b I_bj) sk_j) / n_j, I_bj the integer dot product of the INT8
+ *    code sums of Q block b and key block j, sq/sk the scales, n_j the keys
+ *    in block j, each step one float64 rounding in this order; equal scores
+ *    go to the lower block index.
+ *  - Attention over the kept blocks only, in ascending order: S = (Q8 K8)
+ *    sq sk scale, online softmax, P = e4m3(448 p), l from the unrounded p,
+ *    O = (sum P V8) sv / (448 l); fp32 accumulation, bf16 output.
+ * q, k, v, out, strides, cu_seqlens as for h3_attn_varlen; head_dim must be
+ * 128; a segment may hold at most 4096 * 64 = 262144 tokens
+ * (H3_ERR_UNSUPPORTED otherwise). sparsity in [0, 1) (0: every block kept,
+ * the dense INT8/FP8 attention); softmax_scale 0 means 1 / sqrt(128).
+ * kv_block_lists (optional, device int32 [num_heads, T, list_stride], T =
+ * h3_fp8_num_tiles, list_stride = h3_attn_block_sparse_list_stride):
+ * receives, for each head h and 256-row query block whose first 64-token
+ * block is tile t, the kept key-block indices (within the segment) in
+ * ascending order at [h, t, 0 .. keep); other entries are not written.
+ * The workspace (h3_attn_block_sparse_workspace_size bytes, 256-byte
+ * aligned) also holds the INT8 codes, code sums and, without
+ * kv_block_lists, the lists. Errors leave out untouched.
+ * ---------------------------------------------------------------------- */
+H3_API h3_status h3_attn_block_sparse_list_stride(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                  float sparsity, int64_t* stride_out);
+/* 0 for unsupported sizes (head_dim != 128, sparsity outside [0, 1)). */
+H3_API size_t h3_attn_block_sparse_workspace_size(int32_t num_seqs, int32_t total_tokens,
+                                                  int32_t num_heads, int32_t head_dim,
+                                                  float sparsity);
+H3_API h3_status h3_attn_block_sparse(const void* q, const void* k, const void* v, void* out,
+                                      int64_t q_tok_stride, int64_t k_tok_stride,
+                                      int64_t v_tok_stride, int64_t o_tok_stride,
+                                      const int32_t* cu_seqlens_dev,
+                                      const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                      int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                      float softmax_scale, float sparsity,
+                                      int32_t* kv_block_lists, void* workspace,
+                                      size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * Fused Q/K RMSNorm + 3D RoPE, in place ([FastH3-ZH] "融合 DiT 算子": the
  * Q/K normalisation is merged with RoPE).
  *

@@ -240,3 +240,42 @@ def test_fp8_quantize_argument_errors(lib):
     assert call(n=11) == L.H3_ERR_INVALID_ARGUMENT            # cu[B] != total_tokens
     zcu, zcup = _cu([0, 0])
     assert call(n=0, cu_p=zcup) == L.H3_OK                    # nothing to do, nothing launched
+
+
+def _bsa(lib, cu, n, d=128, heads=2, sparsity=0.8, ws_bytes=1 << 30, lists=0):
+    cu_arr = (C.c_int32 * len(cu))(*cu)
+    return lib.h3_attn_block_sparse(C.c_void_p(0x1000), C.c_void_p(0x2000), C.c_void_p(0x3000),
+                                    C.c_void_p(0x4000), heads * d, heads * d, heads * d, heads * d,
+                                    C.c_void_p(0x5000), cu_arr, len(cu) - 1, n, heads, d,
+                                    C.c_float(0.0), C.c_float(sparsity), C.c_void_p(lists),
+                                    C.c_void_p(0x10000), ws_bytes, None)
+
+
+def test_block_sparse_argument_errors_and_sizes(lib):
+    """Host-side checks of the block-sparse entry points (no GPU call is
+    reached: every case fails validation first)."""
+    assert _bsa(lib, [0, 10], 10, d=64) == L.H3_ERR_UNSUPPORTED
+    assert _bsa(lib, [0, 10], 10, sparsity=1.0) == L.H3_ERR_INVALID_ARGUMENT
+    assert _bsa(lib, [0, 10], 10, sparsity=-0.1) == L.H3_ERR_INVALID_ARGUMENT
+    assert _bsa(lib, [0, 10], 10, ws_bytes=0) == L.H3_ERR_WORKSPACE_TOO_SMALL
+    assert _bsa(lib, [0, 10], 10, lists=0x1002) == L.H3_ERR_INVALID_ARGUMENT
+    big = 4096 * 64 + 1
+    assert _bsa(lib, [0, big], big, ws_bytes=1 << 40) == L.H3_ERR_UNSUPPORTED
+    assert _bsa(lib, [0, 5, 3], 3) == L.H3_ERR_INVALID_ARGUMENT
+    ws = lib.h3_attn_block_sparse_workspace_size
+    assert ws(1, 1000, 2, 64, C.c_float(0.8)) == 0 and ws(1, 1000, 2, 128, C.c_float(1.0)) == 0
+    assert ws(1, 57960, 24, 128, C.c_float(0.8)) > ws(1, 57960, 24, 128, C.c_float(0.9)) > 0
+    stride = C.c_int64(0)
+    cu = (C.c_int32 * 4)(0, 640, 640, 6400)                    # 10 and 90 key blocks
+    assert lib.h3_attn_block_sparse_list_stride(cu, 3, C.c_float(0.8), C.byref(stride)) == L.H3_OK
+    assert stride.value == 18                                  # 90 - floor(72.0)
+    assert lib.h3_attn_block_sparse_list_stride(cu, 3, C.c_float(0.0), C.byref(stride)) == L.H3_OK
+    assert stride.value == 90
+
+
+def test_dense_fallback_helper_matches_oracle():
+    from audio_diffusion_transformer_packed_amd import ops
+    import oracle
+    for start, end in [(8, 13), (8, 12), (0, 13), (0, 0), (50, 0)]:
+        for s in range(50):
+            assert ops.dense_attention_step(s, 50, start, end) == oracle.dense_fallback(s, 50, start, end)
