@@ -99,6 +99,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     // K stage 0, K stage 1, V stage 0, V stage 1
     __shared__ __attribute__((aligned(1024))) char smem[2 * kKT + 2 * kVT];
     __shared__ int32_t wskip[kWaves];
+    // BSA: kept tiles and their K scales, staged once (no dependent global
+    // loads inside the tile loop)
+    __shared__ int32_t s_tile[BSA ? kBsaMaxKeyBlocks : 1];
+    __shared__ float s_sk[BSA ? kBsaMaxKeyBlocks : 1];
 
     const int tid = threadIdx.x;
     // work-item fields and segment bounds are workgroup-uniform: keep them in
@@ -121,15 +125,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const int keys_left = len - (ntiles - 1) * kBN;
     const int tbs = __builtin_amdgcn_readfirstlane(tb[seg]);
     int nsel = ntiles;                  // key tiles this work item visits
-    const int32_t* lst = lists;
     if constexpr (BSA) {
         nsel = max(1, ntiles - static_cast<int>((static_cast<int64_t>(ntiles) * sp_permille) / 1000));
-        lst = lists + (static_cast<int64_t>(head) * num_tiles + tbs + (q0 - kv0) / kBN) * list_stride;
+        nsel = min(nsel, kBsaMaxKeyBlocks);
+        const int32_t* lst = lists + (static_cast<int64_t>(head) * num_tiles + tbs + (q0 - kv0) / kBN) * list_stride;
+        // clamped into the segment, so no list content can address outside it
+        for (int i = tid; i < nsel; i += kThreads) {
+            const int t = min(max(lst[i], 0), ntiles - 1);
+            s_tile[i] = t;
+            s_sk[i] = ksc[static_cast<int64_t>(tbs + t) * num_heads + head];
+        }
+        __syncthreads();
     }
-    // key tile of step u: the u-th kept block (clamped into the segment, so
-    // no list content can address outside it), or tile u
+    // key tile of step u: the u-th kept block, or tile u
     auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
-        if constexpr (BSA) return min(max(__builtin_amdgcn_readfirstlane(lst[u]), 0), ntiles - 1);
+        if constexpr (BSA) return __builtin_amdgcn_readfirstlane(s_tile[u]);
         else return u;
     };
 
@@ -266,7 +276,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     auto softmax_block = [&](int u) __attribute__((always_inline)) {
         if (!wave_active) return;
         const int tile = tile_at(u);
-        const float sk = ksc[static_cast<int64_t>(tbs + tile) * num_heads + head];
+        float sk;
+        if constexpr (BSA) sk = s_sk[u];
+        else sk = ksc[static_cast<int64_t>(tbs + u) * num_heads + head];
         if (tile + 1 == ntiles && keys_left < kBN) {
 #pragma unroll
             for (int b = 0; b < 2; ++b)
@@ -427,7 +439,7 @@ BsaScratch bsa_scratch_layout(int num_seqs, int total_tokens, int num_heads, int
     BsaScratch b;
     b.f = fp8_scratch_layout(num_seqs, total_tokens, num_heads);
     const size_t t = fp8_tiles_upper_bound(num_seqs, total_tokens);
-    const size_t sums = up256(t * num_heads * kD * sizeof(int32_t));
+    const size_t sums = up256(t * num_heads * kD * sizeof(int16_t));
     size_t off = b.f.total;
     b.qsum = off;  off += sums;
     b.ksum = off;  off += sums;
@@ -459,8 +471,8 @@ hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t*
     float* qsc = reinterpret_cast<float*>(base + L.f.qsc);
     float* ksc = reinterpret_cast<float*>(base + L.f.ksc);
     float* vsc = reinterpret_cast<float*>(base + L.f.vsc);
-    int32_t* qsum = reinterpret_cast<int32_t*>(base + L.qsum);
-    int32_t* ksum = reinterpret_cast<int32_t*>(base + L.ksum);
+    int16_t* qsum = reinterpret_cast<int16_t*>(base + L.qsum);
+    int16_t* ksum = reinterpret_cast<int16_t*>(base + L.ksum);
     int32_t* lists = lists_out ? lists_out : reinterpret_cast<int32_t*>(base + L.lists);
     void* ws = base + L.f.ws;
     hipError_t e = launch_fp8_quantize(q, k, v, qs, ks, vs, cu, num_seqs, num_heads, tiles, q8, k8,

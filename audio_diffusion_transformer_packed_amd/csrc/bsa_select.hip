@@ -17,9 +17,9 @@
 // ascending order, the order the attention kernel visits them.
 //
 // One workgroup of 256 threads per work item: the query block's code sums
-// (up to 4 x 128) go to LDS as doubles; each thread scores key blocks j =
-// tid, tid + 256, ..., reading the key block's 128 code sums (512 B, from
-// L2: every query block of the head reads the same sums); the (score, j)
+// (up to 4 x 128, int16) go to LDS; each thread scores four key blocks at a
+// time, j = tid + 256 m, reading each key block's 128 code sums (256 B, from L2:
+// every query block of the head reads the same sums); the (score, j)
 // pairs are sorted in LDS by a bitonic network, the first keep(n) marked,
 // and the marks compacted in ascending j by a workgroup scan.
 #include "h3_common.hpp"
@@ -32,17 +32,24 @@ constexpr int kD = 128;
 constexpr int kBN = 64;
 constexpr int kThreads = 256;
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// acc + a.lo b.lo + a.hi b.hi for two packed int16 pairs, exact (no clamp)
+__device__ __forceinline__ int dot2(uint32_t a, uint32_t b, int acc) {
+    return __builtin_amdgcn_sdot2(__builtin_bit_cast(s16x2, a), __builtin_bit_cast(s16x2, b), acc, false);
+}
+
 __device__ __forceinline__ bool before(double ka, int ia, double kb, int ib) {
     return ka > kb || (ka == kb && ia < ib);
 }
 
 __global__ __launch_bounds__(kThreads) void bsa_select_kernel(
-    const int32_t* __restrict__ qsum, const int32_t* __restrict__ ksum, const float* __restrict__ qsc,
+    const int16_t* __restrict__ qsum, const int16_t* __restrict__ ksum, const float* __restrict__ qsc,
     const float* __restrict__ ksc, const int32_t* __restrict__ cu, const int32_t* __restrict__ tb,
     const int4* __restrict__ items, int num_seqs, int total_tokens, int num_heads, int64_t num_tiles,
     int sp_permille, int64_t list_stride, int32_t* __restrict__ lists) {
 #pragma clang fp contract(off)
-    __shared__ __attribute__((aligned(16))) double pq[4][kD];
+    __shared__ __attribute__((aligned(16))) int16_t pq[4][kD];
     __shared__ double key[kBsaMaxKeyBlocks];
     __shared__ uint16_t idx[kBsaMaxKeyBlocks];
     __shared__ uint8_t mark[kBsaMaxKeyBlocks];
@@ -62,9 +69,9 @@ __global__ __launch_bounds__(kThreads) void bsa_select_kernel(
     const int t0 = tbs + (q0 - kv0) / kBN;            // first 64-row block of the query block
     const int nb = (qlen + kBN - 1) / kBN;
 
-    for (int i = tid; i < nb * kD; i += kThreads)
-        pq[i / kD][i % kD] = static_cast<double>(
-            qsum[(static_cast<int64_t>(t0 + i / kD) * num_heads + head) * kD + i % kD]);
+    for (int i = tid; i < 4 * kD; i += kThreads)
+        pq[i / kD][i % kD] = i / kD < nb ? qsum[(static_cast<int64_t>(t0 + i / kD) * num_heads + head) * kD + i % kD]
+                                         : int16_t{0};
     double sq[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -74,44 +81,77 @@ __global__ __launch_bounds__(kThreads) void bsa_select_kernel(
     for (int j = tid; j < npow; j += kThreads) mark[j] = 0;
     __syncthreads();
 
-    const int32_t* kbase = ksum + (static_cast<int64_t>(head) * num_tiles + tbs) * kD;
-    for (int j = tid; j < npow; j += kThreads) {
-        double score = -INFINITY;
-        if (j < n) {
-            const int4* kp = reinterpret_cast<const int4*>(kbase + static_cast<int64_t>(j) * kD);
-            // products and partial sums are integers below 2^53: exact in any order
-            double dot[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-            for (int c = 0; c < kD / 4; ++c) {
-                const int4 kv = kp[c];
+    // Four key blocks per thread and pass (j = j0 + 256 m), so each LDS read
+    // of the Q sums serves four blocks. |code sum| <= 64 * 127 = 8128 fits
+    // int16: v_dot2_i32_i16 takes two exact products per instruction, 16
+    // products fit an int32 partial (< 1.06e9) and the partials add exactly
+    // in float64 (every value an integer below 2^53).
+    const int16_t* kbase = ksum + (static_cast<int64_t>(head) * num_tiles + tbs) * kD;
+    for (int j0 = tid; j0 < npow; j0 += 4 * kThreads) {
+        const uint4* kp[4];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const double2 p01 = *reinterpret_cast<const double2*>(&pq[b][4 * c]);
-                    const double2 p23 = *reinterpret_cast<const double2*>(&pq[b][4 * c + 2]);
-                    dot[b] = fma(p01.x, static_cast<double>(kv.x), dot[b]);
-                    dot[b] = fma(p01.y, static_cast<double>(kv.y), dot[b]);
-                    dot[b] = fma(p23.x, static_cast<double>(kv.z), dot[b]);
-                    dot[b] = fma(p23.y, static_cast<double>(kv.w), dot[b]);
+        for (int m = 0; m < 4; ++m)
+            kp[m] = reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(min(j0 + kThreads * m, n - 1)) * kD);
+        double dot[4][4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) dot[m][b] = 0.0;
+        for (int c0 = 0; c0 < kD; c0 += 16) {
+            int part[4][4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) part[m][b] = 0;
+#pragma unroll
+            for (int c = c0; c < c0 + 16; c += 8) {
+                uint4 pb[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) pb[b] = *reinterpret_cast<const uint4*>(&pq[b][c]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint4 kv = kp[m][c / 8];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        part[m][b] = dot2(pb[b].x, kv.x, part[m][b]);
+                        part[m][b] = dot2(pb[b].y, kv.y, part[m][b]);
+                        part[m][b] = dot2(pb[b].z, kv.z, part[m][b]);
+                        part[m][b] = dot2(pb[b].w, kv.w, part[m][b]);
+                    }
                 }
             }
-            double acc = 0.0;
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (b < nb) acc = acc + sq[b] * dot[b];
-            const int nj = min(kBN, len - kBN * j);
-            score = (acc * static_cast<double>(ksc[static_cast<int64_t>(tbs + j) * num_heads + head])) /
-                    static_cast<double>(nj);
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) dot[m][b] += static_cast<double>(part[m][b]);
         }
-        key[j] = score;
-        idx[j] = static_cast<uint16_t>(j);          // pads (j >= n) sort after every real block
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int j = j0 + kThreads * m;
+            if (j >= npow) continue;
+            double score = -INFINITY;
+            if (j < n) {
+                double acc = 0.0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    if (b < nb) acc = acc + sq[b] * dot[m][b];
+                const int nj = min(kBN, len - kBN * j);
+                score = (acc * static_cast<double>(ksc[static_cast<int64_t>(tbs + j) * num_heads + head])) /
+                        static_cast<double>(nj);
+            }
+            key[j] = score;
+            idx[j] = static_cast<uint16_t>(j);      // pads (j >= n) sort after every real block
+        }
     }
     __syncthreads();
 
-    // bitonic sort of npow (score, index) pairs into "before" order
+    // bitonic sort of npow (score, index) pairs into "before" order; strides
+    // are powers of two, so the pair index is shifts and masks
     for (int size = 2; size <= npow; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int ls = __builtin_ctz(static_cast<unsigned>(size)) - 1; ls >= 0; --ls) {
+            const int stride = 1 << ls;
             for (int i = tid; i < npow / 2; i += kThreads) {
-                const int lo = 2 * stride * (i / stride) + (i % stride);
+                const int lo = ((i >> ls) << (ls + 1)) | (i & (stride - 1));
                 const int hi = lo + stride;
                 const bool up = (lo & size) == 0;
                 const double klo = key[lo], khi = key[hi];
@@ -150,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void bsa_select_kernel(
 
 }  // namespace
 
-hipError_t launch_bsa_select(const int32_t* qsum, const int32_t* ksum, const float* qsc, const float* ksc,
+hipError_t launch_bsa_select(const int16_t* qsum, const int16_t* ksum, const float* qsc, const float* ksc,
                              const int32_t* cu, const int32_t* tb, const int32_t* items, int64_t num_items,
                              int num_seqs, int total_tokens, int num_heads, int64_t num_tiles,
                              int sp_permille, int64_t list_stride, int32_t* lists, hipStream_t stream) {

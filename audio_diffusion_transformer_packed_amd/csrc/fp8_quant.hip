@@ -39,7 +39,8 @@
 // scale = amax / 127 (1 when amax is 0), code = round-half-even(127 x /
 // amax) in [-127, 127], same layouts, plus per (tile, head) the per-channel
 // sums of the Q codes (qsum [T, H, 128]) and of the K codes (ksum [H, T,
-// 128]), the block means the block selection ranks by.
+// 128]), int16 (|sum| <= 64 * 127), the block means the block selection
+// ranks by.
 // All HBM-bound: q, k, v are streamed once by quant_qk_kernel and v once
 // more by quant_v_kernel (V's scale needs the whole segment first), with
 // 16-byte nontemporal loads. Work items are ordered head-fastest, so the
@@ -188,15 +189,16 @@ __device__ __forceinline__ u32x2 i8_codes8(uint4 raw, float amax, int (&s)[8]) {
 // One workgroup per (key tile, head), head-fastest: Q and K codes + block
 // scales, and the tile's channel amax of V (reduced per segment afterwards).
 // I8: Q and K as INT8 (scale amax / 127) instead of e4m3, plus the tile's
-// per-channel code sums of Q (qsum [T, H, 128]) and K (ksum [H, T, 128]).
+// per-channel code sums of Q (qsum [T, H, 128]) and K (ksum [H, T, 128]),
+// int16.
 template <bool I8>
 __global__ __launch_bounds__(256) void quant_qk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int64_t qs, int64_t ks, int64_t vs, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ tb, int num_seqs, int num_heads, int64_t num_tiles,
     uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, float* __restrict__ qsc,
-    float* __restrict__ ksc, float* __restrict__ vpart, int32_t* __restrict__ qsum,
-    int32_t* __restrict__ ksum) {
+    float* __restrict__ ksc, float* __restrict__ vpart, int16_t* __restrict__ qsum,
+    int16_t* __restrict__ ksum) {
     __shared__ float red[2][4];
     __shared__ float vred[4][kD];
     __shared__ int32_t isum[I8 ? 2 : 1][4][I8 ? kD : 1];
@@ -275,10 +277,11 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
         __syncthreads();
         const int which = tid >> 7, d = tid & 127;
         const int32_t tot = isum[which][0][d] + isum[which][1][d] + isum[which][2][d] + isum[which][3][d];
+        // |sum| <= 64 * 127 = 8128: int16
         if (which == 0)
-            qsum[(static_cast<int64_t>(tile) * num_heads + h) * kD + d] = tot;
+            qsum[(static_cast<int64_t>(tile) * num_heads + h) * kD + d] = static_cast<int16_t>(tot);
         else
-            ksum[(static_cast<int64_t>(h) * num_tiles + tile) * kD + d] = tot;
+            ksum[(static_cast<int64_t>(h) * num_tiles + tile) * kD + d] = static_cast<int16_t>(tot);
         if (tid == 0) {
             qsc[static_cast<int64_t>(tile) * num_heads + h] = amax_q > 0.f ? amax_q / 127.0f : 1.0f;
             ksc[static_cast<int64_t>(tile) * num_heads + h] = amax_k > 0.f ? amax_k / 127.0f : 1.0f;
@@ -396,7 +399,7 @@ hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint1
                                int64_t ks, int64_t vs, const int32_t* cu, int num_seqs,
                                int num_heads, int64_t num_tiles, uint8_t* q8, uint8_t* k8,
                                uint8_t* v8t, float* qsc, float* ksc, float* vsc, void* workspace,
-                               hipStream_t stream, int32_t* qsum, int32_t* ksum) {
+                               hipStream_t stream, int16_t* qsum, int16_t* ksum) {
     if (num_seqs <= 0 || num_tiles <= 0) return hipSuccess;
     if (num_tiles * num_heads > 0xffffffffll) return hipErrorInvalidValue;   // 1-D grid of (tile, head)
     int32_t* tb = static_cast<int32_t*>(workspace);

@@ -29,7 +29,7 @@ hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint1
                                int64_t ks, int64_t vs, const int32_t* cu, int num_seqs,
                                int num_heads, int64_t num_tiles, uint8_t* q8, uint8_t* k8,
                                uint8_t* v8t, float* qsc, float* ksc, float* vsc, void* workspace,
-                               hipStream_t stream, int32_t* qsum = nullptr, int32_t* ksum = nullptr);
+                               hipStream_t stream, int16_t* qsum = nullptr, int16_t* ksum = nullptr);
 
 // fp8 attention over the quantised codes (attn_fp8.hip)
 bool fp8_attention_available();
@@ -45,7 +45,7 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t*
 // Lists: int32 [H, T, list_stride], row (head, first 64-token block of a
 // 256-row query block) holds the kept key blocks of that query block.
 constexpr int kBsaMaxKeyBlocks = 4096;          // 64-key blocks per segment
-hipError_t launch_bsa_select(const int32_t* qsum, const int32_t* ksum, const float* qsc, const float* ksc,
+hipError_t launch_bsa_select(const int16_t* qsum, const int16_t* ksum, const float* qsc, const float* ksc,
                              const int32_t* cu, const int32_t* tb, const int32_t* items, int64_t num_items,
                              int num_seqs, int total_tokens, int num_heads, int64_t num_tiles,
                              int sp_permille, int64_t list_stride, int32_t* lists, hipStream_t stream);

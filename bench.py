@@ -149,6 +149,24 @@ def cpu_baseline(inp, wl, rows_count=16):
                        f"TFLOP algorithmic in {dt:.1f} s")}
 
 
+def bsa_kept_flops(lists, lengths, head_dim, sparsity) -> float:
+    """4 D x (query rows x kept keys), summed over heads and 256-row query
+    blocks, from kept-block lists [H, T, stride] (row = first 64-token block
+    of the query block)."""
+    total = 0.0
+    tile = 0
+    for L in lengths:
+        n_kb = (L + 63) // 64
+        keep = max(1, n_kb - (n_kb * round(1000 * sparsity)) // 1000) if n_kb else 0
+        for t0 in range(0, L, 256):
+            rows = min(256, L - t0)
+            blocks = lists[:, tile + t0 // 64, :keep]                      # [H, keep]
+            keys = np.minimum(64, L - 64 * blocks).sum()
+            total += 4.0 * head_dim * rows * float(keys)
+        tile += n_kb
+    return total
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +365,34 @@ def main():
                "skip_threshold": 8.0}
         rec("fp8_quantize", tq, nbytes=q_bytes)
 
+    # Block-sparse attention (INT8 Q/K, FP8 V) at sparsity 0.8 on the same
+    # q/k/v: the whole pass (quantise, select, attend). Algorithmic flops
+    # count the kept keys only, from the kept-block lists of this input.
+    bsa = None
+    if not args.no_fp8:
+        log("timing block-sparse attention")
+        sp = 0.8
+        bsa_ws = torch.empty(ops.lib().h3_attn_block_sparse_workspace_size(b, n, wl.heads, wl.head_dim, sp),
+                             dtype=torch.uint8, device=dev)
+        t_tiles = ops.fp8_num_tiles(cu)
+        lists = torch.full((wl.heads, t_tiles, ops.attn_block_sparse_list_stride(cu, sp)), -1,
+                           dtype=torch.int32, device=dev)
+        o_bsa = torch.empty_like(o_att)
+        bsa_fn = lambda: ops.attn_block_sparse(qv, kv, vv, cu_d, cu, sparsity=sp, out=o_bsa,
+                                               kv_block_lists=lists, workspace=bsa_ws)
+        bsa_fn()
+        ms_bsa = timer(bsa_fn, max(3, args.steps))
+        kept_flops = bsa_kept_flops(lists.cpu().numpy(), wl.lengths, wl.head_dim, sp)
+        bsa = {"workload": f"{wl.name} q/k/v, block-sparse at sparsity {sp} (256-row query blocks, "
+                           "64-key blocks, INT8 Q/K, FP8 V)",
+               "attention_ms": round(ms_bsa, 4),
+               "speedup_vs_fp8_dense": round(ms_fp8 / ms_bsa, 3),
+               "speedup_vs_bf16_dense": round(ms_attn / ms_bsa, 3),
+               "kept_key_fraction": round(kept_flops / f_attn, 4),
+               "kept_tflops": round(kept_flops / (ms_bsa * 1e-3) / 1e12, 2),
+               "kept_frac_int8_fp8_peak": round(kept_flops / (ms_bsa * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        del bsa_ws, lists, o_bsa
+
     # The same block with MXFP8 (OCP MX, E4M3) linears: weights quantised once
     # before timing; a step quantises its activations inside the step.
     mxr = None
@@ -437,6 +483,7 @@ def main():
                      "traffic": traffic},
         "stages": stages,
         "fp8_attention": fp8,
+        "block_sparse_attention": bsa,
         "mxfp8_linears": mxr,
         "timed_wall_s": round(t_wall, 3),
     }
