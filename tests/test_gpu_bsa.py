@@ -158,3 +158,43 @@ def test_bsa_full_size_sampled_blocks(dev, ops):
     sel = _check_output(got, q, k, v, cu, 0.8, "bsa 58k sampled", query_blocks=qblocks, mask=mask)
     _check_lists(lists, sel, cu, heads_map={0: hs[0], 1: hs[1]})
     assert all(len(b) == oracle.keep_count((n + 63) // 64, 0.8) for b in sel.values())
+
+
+def test_bsa_maximum_segment(dev, ops):
+    """The largest segment the path takes: 262,144 tokens = 4096 key blocks
+    (the selection sorts 4096 pairs in LDS), one head, sparsity 0.9 (410
+    kept). Lists of four sampled query blocks bit for bit, their outputs
+    against the emulation."""
+    import torch
+    n = 4096 * 64
+    cu = np.array([0, n], np.int32)
+    announce(f"bsa maximum segment N={n} H=1 sparsity=0.9")
+    inp = h3synth.attention_inputs(cu, np.zeros((n, 3), np.int32), 1, D, seed=506)
+    out, lists = _run(ops, dev, inp, 0.9)
+    qblocks = [(0, 0), (0, 256 * 417), (0, 256 * 700), (0, n - 256)]
+    rows = np.array(sorted({t for _, t0 in qblocks for t in range(t0, t0 + 256)}))
+    got = np.zeros((n, 1, D))
+    got[rows] = to_np(out.index_select(0, torch.from_numpy(rows).to(dev)))
+    mask = np.zeros((n, 1, 1), dtype=bool)
+    mask[rows] = True
+    sel = _check_output(got, inp.q.f32, inp.k.f32, inp.v.f32, cu, 0.9, "bsa max segment",
+                        query_blocks=qblocks, mask=mask)
+    _check_lists(lists, sel, cu)
+    assert all(len(b) == 410 for b in sel.values())
+
+
+def test_bsa_empty_and_rejected(dev, ops):
+    """No tokens: nothing launched, success. One token over the maximum
+    segment: H3_ERR_UNSUPPORTED before any launch."""
+    import torch
+    from audio_diffusion_transformer_packed_amd import _lib as L
+    z = torch.empty((0, 2, D), dtype=torch.bfloat16, device=dev)
+    cu = np.array([0, 0], np.int32)
+    out = ops.attn_block_sparse(z, z, z, to_dev_i32(cu, dev), cu, sparsity=0.8)
+    assert out.shape == (0, 2, D)
+    n = 4096 * 64 + 1
+    cu = np.array([0, n], np.int32)
+    q = torch.zeros((n, 1, D), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(Exception) as e:
+        ops.attn_block_sparse(q, q, q, to_dev_i32(cu, dev), cu, sparsity=0.8)
+    assert "262144" in str(e.value) or str(L.H3_ERR_UNSUPPORTED) in str(e.value) or "UNSUPPORTED" in str(e.value)
