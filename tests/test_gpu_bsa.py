@@ -198,3 +198,29 @@ def test_bsa_empty_and_rejected(dev, ops):
     with pytest.raises(Exception) as e:
         ops.attn_block_sparse(q, q, q, to_dev_i32(cu, dev), cu, sparsity=0.8)
     assert "262144" in str(e.value) or str(L.H3_ERR_UNSUPPORTED) in str(e.value) or "UNSUPPORTED" in str(e.value)
+
+
+def test_bsa_ties_go_to_lower_blocks(dev, ops):
+    """Equal scores: head 0 has all-zero queries (every score 0), head 1 keys
+    that repeat every 64 tokens (every full block scores the same). The GPU
+    lists must break the ties to the lower block index, as the oracle does;
+    the outputs must still match the emulation."""
+    lens = [64 * 12, 64 * 7 + 9]
+    cu = h3synth.cu_from_lengths(lens)
+    n = int(cu[-1])
+    announce(f"bsa ties lens={lens}")
+    inp = h3synth.attention_inputs(cu, np.zeros((n, 3), np.int32), 2, D, seed=507)
+    q_bits, k_bits = inp.q.bits.copy(), inp.k.bits.copy()
+    q_bits[:, 0] = 0
+    for s in range(len(lens)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        for t in range(a + 64, b):
+            k_bits[t, 1] = k_bits[a + (t - a) % 64, 1]
+    inp.q = h3synth.Bf16Array(q_bits, h3synth.bits_to_f32(q_bits))
+    inp.k = h3synth.Bf16Array(k_bits, h3synth.bits_to_f32(k_bits))
+    out, lists = _run(ops, dev, inp, 0.75)
+    sel = _check_output(to_np(out), inp.q.f32, inp.k.f32, inp.v.f32, cu, 0.75, "bsa ties")
+    _check_lists(lists, sel, cu)
+    for (h, t0), blocks in sel.items():
+        if h == 0:
+            assert list(blocks) == list(range(len(blocks)))
