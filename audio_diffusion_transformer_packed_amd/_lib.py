@@ -34,7 +34,7 @@ EXPORTS = (
     "h3_mx_quantize_bf16",
     "h3_linear_mxfp8", "h3_linear_swiglu_mxfp8", "h3_linear_gated_residual_mxfp8",
     "h3_dit_block_workspace_size", "h3_dit_block_forward", "h3_dit_block_mx_workspace_size",
-    "h3_dit_block_forward_mxfp8",
+    "h3_dit_block_forward_mxfp8", "h3_dit_block_mx_bsa_workspace_size", "h3_dit_block_forward_mxfp8_bsa",
 )
 
 
@@ -118,6 +118,8 @@ def _declare(lib):
         "h3_dit_block_forward": (C.c_int, [P, P, P, P, P, P, P, I32, I32, P, P, P, SZ, P]),
         "h3_dit_block_mx_workspace_size": (SZ, [P, I32, I32]),
         "h3_dit_block_forward_mxfp8": (C.c_int, [P, P, P, P, P, P, P, I32, I32, P, P, SZ, P]),
+        "h3_dit_block_mx_bsa_workspace_size": (SZ, [P, I32, I32, F32]),
+        "h3_dit_block_forward_mxfp8_bsa": (C.c_int, [P, P, P, P, P, P, P, I32, I32, P, F32, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

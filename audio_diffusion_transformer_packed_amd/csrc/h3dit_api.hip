@@ -346,13 +346,60 @@ H3_API h3_status h3_attn_block_sparse_list_stride(const int32_t* cu_seqlens_host
     return ok();
 }
 
-H3_API size_t h3_attn_block_sparse_workspace_size(int32_t num_seqs, int32_t total_tokens,
-                                                  int32_t num_heads, int32_t head_dim, float sparsity) {
+namespace {
+
+size_t bsa_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                           float sparsity) {
     if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || head_dim != 128 || !sparsity_ok(sparsity))
         return 0;
     const int64_t stride = bsa_list_stride_bound(total_tokens, sparsity_permille(sparsity));
     return attn_plan(num_seqs, total_tokens, num_heads, head_dim, H3_ATTN_BF16).total +
            align_up(h3::bsa_scratch_bytes(num_seqs, total_tokens, num_heads, stride));
+}
+
+// Argument checks shared by the attention entry point and the block.
+h3_status check_bsa(const int32_t* cu_host, int32_t num_seqs, int32_t head_dim, float sparsity) {
+    if (head_dim != 128)
+        return fail(H3_ERR_UNSUPPORTED, "block-sparse attention needs head_dim 128 (got %d)", head_dim);
+    if (!sparsity_ok(sparsity)) return fail(H3_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1)");
+    for (int32_t s = 0; s < num_seqs; ++s)
+        if (cu_host[s + 1] - cu_host[s] > h3::kBsaMaxKeyBlocks * H3_FP8_QK_BLOCK)
+            return fail(H3_ERR_UNSUPPORTED, "segment %d has %d tokens; block-sparse attention takes at most %d",
+                        s, cu_host[s + 1] - cu_host[s], h3::kBsaMaxKeyBlocks * H3_FP8_QK_BLOCK);
+    return ok();
+}
+
+// Enqueues bookkeeping + the block-sparse pass; arguments already validated.
+h3_status run_attention_bsa(const void* q, const void* k, const void* v, void* out, int64_t qs, int64_t ks,
+                            int64_t vs, int64_t os, const int32_t* cu_dev, const int32_t* cu_host,
+                            int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+                            float softmax_scale, float sparsity, int32_t* lists, void* workspace,
+                            hipStream_t stream) {
+    const int permille = sparsity_permille(sparsity);
+    const AttnPlan plan = attn_plan(num_seqs, total_tokens, num_heads, head_dim, H3_ATTN_BF16);
+    const int64_t n_items = count_items(cu_host, num_seqs, num_heads, H3_ATTN_BLOCK_M);
+    if (n_items == 0) return ok();
+    char* ws = static_cast<char*>(workspace);
+    int32_t* items = reinterpret_cast<int32_t*>(ws);
+    hipError_t e = h3::launch_bookkeeping(cu_dev, num_seqs, total_tokens, num_heads, H3_ATTN_BLOCK_M,
+                                          nullptr, nullptr, items, plan.items_cap, ws + plan.items_bytes,
+                                          stream);
+    if (e != hipSuccess) return hip_fail(e, "bookkeeping launch");
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+    e = h3::launch_attn_bsa(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), qs, ks, vs, os,
+                            cu_dev, cu_host, items, n_items, num_seqs, total_tokens, num_heads, scale,
+                            permille, bsa_list_stride(cu_host, num_seqs, permille), lists,
+                            ws + plan.total, stream);
+    if (e != hipSuccess) return hip_fail(e, "block-sparse attention launch");
+    return ok();
+}
+
+}  // namespace
+
+H3_API size_t h3_attn_block_sparse_workspace_size(int32_t num_seqs, int32_t total_tokens,
+                                                  int32_t num_heads, int32_t head_dim, float sparsity) {
+    return bsa_workspace_bytes(num_seqs, total_tokens, num_heads, head_dim, sparsity);
 }
 
 H3_API h3_status h3_attn_block_sparse(const void* q, const void* k, const void* v, void* out,
@@ -366,15 +413,10 @@ H3_API h3_status h3_attn_block_sparse(const void* q, const void* k, const void* 
     h3_status st = check_cu(cu_seqlens_host, num_seqs, total_tokens);
     if (st != H3_OK) return st;
     if (num_heads <= 0) return fail(H3_ERR_INVALID_ARGUMENT, "num_heads=%d <= 0", num_heads);
-    if (head_dim != 128)
-        return fail(H3_ERR_UNSUPPORTED, "block-sparse attention needs head_dim 128 (got %d)", head_dim);
-    if (!sparsity_ok(sparsity)) return fail(H3_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1)");
+    st = check_bsa(cu_seqlens_host, num_seqs, head_dim, sparsity);
+    if (st != H3_OK) return st;
     if (!(softmax_scale >= 0.f) || std::isinf(softmax_scale))
         return fail(H3_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
-    for (int32_t s = 0; s < num_seqs; ++s)
-        if (cu_seqlens_host[s + 1] - cu_seqlens_host[s] > h3::kBsaMaxKeyBlocks * H3_FP8_QK_BLOCK)
-            return fail(H3_ERR_UNSUPPORTED, "segment %d has %d tokens; block-sparse attention takes at most %d",
-                        s, cu_seqlens_host[s + 1] - cu_seqlens_host[s], h3::kBsaMaxKeyBlocks * H3_FP8_QK_BLOCK);
     if (total_tokens == 0) return ok();
     if (!q || !k || !v || !out || !cu_seqlens_dev)
         return fail(H3_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
@@ -394,26 +436,10 @@ H3_API h3_status h3_attn_block_sparse(const void* q, const void* k, const void* 
         return fail(H3_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
         return fail(H3_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    const int permille = sparsity_permille(sparsity);
-    const AttnPlan plan = attn_plan(num_seqs, total_tokens, num_heads, head_dim, H3_ATTN_BF16);
-    const int64_t n_items = count_items(cu_seqlens_host, num_seqs, num_heads, H3_ATTN_BLOCK_M);
-    if (n_items == 0) return ok();
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    char* ws = static_cast<char*>(workspace);
-    int32_t* items = reinterpret_cast<int32_t*>(ws);
-    hipError_t e = h3::launch_bookkeeping(cu_seqlens_dev, num_seqs, total_tokens, num_heads,
-                                          H3_ATTN_BLOCK_M, nullptr, nullptr, items, plan.items_cap,
-                                          ws + plan.items_bytes, stream);
-    if (e != hipSuccess) return hip_fail(e, "bookkeeping launch");
-    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
-    e = h3::launch_attn_bsa(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), q_tok_stride,
-                            k_tok_stride, v_tok_stride, o_tok_stride, cu_seqlens_dev, cu_seqlens_host,
-                            items, n_items, num_seqs, total_tokens, num_heads, scale, permille,
-                            bsa_list_stride(cu_seqlens_host, num_seqs, permille), kv_block_lists,
-                            ws + plan.total, stream);
-    if (e != hipSuccess) return hip_fail(e, "block-sparse attention launch");
-    return ok();
+    return run_attention_bsa(q, k, v, out, q_tok_stride, k_tok_stride, v_tok_stride, o_tok_stride,
+                             cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens, num_heads, head_dim,
+                             softmax_scale, sparsity, kv_block_lists, workspace,
+                             static_cast<hipStream_t>(hip_stream));
 }
 
 H3_API h3_status h3_fp8_num_tiles(const int32_t* cu_seqlens_host, int32_t num_seqs,
@@ -940,7 +966,9 @@ struct BlockPlanMX {
     size_t mod, h8, hs, qkv, o, o8, os, x1, a8, as, attn, total;
 };
 
-BlockPlanMX block_plan_mx(const h3_dit_dims* d, int32_t num_seqs, int32_t total_tokens) {
+// sparsity < 0: dense bf16 attention; else block-sparse at that sparsity
+BlockPlanMX block_plan_mx(const h3_dit_dims* d, int32_t num_seqs, int32_t total_tokens,
+                          float sparsity = -1.f) {
     BlockPlanMX p;
     const size_t n = static_cast<size_t>(total_tokens), c = static_cast<size_t>(d->hidden);
     const size_t f = static_cast<size_t>(d->ffn_dim);
@@ -954,7 +982,8 @@ BlockPlanMX block_plan_mx(const h3_dit_dims* d, int32_t num_seqs, int32_t total_
     p.x1 = align_up(n * c * 2);
     p.a8 = align_up(n * f);
     p.as = align_up(n * f / 32);
-    p.attn = attn_plan(num_seqs, total_tokens, d->num_heads, d->head_dim, H3_ATTN_BF16).total;
+    p.attn = sparsity < 0.f ? attn_plan(num_seqs, total_tokens, d->num_heads, d->head_dim, H3_ATTN_BF16).total
+                            : bsa_workspace_bytes(num_seqs, total_tokens, d->num_heads, d->head_dim, sparsity);
     p.total = p.mod + p.h8 + p.hs + p.qkv + p.o + p.o8 + p.os + p.x1 + p.a8 + p.as + p.attn;
     return p;
 }
@@ -981,18 +1010,25 @@ H3_API size_t h3_dit_block_mx_workspace_size(const h3_dit_dims* dims, int32_t nu
     return block_plan_mx(dims, num_seqs, total_tokens).total;
 }
 
-H3_API h3_status h3_dit_block_forward_mxfp8(const void* x, void* x_out, const void* cond,
-                                            const h3_dit_mx_weights* weights,
-                                            const h3_dit_dims* dims,
-                                            const int32_t* cu_seqlens_dev,
-                                            const int32_t* cu_seqlens_host, int32_t num_seqs,
-                                            int32_t total_tokens, const int32_t* rope_grid,
-                                            void* workspace, size_t workspace_bytes,
-                                            void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The MXFP8 block; sparsity < 0 runs dense bf16 attention, otherwise the
+// block-sparse INT8/FP8 attention at that sparsity.
+h3_status block_forward_mx(const void* x, void* x_out, const void* cond, const h3_dit_mx_weights* weights,
+                           const h3_dit_dims* dims, const int32_t* cu_seqlens_dev,
+                           const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                           const int32_t* rope_grid, float sparsity, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
     h3_status st = check_dims_mx(dims, total_tokens);
     if (st != H3_OK) return st;
     st = check_cu(cu_seqlens_host, num_seqs, total_tokens);
     if (st != H3_OK) return st;
+    if (sparsity >= 0.f) {
+        st = check_bsa(cu_seqlens_host, num_seqs, dims->head_dim, sparsity);
+        if (st != H3_OK) return st;
+    }
     if (total_tokens == 0) return ok();
     if (!x || !x_out || !cond || !weights || !cu_seqlens_dev || !rope_grid)
         return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
@@ -1009,7 +1045,7 @@ H3_API h3_status h3_dit_block_forward_mxfp8(const void* x, void* x_out, const vo
                          reinterpret_cast<uintptr_t>(cond) | reinterpret_cast<uintptr_t>(w.w_mod) |
                          reinterpret_cast<uintptr_t>(w.q_norm) | reinterpret_cast<uintptr_t>(w.k_norm);
     if (al & 15) return fail(H3_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
-    const BlockPlanMX p = block_plan_mx(dims, num_seqs, total_tokens);
+    const BlockPlanMX p = block_plan_mx(dims, num_seqs, total_tokens, sparsity);
     if (workspace_bytes < p.total || workspace == nullptr)
         return fail(H3_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, p.total);
     if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
@@ -1054,9 +1090,14 @@ H3_API h3_status h3_dit_block_forward_mxfp8(const void* x, void* x_out, const vo
                                    total_tokens, dims->num_heads, dims->head_dim,
                                    dims->rope_split, dims->rope_theta, dims->eps, stream),
            "qk norm rope");
-    h3_status ast = run_attention(qkv, qkv + c, qkv + 2 * c, obuf, 3 * c, 3 * c, 3 * c, c,
-                                  cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
-                                  dims->num_heads, dims->head_dim, nullptr, attn_ws, stream);
+    h3_status ast = sparsity < 0.f
+                        ? run_attention(qkv, qkv + c, qkv + 2 * c, obuf, 3 * c, 3 * c, 3 * c, c,
+                                        cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                                        dims->num_heads, dims->head_dim, nullptr, attn_ws, stream)
+                        : run_attention_bsa(qkv, qkv + c, qkv + 2 * c, obuf, 3 * c, 3 * c, 3 * c, c,
+                                            cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                                            dims->num_heads, dims->head_dim, 0.f, sparsity, nullptr,
+                                            attn_ws, stream);
     if (ast != H3_OK) return ast;
     H3_TRY(h3::launch_mx_quantize(obuf, c, n, c, o8, os, stream), "o quantize");
     H3_TRY(h3::launch_gemm_mx(h3::kEpiGatedResidual, o8, os, u8(w.w_o.codes), u8(w.w_o.scales), nullptr,
@@ -1072,6 +1113,42 @@ H3_API h3_status h3_dit_block_forward_mxfp8(const void* x, void* x_out, const vo
                               cu_seqlens_dev, num_seqs, stream), "down gemm");
 #undef H3_TRY
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+H3_API h3_status h3_dit_block_forward_mxfp8(const void* x, void* x_out, const void* cond,
+                                            const h3_dit_mx_weights* weights,
+                                            const h3_dit_dims* dims,
+                                            const int32_t* cu_seqlens_dev,
+                                            const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                            int32_t total_tokens, const int32_t* rope_grid,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* hip_stream) {
+    return block_forward_mx(x, x_out, cond, weights, dims, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                            total_tokens, rope_grid, -1.f, workspace, workspace_bytes, hip_stream);
+}
+
+H3_API size_t h3_dit_block_mx_bsa_workspace_size(const h3_dit_dims* dims, int32_t num_seqs,
+                                                 int32_t total_tokens, float sparsity) {
+    if (dims == nullptr || num_seqs < 0 || total_tokens < 0 || !sparsity_ok(sparsity)) return 0;
+    if (check_dims_mx(dims, total_tokens) != H3_OK || dims->head_dim != 128) return 0;
+    return block_plan_mx(dims, num_seqs, total_tokens, sparsity).total;
+}
+
+H3_API h3_status h3_dit_block_forward_mxfp8_bsa(const void* x, void* x_out, const void* cond,
+                                                const h3_dit_mx_weights* weights,
+                                                const h3_dit_dims* dims,
+                                                const int32_t* cu_seqlens_dev,
+                                                const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                int32_t total_tokens, const int32_t* rope_grid,
+                                                float sparsity, void* workspace,
+                                                size_t workspace_bytes, void* hip_stream) {
+    if (!sparsity_ok(sparsity)) return fail(H3_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1)");
+    return block_forward_mx(x, x_out, cond, weights, dims, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                            total_tokens, rope_grid, sparsity, workspace, workspace_bytes, hip_stream);
 }
 
 }  // extern "C"

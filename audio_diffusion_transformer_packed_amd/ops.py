@@ -569,11 +569,14 @@ MX_WEIGHT_NAMES = ("w_qkv", "w_o", "w_gate", "w_up", "w_down")
 
 class DitBlockMX:
     """The block with MXFP8 linears: the five linear weights are quantised
-    once here (h3_mx_quantize_bf16); forward() calls h3_dit_block_forward_mxfp8."""
+    once here (h3_mx_quantize_bf16); forward() calls h3_dit_block_forward_mxfp8,
+    or, with attn_sparsity set, h3_dit_block_forward_mxfp8_bsa (block-sparse
+    INT8/FP8 attention at that sparsity: the pages' lossy configuration)."""
 
     def __init__(self, weights: Dict[str, torch.Tensor], heads: int, head_dim: int,
                  ffn_dim: int, rope_split: Sequence[int], rope_theta: float = 10000.0,
-                 eps: float = 1e-6):
+                 eps: float = 1e-6, attn_sparsity: Optional[float] = None):
+        self.attn_sparsity = None if attn_sparsity is None else float(attn_sparsity)
         hidden = heads * head_dim
         for nm in WEIGHT_NAMES:
             _need(weights[nm], nm, BF16)
@@ -590,6 +593,9 @@ class DitBlockMX:
         self.hidden, self.ffn = hidden, ffn_dim
 
     def workspace_bytes(self, num_seqs: int, total_tokens: int) -> int:
+        if self.attn_sparsity is not None:
+            return lib().h3_dit_block_mx_bsa_workspace_size(C.byref(self.dims), num_seqs, total_tokens,
+                                                            self.attn_sparsity)
         return lib().h3_dit_block_mx_workspace_size(C.byref(self.dims), num_seqs, total_tokens)
 
     def forward(self, x: torch.Tensor, cond: torch.Tensor, cu_seqlens: torch.Tensor, cu_host,
@@ -607,8 +613,11 @@ class DitBlockMX:
         if out is None:
             out = torch.empty_like(x)
         ws = _workspace(self.workspace_bytes(b, n), dev, workspace)
-        check(lib().h3_dit_block_forward_mxfp8(_ptr(x), _ptr(out), _ptr(cond), C.byref(self.c_weights),
-                                               C.byref(self.dims), _ptr(cu_seqlens),
-                                               cu.ctypes.data_as(C.c_void_p), b, n, _ptr(rope_grid),
-                                               _ptr(ws), ws.numel(), _stream(dev)))
+        common = (_ptr(x), _ptr(out), _ptr(cond), C.byref(self.c_weights), C.byref(self.dims),
+                  _ptr(cu_seqlens), cu.ctypes.data_as(C.c_void_p), b, n, _ptr(rope_grid))
+        if self.attn_sparsity is not None:
+            check(lib().h3_dit_block_forward_mxfp8_bsa(*common, self.attn_sparsity, _ptr(ws), ws.numel(),
+                                                       _stream(dev)))
+        else:
+            check(lib().h3_dit_block_forward_mxfp8(*common, _ptr(ws), ws.numel(), _stream(dev)))
         return out

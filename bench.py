@@ -452,7 +452,19 @@ def main():
                "block_tflops": round((f_attn + f_gemm) / (ms_mx * 1e-3) / 1e12, 2),
                "speedup_vs_bf16_block": round(ms_step / ms_mx, 4),
                "stages": mods}
-        del blk_mx, ws_mx, out_mx
+        # The pages' lossy configuration: the same MXFP8 block with its
+        # attention block-sparse (INT8 Q/K, FP8 V) at sparsity 0.8.
+        blk_l = ops.DitBlockMX(weights, wl.heads, wl.head_dim, wl.ffn, split, attn_sparsity=0.8)
+        ws_l = torch.empty(blk_l.workspace_bytes(b, n), dtype=torch.uint8, device=dev)
+        step_l = lambda: blk_l.forward(x, cond, cu_d, cu, grid_d, out=out_mx, workspace=ws_l)
+        for _ in range(args.warmup):
+            step_l()
+        ms_l = timer(step_l, args.steps)
+        mxr["lossy_block_mxfp8_bsa"] = {
+            "workload": f"{wl.name}, MXFP8 linears + block-sparse attention at sparsity 0.8",
+            "block_ms": round(ms_l, 4), "speedup_vs_bf16_block": round(ms_step / ms_l, 3),
+            "speedup_vs_mxfp8_block": round(ms_mx / ms_l, 3)}
+        del blk_mx, ws_mx, out_mx, blk_l, ws_l
 
     traffic = load_traffic()
     result = {

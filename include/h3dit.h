@@ -488,6 +488,32 @@ H3_API h3_status h3_dit_block_forward_mxfp8(const void* x, void* x_out, const vo
                                             void* workspace, size_t workspace_bytes,
                                             void* hip_stream);
 
+/* ------------------------------------------------------------------------
+ * The block in the pages' lossy configuration ("MiniMax H3 on Ascend 950PR
+ * / 950DT", section "Recommended lossy configuration (Ascend 950PR /
+ * 950DT)": EQBSA block-sparse attention together with MXFP8 online
+ * quantisation of the transformer): h3_dit_block_forward_mxfp8 with its
+ * attention step replaced by the block-sparse INT8/FP8 attention of
+ * h3_attn_block_sparse at `sparsity` (default softmax scale). Arguments,
+ * layouts and errors as for h3_dit_block_forward_mxfp8, plus those of
+ * h3_attn_block_sparse (head_dim 128, segments of at most 262144 tokens,
+ * sparsity in [0, 1)). The workspace (h3_dit_block_mx_bsa_workspace_size
+ * bytes, 0 for unsupported sizes) replaces the dense attention's share with
+ * the block-sparse pass's. The dense-fallback window of the pages (leading
+ * and trailing denoising steps) is the caller's per-step choice between
+ * this call and h3_dit_block_forward_mxfp8.
+ * ---------------------------------------------------------------------- */
+H3_API size_t h3_dit_block_mx_bsa_workspace_size(const h3_dit_dims* dims, int32_t num_seqs,
+                                                 int32_t total_tokens, float sparsity);
+H3_API h3_status h3_dit_block_forward_mxfp8_bsa(const void* x, void* x_out, const void* cond,
+                                                const h3_dit_mx_weights* weights,
+                                                const h3_dit_dims* dims,
+                                                const int32_t* cu_seqlens_dev,
+                                                const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                int32_t total_tokens, const int32_t* rope_grid,
+                                                float sparsity, void* workspace,
+                                                size_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

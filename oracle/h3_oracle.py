@@ -270,7 +270,8 @@ def dit_block_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], gr
                   heads: int, head_dim: int, rope_split: Sequence[int],
                   rope_theta: float = 10000.0, eps: float = 1e-6,
                   emulate_bf16_storage: bool = False,
-                  linear_quant: Optional[Callable] = None) -> Dict[str, np.ndarray]:
+                  linear_quant: Optional[Callable] = None,
+                  attention: Optional[Callable] = None) -> Dict[str, np.ndarray]:
     """One block over the whole packed sequence; returns every intermediate.
 
     With emulate_bf16_storage, every intermediate that the device path stores
@@ -284,6 +285,12 @@ def dit_block_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], gr
     quantised from their unrounded values (the producing kernels quantise
     in registers), o from its stored value. The returned h, o, h2, a are the
     values the linears consumed.
+
+    attention (default attn_varlen_ref) is called as attention(q, k, v, cu)
+    on [N, H, D] arrays and returns o [N, H, D]; block_sparse_attention's
+    emulation plugs in here for the pages' lossy configuration ("MiniMax H3
+    on Ascend 950PR / 950DT", recommended lossy configuration: EQBSA with
+    MXFP8).
 
     h   = RMSNorm(x)(1+scale1)+shift1
     qkv = h W_qkv^T                   (q | k | v, each head-major [H*D])
@@ -311,7 +318,7 @@ def dit_block_ref(x, cond, weights: Dict[str, np.ndarray], cu: Sequence[int], gr
     qr, kr = qk_norm_rope_ref(q, k, weights["q_norm"], weights["k_norm"], grid, rope_split,
                               rope_theta, eps)
     qr, kr = st(qr), st(kr)
-    o = st(attn_varlen_ref(qr, kr, v, cu).reshape(n, c))
+    o = st((attention or attn_varlen_ref)(qr, kr, v, cu).reshape(n, c))
     if lq:
         o = lq(o)
     x1 = st(gated_residual_ref(x, m["gate1"], o @ wt("w_o").T, seg))

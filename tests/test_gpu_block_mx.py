@@ -128,3 +128,40 @@ def test_block_mx_full_size_sampled_rows(dev, ops):
     emul_alt = oracle.dit_block_rows_ref(*args, linear_quant=oracle.mx_fake_quant)
     exact = oracle.dit_block_rows_ref(*args)
     _check_branch(got, inp.x.f32[rows].astype(np.float64), emul, emul_alt, exact, name)
+
+
+def _bsa_attention(sparsity, quantize=True):
+    return lambda q, k, v, cu: oracle.bsa_attn_emulated_ref(q, k, v, cu, sparsity, quantize=quantize)[0]
+
+
+def test_block_mx_bsa_small(dev, ops):
+    """The pages' lossy configuration: MXFP8 linears and block-sparse
+    INT8/FP8 attention (sparsity 0.5: 3 of 5, 2 of 4 and 1 of 2 key blocks
+    kept in the three segments). Against the block emulating both (MX fake
+    quantisation, the block-sparse emulation, bf16 storage), with the same
+    self-calibrated bar as the MXFP8 block, and against the same block with
+    nothing quantised (exact softmax over the kept keys) for the floor."""
+    announce("block mx + block-sparse attention small (H=4, D=128, C=512, sparsity 0.5)")
+    inp = _small_inputs()
+    split = (32, 48, 48)
+    w = {nm: to_dev_bf16(getattr(inp, nm), dev) for nm in ops.WEIGHT_NAMES}
+    blk = ops.DitBlockMX(w, inp.heads, inp.head_dim, inp.ffn, split, attn_sparsity=0.5)
+    out = _run(dev, blk, inp)
+    args = (inp.x.f32, inp.cond.f32, _weights(inp), inp.cu_seqlens, inp.grid, 4, 128, split)
+    emul = oracle.dit_block_ref(*args, emulate_bf16_storage=True, linear_quant=oracle.mx_fake_quant,
+                                attention=_bsa_attention(0.5))
+    emul_alt = oracle.dit_block_ref(*args, linear_quant=oracle.mx_fake_quant, attention=_bsa_attention(0.5))
+    exact = oracle.dit_block_ref(*args, attention=_bsa_attention(0.5, quantize=False))
+    _check_branch(to_np(out), inp.x.f32.astype(np.float64), emul, emul_alt, exact, "small mx+bsa")
+
+
+def test_block_mx_bsa_deterministic_and_differs_from_dense(dev, ops):
+    import torch
+    announce("block mx + block-sparse determinism")
+    inp = _small_inputs(lens=(600, 211), seed=6)
+    w = {nm: to_dev_bf16(getattr(inp, nm), dev) for nm in ops.WEIGHT_NAMES}
+    sparse = ops.DitBlockMX(w, inp.heads, inp.head_dim, inp.ffn, (32, 48, 48), attn_sparsity=0.8)
+    dense = ops.DitBlockMX(w, inp.heads, inp.head_dim, inp.ffn, (32, 48, 48))
+    o1, o2 = _run(dev, sparse, inp), _run(dev, sparse, inp)
+    assert np.array_equal(bf16_bits_of(o1), bf16_bits_of(o2))
+    assert not np.array_equal(bf16_bits_of(o1), bf16_bits_of(_run(dev, dense, inp)))

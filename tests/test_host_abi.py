@@ -279,3 +279,15 @@ def test_dense_fallback_helper_matches_oracle():
     for start, end in [(8, 13), (8, 12), (0, 13), (0, 0), (50, 0)]:
         for s in range(50):
             assert ops.dense_attention_step(s, 50, start, end) == oracle.dense_fallback(s, 50, start, end)
+
+
+def test_block_mx_bsa_sizes(lib):
+    split = (C.c_int32 * 3)(32, 48, 48)
+    dims = L.DitDims(3072, 24, 128, 8192, split, 1e4, 1e-6)
+    ws = lib.h3_dit_block_mx_bsa_workspace_size
+    dense = lib.h3_dit_block_mx_workspace_size(C.byref(dims), 1, 57960)
+    sparse = ws(C.byref(dims), 1, 57960, C.c_float(0.8))
+    assert dense > 0 and sparse > 0 and sparse != dense
+    assert ws(C.byref(dims), 1, 57960, C.c_float(1.0)) == 0
+    dims64 = L.DitDims(3072, 48, 64, 8192, (C.c_int32 * 3)(16, 24, 24), 1e4, 1e-6)
+    assert ws(C.byref(dims64), 1, 57960, C.c_float(0.8)) == 0
