@@ -30,6 +30,14 @@
 //  * ping-pong: the two waves of a SIMD run their MFMA and softmax blocks
 //    half a tile apart (see the bf16 kernel), so one wave's softmax VALU
 //    work overlaps the other's MFMAs.
+//
+// The same kernel, instantiated with BSA = true, runs the block-sparse
+// attention ("MiniMax H3 on Ascend 950PR / 950DT", section "Recommended
+// lossy configuration (Ascend 950PR / 950DT)": EQBSA, Q/K in INT8 and V in
+// FP8): Q and K hold INT8 codes (fp8_quant.hip's INT8 variant), S^T runs on
+// v_mfma_i32_32x32x32_i8 and is converted to fp32, and each work item walks
+// only its query block's kept key tiles (bsa_select.hip), staged with their
+// K scales in LDS before the loop; V, P and the softmax are the fp8 path's.
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
