@@ -18,7 +18,7 @@
 //
 // One workgroup of 256 threads per work item: the query block's code sums
 // (up to 4 x 128, int16) go to LDS; each thread scores four key blocks at a
-// time, j = tid + 256 m, reading each key block's 128 code sums (256 B, from L2:
+// time, j = tid + 256 m, reading each key block's 128 code sums (256 B, from L2,
 // every query block of the head reads the same sums); the (score, j)
 // pairs are sorted in LDS by a bitonic network, the first keep(n) marked,
 // and the marks compacted in ascending j by a workgroup scan.
@@ -86,12 +86,14 @@ __global__ __launch_bounds__(kThreads) void bsa_select_kernel(
     // int16: v_dot2_i32_i16 takes two exact products per instruction, 16
     // products fit an int32 partial (< 1.06e9) and the partials add exactly
     // in float64 (every value an integer below 2^53).
-    const int16_t* kbase = ksum + (static_cast<int64_t>(head) * num_tiles + tbs) * kD;
+    // K sums are channel chunk-major ([H][16][T][8]): chunk c of key block j
+    // is 16 bytes at ((head * 16 + c) * T + tbs + j) * 8, so the lanes of a
+    // wave (consecutive j) read 1 KB contiguous per load instruction
+    const uint4* kbase = reinterpret_cast<const uint4*>(ksum) + static_cast<int64_t>(head) * (kD / 8) * num_tiles + tbs;
     for (int j0 = tid; j0 < npow; j0 += 4 * kThreads) {
         const uint4* kp[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            kp[m] = reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(min(j0 + kThreads * m, n - 1)) * kD);
+        for (int m = 0; m < 4; ++m) kp[m] = kbase + min(j0 + kThreads * m, n - 1);
         double dot[4][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void bsa_select_kernel(
                 for (int b = 0; b < 4; ++b) pb[b] = *reinterpret_cast<const uint4*>(&pq[b][c]);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const uint4 kv = kp[m][c / 8];
+                    const uint4 kv = kp[m][static_cast<int64_t>(c / 8) * num_tiles];
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         part[m][b] = dot2(pb[b].x, kv.x, part[m][b]);

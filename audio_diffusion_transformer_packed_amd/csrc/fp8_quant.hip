@@ -38,9 +38,10 @@
 // With code sums requested (the block-sparse path) Q and K are INT8 instead:
 // scale = amax / 127 (1 when amax is 0), code = round-half-even(127 x /
 // amax) in [-127, 127], same layouts, plus per (tile, head) the per-channel
-// sums of the Q codes (qsum [T, H, 128]) and of the K codes (ksum [H, T,
-// 128]), int16 (|sum| <= 64 * 127), the block means the block selection
-// ranks by.
+// sums of the Q codes (qsum [T, H, 128]) and of the K codes (ksum [H, 16,
+// T, 8]: channel chunk-major, so that consecutive key blocks' 16-byte chunks
+// are adjacent), int16 (|sum| <= 64 * 127), the block means the block
+// selection ranks by.
 // All HBM-bound: q, k, v are streamed once by quant_qk_kernel and v once
 // more by quant_v_kernel (V's scale needs the whole segment first), with
 // 16-byte nontemporal loads. Work items are ordered head-fastest, so the
@@ -189,8 +190,8 @@ __device__ __forceinline__ u32x2 i8_codes8(uint4 raw, float amax, int (&s)[8]) {
 // One workgroup per (key tile, head), head-fastest: Q and K codes + block
 // scales, and the tile's channel amax of V (reduced per segment afterwards).
 // I8: Q and K as INT8 (scale amax / 127) instead of e4m3, plus the tile's
-// per-channel code sums of Q (qsum [T, H, 128]) and K (ksum [H, T, 128]),
-// int16.
+// per-channel code sums of Q (qsum [T, H, 128]) and K (ksum [H, 16, T, 8],
+// channel chunk-major), int16.
 template <bool I8>
 __global__ __launch_bounds__(256) void quant_qk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -280,8 +281,9 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
         // |sum| <= 64 * 127 = 8128: int16
         if (which == 0)
             qsum[(static_cast<int64_t>(tile) * num_heads + h) * kD + d] = static_cast<int16_t>(tot);
-        else
-            ksum[(static_cast<int64_t>(h) * num_tiles + tile) * kD + d] = static_cast<int16_t>(tot);
+        else   // chunk-major: [H][16 channel chunks][T][8]
+            ksum[((static_cast<int64_t>(h) * (kD / 8) + d / 8) * num_tiles + tile) * 8 + d % 8] =
+                static_cast<int16_t>(tot);
         if (tid == 0) {
             qsc[static_cast<int64_t>(tile) * num_heads + h] = amax_q > 0.f ? amax_q / 127.0f : 1.0f;
             ksc[static_cast<int64_t>(tile) * num_heads + h] = amax_k > 0.f ? amax_k / 127.0f : 1.0f;
