@@ -470,7 +470,12 @@ hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t*
                            hipStream_t stream) {
     if (num_items <= 0 || num_seqs <= 0) return hipSuccess;
     int64_t tiles = 0;
-    for (int s = 0; s < num_seqs; ++s) tiles += (cu_host[s + 1] - cu_host[s] + kBN - 1) / kBN;
+    int max_blocks = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+        const int nb = (cu_host[s + 1] - cu_host[s] + kBN - 1) / kBN;
+        tiles += nb;
+        max_blocks = nb > max_blocks ? nb : max_blocks;
+    }
     const BsaScratch L = bsa_scratch_layout(num_seqs, total_tokens, num_heads, list_stride);
     char* base = static_cast<char*>(scratch);
     uint8_t* q8 = reinterpret_cast<uint8_t*>(base + L.f.q8);
@@ -488,7 +493,7 @@ hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t*
     if (e != hipSuccess) return e;
     const int32_t* tb = static_cast<const int32_t*>(ws);   // tile prefix sums from the quantise pass
     e = launch_bsa_select(qsum, ksum, qsc, ksc, cu, tb, items, num_items, num_seqs, total_tokens,
-                          num_heads, tiles, sp_permille, list_stride, lists, stream);
+                          num_heads, tiles, sp_permille, list_stride, lists, max_blocks, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(static_cast<unsigned>(num_items)), dim3(kThreads), 0,
                        stream, q8, k8, v8t, qsc, ksc, vsc, o, os, cu, tb,

@@ -47,12 +47,16 @@ __global__ __launch_bounds__(kThreads) void bsa_select_kernel(
     const int16_t* __restrict__ qsum, const int16_t* __restrict__ ksum, const float* __restrict__ qsc,
     const float* __restrict__ ksc, const int32_t* __restrict__ cu, const int32_t* __restrict__ tb,
     const int4* __restrict__ items, int num_seqs, int total_tokens, int num_heads, int64_t num_tiles,
-    int sp_permille, int64_t list_stride, int32_t* __restrict__ lists) {
+    int sp_permille, int64_t list_stride, int32_t* __restrict__ lists, int npow_max) {
 #pragma clang fp contract(off)
     __shared__ __attribute__((aligned(16))) int16_t pq[4][kD];
-    __shared__ double key[kBsaMaxKeyBlocks];
-    __shared__ uint16_t idx[kBsaMaxKeyBlocks];
-    __shared__ uint8_t mark[kBsaMaxKeyBlocks];
+    // sort arrays sized at launch for the longest segment (npow_max slots:
+    // 8 + 2 + 1 bytes each), so short segments leave room for more
+    // workgroups per CU
+    extern __shared__ __attribute__((aligned(16))) char dyn[];
+    double* key = reinterpret_cast<double*>(dyn);
+    uint16_t* idx = reinterpret_cast<uint16_t*>(dyn + 8 * npow_max);
+    uint8_t* mark = reinterpret_cast<uint8_t*>(dyn + 10 * npow_max);
     __shared__ int32_t part[kThreads];
 
     const int tid = threadIdx.x;
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void bsa_select_kernel(
     if (qlen <= 0 || q0 < kv0 || q0 + qlen > kv1 || (q0 - kv0) % (4 * kBN) != 0) return;
     const int len = kv1 - kv0;
     const int n = (len + kBN - 1) / kBN;
-    if (n > kBsaMaxKeyBlocks) return;                 // rejected on the host
+    if (n > npow_max) return;                         // never: npow_max covers every segment
     const int keep = max(1, n - static_cast<int>((static_cast<int64_t>(n) * sp_permille) / 1000));
     const int tbs = tb[seg];
     const int t0 = tbs + (q0 - kv0) / kBN;            // first 64-row block of the query block
@@ -195,11 +199,16 @@ __global__ __launch_bounds__(kThreads) void bsa_select_kernel(
 hipError_t launch_bsa_select(const int16_t* qsum, const int16_t* ksum, const float* qsc, const float* ksc,
                              const int32_t* cu, const int32_t* tb, const int32_t* items, int64_t num_items,
                              int num_seqs, int total_tokens, int num_heads, int64_t num_tiles,
-                             int sp_permille, int64_t list_stride, int32_t* lists, hipStream_t stream) {
+                             int sp_permille, int64_t list_stride, int32_t* lists, int max_key_blocks,
+                             hipStream_t stream) {
     if (num_items <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bsa_select_kernel, dim3(static_cast<unsigned>(num_items)), dim3(kThreads), 0, stream,
+    if (max_key_blocks > kBsaMaxKeyBlocks) return hipErrorInvalidValue;
+    int npow_max = 1;
+    while (npow_max < max_key_blocks) npow_max <<= 1;
+    hipLaunchKernelGGL(bsa_select_kernel, dim3(static_cast<unsigned>(num_items)), dim3(kThreads),
+                       static_cast<unsigned>(11 * npow_max), stream,
                        qsum, ksum, qsc, ksc, cu, tb, reinterpret_cast<const int4*>(items), num_seqs,
-                       total_tokens, num_heads, num_tiles, sp_permille, list_stride, lists);
+                       total_tokens, num_heads, num_tiles, sp_permille, list_stride, lists, npow_max);
     return hipGetLastError();
 }
 

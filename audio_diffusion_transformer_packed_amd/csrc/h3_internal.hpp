@@ -48,7 +48,8 @@ constexpr int kBsaMaxKeyBlocks = 4096;          // 64-key blocks per segment
 hipError_t launch_bsa_select(const int16_t* qsum, const int16_t* ksum, const float* qsc, const float* ksc,
                              const int32_t* cu, const int32_t* tb, const int32_t* items, int64_t num_items,
                              int num_seqs, int total_tokens, int num_heads, int64_t num_tiles,
-                             int sp_permille, int64_t list_stride, int32_t* lists, hipStream_t stream);
+                             int sp_permille, int64_t list_stride, int32_t* lists, int max_key_blocks,
+                             hipStream_t stream);
 size_t bsa_scratch_bytes(int num_seqs, int total_tokens, int num_heads, int64_t list_stride);
 hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            int64_t qs, int64_t ks, int64_t vs, int64_t os, const int32_t* cu,
