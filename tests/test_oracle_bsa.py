@@ -218,5 +218,6 @@ def test_quantised_single_block_matches_direct_formula():
     p = np.exp(logits - logits.max(axis=1, keepdims=True))
     vam = np.abs(v[:, 0]).max(axis=0)                                # per channel over the segment
     v8 = e4m3_round(448 * v[keys, 0] / vam[None, :])
-    ref = (e4m3_round(448 * p) @ v8) * (vam / 448)[None, :] / (448 * p.sum(axis=1, keepdims=True))
+    p8 = e4m3_round(448 * p)
+    ref = (p8 @ v8) * (vam / 448)[None, :] / p8.sum(axis=1, keepdims=True)
     assert np.max(np.abs(out[:, 0] - ref)) < 1e-12

@@ -220,3 +220,22 @@ def test_codes_match_torch_float32_pipeline():
         amax = xt.abs().amax(dim=0)
         ref = ((xt * 448.0) / amax[None]).to(torch.float8_e4m3fn).to(torch.float64)
         assert np.array_equal(vc[a:b], ref.numpy())
+
+
+def test_one_tile_matches_direct_formula_with_quantised_denominator():
+    """A segment of one key tile makes the online softmax a single step:
+    written out from the e4m3 definitions (codes from amax, S from the codes
+    and scales, P = e4m3(448 p), denominator the row sum of the same P), the
+    emulation must agree to rounding."""
+    rng = np.random.default_rng(71)
+    q, k, v = (np.asarray(rng.standard_normal((60, 1, 128)), dtype=np.float64) for _ in range(3))
+    out, _ = fp8_attn_emulated_ref(q, k, v, [0, 60])
+    aq, ak = np.abs(q).max(), np.abs(k).max()
+    qc, kc = e4m3_round(448 * q[:, 0] / aq), e4m3_round(448 * k[:, 0] / ak)
+    s = (qc @ kc.T) * (aq / 448) * (ak / 448) / math.sqrt(128)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    av = np.abs(v[:, 0]).max(axis=0)
+    vc = e4m3_round(448 * v[:, 0] / av)
+    p8 = e4m3_round(448 * p)
+    ref = (p8 @ vc) * (av / 448)[None, :] / p8.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(out[:, 0] - ref)) < 1e-12
