@@ -9,7 +9,8 @@
 // pass (fp8_quant.hip):
 //   S = (Q8 K8^T) s_q s_k * scale, online softmax over 64-key tiles in
 //   ascending order with the exact running row max m,
-//   P8 = e4m3(448 p), p = exp(S - m), l = sum of the unquantised p,
+//   P8 = e4m3(448 p), p = exp(S - m), l = the row sum of P8 (one more P V
+//   MFMA against an all-ones operand, in place of 32 fp32 adds per tile),
 //   O = (sum P8 V8) s_v / (448 l).
 // Skip rule: for the 32 query rows of a wave, a key tile other than the
 // segment's first is skipped (no exp, no P V) when every valid row has its
@@ -237,7 +238,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) oacc[b] = f32x16{};
     float m_run = -1e30f;     // running row max, exp2 units (finite start: no inf - inf)
-    float l_run = 0.f;        // partial sum of 448 p over this lane's keys
+    // row sums of P8 = e4m3(448 p): one more P V MFMA with an all-ones A
+    // operand (e4m3 1.0 = 0x38) puts every row's sum into each of the lane's
+    // 16 accumulators; only element 0 is read (and rescaled)
+    f32x16 lacc = f32x16{};
+    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};
     int nskip = 0;
     f32x16 sc[2] = {f32x16{}, f32x16{}};
     i32x8 pf = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -278,6 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
 #pragma unroll
             for (int db = 0; db < 4; ++db)
                 oacc[db] = mfma_fp8(read32(vl + 2048 * db + vro[0], vl + 2048 * db + vro[1]), pf, oacc[db]);
+            lacc = mfma_fp8(ones, pf, lacc);
         }
     };
     // softmax block S(u): tile max, skip rule, rescale, P of tile u
@@ -313,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
             const float m_new = fmaxf(m_run, tmax);
             if (__any(m_new > m_run)) {               // wave-uniform
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
+                lacc[0] *= alpha;
 #pragma unroll
                 for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
             }
@@ -321,7 +328,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
             // 448 p = exp2(s ct - m + log2 448); bytes in B-operand order:
             // byte 16 b + r of this lane holds score sc[b][r]
             const float mb = m_new - kLog2_448;
-            float ps = 0.f;
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
                 const int b = w >> 2, r = 4 * (w & 3);
@@ -329,12 +335,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 1], ct, -mb));
                 const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 2], ct, -mb));
                 const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 3], ct, -mb));
-                ps += (p0 + p1) + (p2 + p3);
                 int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
                 word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
                 pf[w] = word;
             }
-            l_run += ps;
         }
     };
 
@@ -384,8 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     if (g0) bar();
 
     // ---- O = acc s_v / l; lane holds channels 32 db + 8 r4 + 4 g + [0, 4) ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / lacc[0];
     if (qvalid) {
         uint16_t* op = o + static_cast<int64_t>(q0 + qrow_local) * os + static_cast<int64_t>(head) * kD;
         const float* svp = vsc + (static_cast<int64_t>(seg) * num_heads + head) * kD;

@@ -132,7 +132,8 @@ H3_API h3_status h3_varlen_bookkeeping(const int32_t* cu_seqlens_dev,
  * Skip-Softmax) quantises Q and K to OCP e4m3 with one scale per (head,
  * 64-token block aligned to the segment start), V with one scale per
  * (segment, head, channel), runs Q K^T and P V on fp8 MFMA with P encoded
- * as e4m3(448 * p), and, with skip_softmax set, skips exp and P V for a key
+ * as e4m3(448 * p) and the softmax denominator the row sum of those encoded
+ * values (the weights the numerator uses), and, with skip_softmax set, skips exp and P V for a key
  * tile of 64 keys when every valid row of a 32-row query group has its tile
  * maximum more than skip_threshold (natural-log units) below its running
  * maximum (never the segment's first key tile). fp8 needs head_dim 128.
@@ -223,7 +224,7 @@ H3_API h3_status h3_fp8_quantize(const void* q, const void* k, const void* v,
  *    in block j, each step one float64 rounding in this order; equal scores
  *    go to the lower block index.
  *  - Attention over the kept blocks only, in ascending order: S = (Q8 K8)
- *    sq sk scale, online softmax, P = e4m3(448 p), l from the unrounded p,
+ *    sq sk scale, online softmax, P = e4m3(448 p), l the row sum of P,
  *    O = (sum P V8) sv / (448 l); fp32 accumulation, bf16 output.
  * q, k, v, out, strides, cu_seqlens as for h3_attn_varlen; head_dim must be
  * 128; a segment may hold at most 4096 * 64 = 262144 tokens
