@@ -36,7 +36,7 @@ granularity. Readings taken here, each the plainest one the rest supports:
     taken in float64 by both this oracle and the kernel, in the same order.
   * Attention over the kept key blocks only, in ascending block order, with
     the fp8 path's online softmax: S = (Q8 . K8) sq sk scale, running row
-    max m, P = e4m3(448 exp(S - m)), l summed from the same P (P / 448),
+    max m, p = exp(S - m), P = e4m3(448 p), l the sum of the unquantised p,
     O = (sum P V8) sv / (448 l).
 With quantize=False every rounding is the identity (codes are the values,
 scales 1) and the result is the exact softmax over the kept keys.
@@ -203,7 +203,7 @@ def bsa_attn_emulated_ref(q, k, v, cu: Sequence[int], sparsity: float,
             m_new = np.maximum(m, sc.max(axis=1))
             alpha = np.exp(m - m_new)
             p = np.exp(sc - m_new[:, None])
-            l = l * alpha + rnd(p_mul * p).sum(axis=1) / p_mul
+            l = l * alpha + p.sum(axis=1)
             acc = acc * alpha[:, None] + rnd(p_mul * p) @ vc[j0:j1, h]
             m = m_new
         out[rows, h] = acc * vs[s, h][None, :] / (p_mul * l[:, None])

@@ -22,10 +22,11 @@ skip threshold. This module follows this reading:
     segment start (the last block of a segment may be short);
   * V: one scale per (segment, head, channel), so it factors out of the sum
     over keys and is applied once at the end;
-  * P: e4m3(448 * p) with p = exp(s - m) relative to the running row max,
-    the softmax denominator l summed from the same quantised values
-    (l = sum of e4m3(448 p) / 448), so that numerator and denominator use
-    one set of weights and each row of the quantised weights sums to one;
+  * P: e4m3(448 * p) with p = exp(s - m) relative to the running row max
+    feeds the P x V product; the softmax denominator l is the sum of the
+    unquantised p (only the operands of the two products are encoded; the
+    row sum is an accumulation, kept at full precision like the products'
+    accumulators);
   * tiles: keys in blocks of 64 from the segment start, in ascending order,
     online softmax across them;
   * skip rule: a key tile is skipped for a group of query rows iff it is not
@@ -216,7 +217,7 @@ def fp8_attn_emulated_ref(q, k, v, cu: Sequence[int], scale: Optional[float] = N
             m_new = np.maximum(m, tmax)
             alpha = np.exp(m - m_new)
             p = np.exp(sc - m_new[:, None])
-            l = l * alpha + rnd(p_mul * p).sum(axis=1) / p_mul
+            l = l * alpha + p.sum(axis=1)
             acc = acc * alpha[:, None] + rnd(p_mul * p) @ vc[j0:j1, h, :]
             m = m_new
         out[rows, h, :] = acc * vs[s, h][None, :] / (p_mul * l[:, None])

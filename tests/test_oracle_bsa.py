@@ -200,7 +200,8 @@ def test_dense_fallback_window():
 def test_quantised_single_block_matches_direct_formula():
     """With one kept key block the online softmax is one step: written out
     directly from the INT8 / e4m3 definitions (codes and scales recomputed
-    here from amax), the emulation must agree to rounding."""
+    here from amax; P = e4m3(448 p) in the numerator, the unquantised p in
+    the denominator), the emulation must agree to rounding."""
     from oracle import e4m3_round
     cu = [0, 256]
     q, k, v = _qkv(256, 1, 128, 11)
@@ -219,5 +220,8 @@ def test_quantised_single_block_matches_direct_formula():
     vam = np.abs(v[:, 0]).max(axis=0)                                # per channel over the segment
     v8 = e4m3_round(448 * v[keys, 0] / vam[None, :])
     p8 = e4m3_round(448 * p)
-    ref = (p8 @ v8) * (vam / 448)[None, :] / p8.sum(axis=1, keepdims=True)
+    ref = (p8 @ v8) * (vam / 448)[None, :] / (448 * p.sum(axis=1, keepdims=True))
     assert np.max(np.abs(out[:, 0] - ref)) < 1e-12
+    # the denominator summed from the encoded P is a different reading
+    other = (p8 @ v8) * (vam / 448)[None, :] / p8.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(other - ref)) > 1e-6

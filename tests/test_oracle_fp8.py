@@ -222,11 +222,13 @@ def test_codes_match_torch_float32_pipeline():
         assert np.array_equal(vc[a:b], ref.numpy())
 
 
-def test_one_tile_matches_direct_formula_with_quantised_denominator():
+def test_one_tile_matches_direct_formula():
     """A segment of one key tile makes the online softmax a single step:
     written out from the e4m3 definitions (codes from amax, S from the codes
-    and scales, P = e4m3(448 p), denominator the row sum of the same P), the
-    emulation must agree to rounding."""
+    and scales, P = e4m3(448 p) in the numerator, denominator the sum of the
+    unquantised p), the emulation must agree to rounding. The denominator
+    summed from the encoded P instead is measurably different, so this pin
+    tells the two readings apart."""
     rng = np.random.default_rng(71)
     q, k, v = (np.asarray(rng.standard_normal((60, 1, 128)), dtype=np.float64) for _ in range(3))
     out, _ = fp8_attn_emulated_ref(q, k, v, [0, 60])
@@ -237,5 +239,7 @@ def test_one_tile_matches_direct_formula_with_quantised_denominator():
     av = np.abs(v[:, 0]).max(axis=0)
     vc = e4m3_round(448 * v[:, 0] / av)
     p8 = e4m3_round(448 * p)
-    ref = (p8 @ vc) * (av / 448)[None, :] / p8.sum(axis=1, keepdims=True)
+    ref = (p8 @ vc) * (av / 448)[None, :] / (448 * p.sum(axis=1, keepdims=True))
     assert np.max(np.abs(out[:, 0] - ref)) < 1e-12
+    other = (p8 @ vc) * (av / 448)[None, :] / p8.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(other - ref)) > 1e-6
