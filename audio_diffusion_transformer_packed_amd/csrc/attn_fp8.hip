@@ -505,8 +505,6 @@ hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t*
     return hipGetLastError();
 }
 
-bool fp8_attention_available() { return true; }
-
 size_t fp8_scratch_bytes(int num_seqs, int total_tokens, int num_heads, int head_dim) {
     if (head_dim != kD) return 0;
     return fp8_scratch_layout(num_seqs, total_tokens, num_heads).total;

@@ -18,8 +18,11 @@
 //    v_mfma_f32_32x32x16_bf16, 128 accumulators per lane);
 //  * the MFMA computes C^T = W a^T: the W tile is the A operand, the
 //    activation tile the B operand, so each lane ends up owning one output
-//    row and four consecutive output columns per register group (8-byte
-//    stores, no LDS round trip in the epilogue);
+//    row and four consecutive output columns per register group;
+//  * epilogue: each wave stages its 128 x 64 outputs (after the fused
+//    operation, rounded to bf16) through 16 KB of LDS, XOR-swizzled, and
+//    writes them back row-contiguous with 16-byte stores, 8 lanes per
+//    128-byte row segment;
 //  * tiles move global -> LDS with buffer_load_dwordx4 ... lds (no staging
 //    registers; scalar buffer descriptors, so the loads cost no vector
 //    address arithmetic), double buffered; each wave instruction fills 1 KB = 8 rows

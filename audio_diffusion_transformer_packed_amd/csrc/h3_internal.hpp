@@ -32,7 +32,6 @@ hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint1
                                hipStream_t stream, int16_t* qsum = nullptr, int16_t* ksum = nullptr);
 
 // fp8 attention over the quantised codes (attn_fp8.hip)
-bool fp8_attention_available();
 size_t fp8_scratch_bytes(int num_seqs, int total_tokens, int num_heads, int head_dim);
 hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            uint16_t* o, int64_t qs, int64_t ks, int64_t vs, int64_t os,

@@ -104,8 +104,6 @@ h3_status check_opts(const h3_attn_opts* opts, int32_t head_dim) {
     if (opts == nullptr) return ok();
     if (opts->precision != H3_ATTN_BF16 && opts->precision != H3_ATTN_FP8_E4M3)
         return fail(H3_ERR_INVALID_ARGUMENT, "unknown attention precision %d", opts->precision);
-    if (opts->precision == H3_ATTN_FP8_E4M3 && !h3::fp8_attention_available())
-        return fail(H3_ERR_UNSUPPORTED, "fp8 attention is not available in this build");
     if (opts->precision == H3_ATTN_FP8_E4M3 && head_dim != 128)
         return fail(H3_ERR_UNSUPPORTED, "fp8 attention needs head_dim 128 (got %d)", head_dim);
     if (opts->precision == H3_ATTN_BF16 && opts->skip_softmax)

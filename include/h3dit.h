@@ -133,7 +133,9 @@ H3_API h3_status h3_varlen_bookkeeping(const int32_t* cu_seqlens_dev,
  * 64-token block aligned to the segment start), V with one scale per
  * (segment, head, channel), runs Q K^T and P V on fp8 MFMA with P encoded
  * as e4m3(448 * p) and the softmax denominator the row sum of those encoded
- * values (the weights the numerator uses), and, with skip_softmax set, skips exp and P V for a key
+ * values (summed on the matrix core; a sum of the unquantised p, the plainer
+ * reading of the method, differs from it by about 2e-3 relative Frobenius
+ * error), and, with skip_softmax set, skips exp and P V for a key
  * tile of 64 keys when every valid row of a 32-row query group has its tile
  * maximum more than skip_threshold (natural-log units) below its running
  * maximum (never the segment's first key tile). fp8 needs head_dim 128.
@@ -170,9 +172,10 @@ H3_API h3_status h3_attn_varlen(const void* q, const void* k, const void* v, voi
  * h3_attn_varlen with H3_ATTN_FP8_E4M3 runs it internally; it is exported so
  * the codes can be inspected and reused.
  *
- * Format OCP e4m3fn (max 448). scale = amax / 448 (1 when amax == 0),
- * code = round-to-nearest-even(x / scale) clamped to +-448, the division in
- * IEEE fp32. Q and K: one scale per (64-token block aligned to the segment
+ * Format OCP e4m3fn (max 448). scale = amax / 448 stored as the fp32
+ * quotient (1 when amax == 0); code = round-to-nearest-even(448 x / amax) of
+ * the exact quotient (not of x divided by the rounded scale, which can move
+ * an exact midpoint off the tie), saturating at +-448; 0 when amax == 0. Q and K: one scale per (64-token block aligned to the segment
  * start, head); V: one scale per (segment, head, channel). head_dim must be
  * 128. q, k, v as for h3_attn_varlen (bf16, token strides in elements,
  * multiples of 8, 16-byte aligned). T = sum over segments of ceil(L_s / 64)
@@ -224,7 +227,8 @@ H3_API h3_status h3_fp8_quantize(const void* q, const void* k, const void* v,
  *    in block j, each step one float64 rounding in this order; equal scores
  *    go to the lower block index.
  *  - Attention over the kept blocks only, in ascending order: S = (Q8 K8)
- *    sq sk scale, online softmax, P = e4m3(448 p), l the row sum of P,
+ *    sq sk scale, online softmax, P = e4m3(448 p), l the row sum of P
+ *    (as in the fp8 attention: within about 2e-3 of a sum of unquantised p),
  *    O = (sum P V8) sv / (448 l); fp32 accumulation, bf16 output.
  * q, k, v, out, strides, cu_seqlens as for h3_attn_varlen; head_dim must be
  * 128; a segment may hold at most 4096 * 64 = 262144 tokens
