@@ -4,8 +4,18 @@
 // vLLM-Omni", section "System-wide optimizations in vLLM-Omni", GPU output
 // preparation bullet: converted once on the GPU, a quarter of the bytes).
 // Value map (the pages give none; the decoded-video convention for [-1, 1]):
-//   u = round_half_even(255 * clamp(x * 0.5 + 0.5, 0, 1)), NaN -> 0,
-// in fp32 in that order.
+//   u = round_half_even(255 * clamp(x / 2 + 1/2, 0, 1)), NaN -> 0,
+// the exact value for the fp32 input (no intermediate rounding decides a
+// level). For x in (-1, 1), y = 127.5 + 127.5 x: the product is exact in
+// fp64 and one fma rounds the sum once. Writing x = M 2^E (M of 24 bits),
+// y - (k + 1/2) = (255 x + 254 - 2k) / 2 is a nonzero multiple of 2^(E-1)
+// unless x = 0, so for |x| >= 2^-20 (E >= -43) y stays at least 2^-44 from
+// every midpoint, more than the fma's rounding (<= 2^-46 below 256) can
+// cross, and rint of the fp64 value is the exact level. For |x| < 2^-20 the
+// level is 127 for negative x and 128 otherwise (x = 0 is the tie 127.5,
+// which goes to the even 128). An fp32 evaluation of x * 0.5 + 0.5 would
+// instead send every negative x above -2^-25 to 128 and misplace 674 other
+// fp32 inputs next to midpoints.
 //
 // HBM-bound (4 C bytes read and C written per pixel). Vector path: a wave
 // takes 1024 consecutive pixels, reads them with 1 KB-contiguous 16-byte
@@ -19,12 +29,12 @@ namespace h3 {
 namespace {
 
 __device__ __forceinline__ uint32_t to_u8(float x) {
-#pragma clang fp contract(off)
-    float y = x * 0.5f;
-    y = y + 0.5f;
-    y = fminf(fmaxf(y, 0.0f), 1.0f);       // NaN -> 0: max returns the non-NaN operand
-    const float z = y * 255.0f;
-    return static_cast<uint32_t>(__builtin_rintf(z));
+    double y = __builtin_fma(127.5, static_cast<double>(x), 127.5);
+    y = __builtin_fmin(__builtin_fmax(y, 0.0), 255.0);   // in range for the conversion
+    uint32_t u = static_cast<uint32_t>(__builtin_rint(y));
+    u = __builtin_fabsf(x) < 0x1p-20f ? (x < 0.0f ? 127u : 128u) : u;
+    u = x >= 1.0f ? 255u : u;
+    return x > -1.0f ? u : 0u;              // x <= -1, -inf and NaN give 0
 }
 
 // One wave per 1024 consecutive pixels of one batch entry: load q (0..3) of

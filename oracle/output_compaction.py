@@ -12,11 +12,18 @@ the GPU, to uint8 BTHWC (a quarter of the bytes) before they go to the host.
 The pages give neither the value range nor the rounding. Reading taken (the
 usual convention for decoded video in [-1, 1]):
     u = round_half_even(255 * clamp(x / 2 + 1/2, 0, 1)),
-evaluated in IEEE float32 in exactly this order (x * 0.5, + 0.5, clamp,
-* 255, round to nearest even), the precision the kernel uses, so that both
-sides take the integer decision in the same arithmetic; NaN maps to 0
-(IEEE max/min return the non-NaN operand). Layout: x[b, c, t, h, w] ->
-u[b, t, h, w, c].
+the exact value of this expression for the float32 input x (no intermediate
+rounding), NaN mapping to 0. Layout: x[b, c, t, h, w] -> u[b, t, h, w, c].
+
+For x in (-1, 1) the level is RNE(255 (1 + x) / 2). Writing x = M 2^E with M
+an integer of at most 24 bits, 255 (1 + x) / 2 = 255 (2^-E + M) / 2^(1-E),
+an integer over a power of two, so the rounding is decided exactly on
+integers: quotient, remainder, and the remainder compared with half the
+divisor (equal: a tie, which goes to the even quotient). This is done for
+|x| >= 2^-16 (2^-E <= 2^40, so everything fits in int64); for smaller |x| the
+value lies within 0.002 of 127.5, below it exactly when x < 0, so the level
+is 127 for negative x and 128 otherwise (x = 0 gives 127.5 exactly, a tie,
+and goes to the even 128).
 """
 from __future__ import annotations
 
@@ -26,14 +33,26 @@ F32 = np.float32
 
 
 def frames_to_uint8_values(x) -> np.ndarray:
-    """The per-element map in float32 (any shape), as uint8."""
+    """The exact per-element map (any shape), as uint8."""
     x = np.asarray(x, dtype=F32)
-    y = (x * F32(0.5)).astype(F32)
-    y = (y + F32(0.5)).astype(F32)
-    y = np.where(np.isnan(y), F32(0.0), y)
-    y = np.minimum(np.maximum(y, F32(0.0)), F32(1.0)).astype(F32)
-    z = (y * F32(255.0)).astype(F32)
-    return np.rint(z).astype(np.uint8)      # rint: round half to even
+    xd = x.astype(np.float64)                       # exact
+    out = np.zeros(x.shape, dtype=np.uint8)         # x <= -1, -inf and NaN give 0
+    out[xd >= 1.0] = 255
+    inner = (xd > -1.0) & (xd < 1.0)
+    v = xd[inner]
+    m, e = np.frexp(v)                              # v = m 2^e, 0.5 <= |m| < 1 (or 0)
+    big_m = np.rint(np.ldexp(m, 24)).astype(np.int64)   # exact integer, |M| < 2^24
+    shift = 24 - e.astype(np.int64)                 # v = M 2^-shift
+    u = np.where(v < 0, 127, 128).astype(np.int64)  # |v| < 2^-16
+    ok = shift <= 40
+    s = shift[ok]
+    num = 255 * ((np.int64(1) << s) + big_m[ok])    # 255 (1 + v) 2^s, an exact integer
+    q = num >> (s + 1)                              # floor(255 (1 + v) / 2)
+    r = num & ((np.int64(1) << (s + 1)) - 1)
+    half = np.int64(1) << s
+    u[ok] = q + (r > half) + ((r == half) & ((q & 1) == 1))
+    out[inner] = u.astype(np.uint8)
+    return out
 
 
 def frames_to_uint8_bthwc(x) -> np.ndarray:

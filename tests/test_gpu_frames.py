@@ -1,6 +1,7 @@
 """GPU parity of the decoded-frame compaction (h3_frames_to_uint8_bthwc):
-every byte equal to the oracle's float32 map, on the vector path and the
-per-pixel path."""
+every byte equal to the oracle's exact map, on the vector path and the
+per-pixel path, including inputs next to every rounding midpoint and tiny
+values of both signs (where a float32 evaluation would differ)."""
 import numpy as np
 import pytest
 
@@ -21,15 +22,27 @@ def ops():
     return o
 
 
+def _special_values() -> np.ndarray:
+    """Exact ties (0 -> 127.5), the ends, NaN, infinities, the float32
+    values next to each of the 255 midpoints (255 (1 + x) / 2 = k + 1/2) and
+    tiny values of both signs down to the smallest subnormal."""
+    vals = [0.0, -0.0, 1.0, -1.0, np.nan, np.inf, -np.inf, 2.0 / 255 - 1]
+    for k in range(255):
+        c = np.float32((2 * k + 1) / 255.0 - 1.0)
+        vals += [np.nextafter(c, np.float32(-2)), c, np.nextafter(c, np.float32(2))]
+    for n in list(range(17, 150, 3)) + [149]:
+        vals += [2.0 ** -n, -(2.0 ** -n)]
+    return np.array(vals, np.float32)
+
+
 def _frames(shape, seed):
-    """Values over [-1.5, 1.5] plus exact ties (0 -> 127.5), the ends, NaN
-    and infinities."""
+    """Values over [-1.5, 1.5] with the special values scattered in."""
     rng = np.random.default_rng(seed)
     x = rng.uniform(-1.5, 1.5, size=shape).astype(np.float32)
     flat = x.reshape(-1)
-    idx = rng.choice(flat.size, size=min(flat.size, 64), replace=False)
-    flat[idx] = np.resize(np.array([0.0, -0.0, 1.0, -1.0, np.nan, np.inf, -np.inf, 2.0 / 255 - 1],
-                                   np.float32), idx.size)
+    sp = _special_values()
+    idx = rng.choice(flat.size, size=min(flat.size, sp.size), replace=False)
+    flat[idx] = sp[:idx.size]
     return x
 
 
