@@ -225,7 +225,9 @@ H3_API h3_status h3_fp8_quantize(const void* q, const void* k, const void* v,
  *    of sq_b I_bj) sk_j) / n_j, I_bj the integer dot product of the INT8
  *    code sums of Q block b and key block j, sq/sk the scales, n_j the keys
  *    in block j, each step one float64 rounding in this order; equal scores
- *    go to the lower block index.
+ *    go to the lower block index (this equals the ranking by the exact
+ *    scores unless two scores at the keep boundary lie within float64
+ *    rounding of each other).
  *  - Attention over the kept blocks only, in ascending order: S = (Q8 K8)
  *    sq sk scale, online softmax, P = e4m3(448 p), l the row sum of P
  *    (as in the fp8 attention: within about 2e-3 of a sum of unquantised p),

@@ -27,13 +27,14 @@ granularity. Readings taken here, each the plainest one the rest supports:
     Q and K. With Qsum_b[d] the sum of the codes of 64-row Q block b (of the
     query block's up to four), Ksum_j[d] that of key block j, I_bj their
     exact integer dot product, sq_b / sk_j the stored float32 scales and n_j
-    the keys in block j, the ranking score is
-        score_j = ((sum over b ascending of sq_b * I_bj) * sk_j) / n_j,
-    every operation one IEEE float64 rounding in this order (the common
-    positive factors, 1/(query rows) and the softmax scale, are dropped:
-    they do not change the ranking). The keep(n) highest scores are kept,
-    equal scores going to the lower block index. This integer decision is
-    taken in float64 by both this oracle and the kernel, in the same order.
+    the keys in block j, the ranking score is the exact rational
+        score_j = (sum over b of sq_b * I_bj) * sk_j / n_j
+    (the common positive factors, 1/(query rows) and the softmax scale, are
+    dropped: they do not change the ranking). The keep(n) highest scores are
+    kept, equal scores going to the lower block index. The ranking is
+    computed from float64 estimates with an error bound, and every block
+    whose estimate is too close to the keep boundary for the bound to decide
+    is ranked again with exact rational arithmetic (fractions.Fraction).
   * Attention over the kept key blocks only, in ascending block order, with
     the fp8 path's online softmax: S = (Q8 . K8) sq sk scale, running row
     max m, p = exp(S - m), P = e4m3(448 p), l the sum of the unquantised p,
@@ -44,6 +45,7 @@ scales 1) and the result is the exact softmax over the kept keys.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
@@ -103,6 +105,17 @@ def _segment_blocks(cu: np.ndarray, size: int):
     return out
 
 
+def _exact_scores(qblocks, ksum_i, sk, n_j, idx):
+    """Exact rational scores of key blocks `idx`: (sum_b sq_b I_bj) sk_j / n_j."""
+    out = {}
+    for j in idx:
+        tot = Fraction(0)
+        for sq, qsum in qblocks:
+            tot += Fraction(float(sq)) * int(ksum_i[j] @ qsum)
+        out[int(j)] = tot * Fraction(float(sk[j])) / int(n_j[j])
+    return out
+
+
 def select_kv_blocks(q8, q_scale, k8, k_scale, cu: Sequence[int], sparsity: float,
                      query_blocks: Optional[Sequence[Tuple[int, int]]] = None
                      ) -> Dict[Tuple[int, int], np.ndarray]:
@@ -111,6 +124,14 @@ def select_kv_blocks(q8, q_scale, k8, k_scale, cu: Sequence[int], sparsity: floa
     q8, k8: int codes [N, H, D]; q_scale, k_scale: float32 [num_64_blocks, H].
     Returns {(head, first token of the query block): ascending int64 array of
     key-block indices within the segment}.
+
+    Ranking: float64 estimates est_j of the exact scores with a bound e_j on
+    their error (each float64 operation adds at most 2^-53 of the running
+    magnitude; 2^-46 of the sum of |terms| is used). With K the keep(n)
+    leading blocks of the estimate order and R the rest, a block of K whose
+    est - e exceeds every est + e of R is in the exact top keep(n) (it beats
+    every block of R), and a block of R whose est + e is below every est - e
+    of K is not; the blocks left are ranked by their exact scores.
     """
     q8 = np.asarray(q8, dtype=np.int64)
     k8 = np.asarray(k8, dtype=np.int64)
@@ -127,18 +148,33 @@ def select_kv_blocks(q8, q_scale, k8, k_scale, cu: Sequence[int], sparsity: floa
         a, b = int(cu[s]), int(cu[s + 1])
         kstarts = list(range(a, b, KV_BLOCK))
         n = len(kstarts)
-        ksum = np.stack([k8[j0:j0 + KV_BLOCK, h].sum(axis=0) if j0 + KV_BLOCK <= b
-                         else k8[j0:b, h].sum(axis=0) for j0 in kstarts])            # [n, D]
-        n_j = np.array([min(KV_BLOCK, b - j0) for j0 in kstarts], dtype=_F)
-        sk = np.array([k_scale[index64[j0], h] for j0 in kstarts], dtype=np.float32).astype(_F)
+        ksum = np.stack([k8[j0:min(b, j0 + KV_BLOCK), h].sum(axis=0) for j0 in kstarts])   # [n, D]
+        n_j = np.array([min(KV_BLOCK, b - j0) for j0 in kstarts], dtype=np.int64)
+        sk = np.array([k_scale[index64[j0], h] for j0 in kstarts], dtype=np.float32)
+        qblocks = [(np.float32(q_scale[index64[t], h]), q8[t:min(b, t + QK_SCALE_BLOCK), h].sum(axis=0))
+                   for t in range(t0, min(b, t0 + Q_BLOCK), QK_SCALE_BLOCK)]
         acc = np.zeros(n)
-        for t in range(t0, min(b, t0 + Q_BLOCK), QK_SCALE_BLOCK):
-            qsum = q8[t:min(b, t + QK_SCALE_BLOCK), h].sum(axis=0)                   # [D]
-            dots = ksum @ qsum                                                     # exact int64
-            acc = acc + np.float64(q_scale[index64[t], h]) * dots.astype(_F)
-        scores = (acc * sk) / n_j
-        order = sorted(range(n), key=lambda j: (-float(scores[j]), j))
-        out[(h, t0)] = np.array(sorted(order[:keep_count(n, sparsity)]), dtype=np.int64)
+        mag = np.zeros(n)
+        for sq, qsum in qblocks:
+            term = np.float64(sq) * (ksum @ qsum).astype(_F)          # the dot products are exact int64
+            acc += term
+            mag += np.abs(term)
+        est = acc * sk.astype(_F) / n_j
+        err = mag * np.abs(sk.astype(_F)) / n_j * 2.0 ** -46
+        keep = keep_count(n, sparsity)
+        order = np.lexsort((np.arange(n), -est))
+        kept, rest = order[:keep], order[keep:]
+        if rest.size:
+            hi_rest = np.max(est[rest] + err[rest])
+            lo_kept = np.min(est[kept] - err[kept])
+            if lo_kept <= hi_rest:
+                amb = np.concatenate([kept[est[kept] - err[kept] <= hi_rest],
+                                      rest[est[rest] + err[rest] >= lo_kept]])
+                sure = kept[est[kept] - err[kept] > hi_rest]
+                exact = _exact_scores(qblocks, ksum, sk, n_j, amb)
+                ranked = sorted(exact, key=lambda j: (-exact[j], j))
+                kept = np.concatenate([sure, np.array(ranked[:keep - sure.size], dtype=np.int64)])
+        out[(h, t0)] = np.sort(kept).astype(np.int64)
     return out
 
 

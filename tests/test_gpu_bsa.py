@@ -1,7 +1,8 @@
 """GPU parity of block-sparse attention with INT8 Q/K and FP8 V
 (h3_attn_block_sparse): the kept-block lists bit for bit against the
-oracle's selection (an integer decision both sides take in float64 in the
-same order), the output against the float64 emulation at the 1e-2 bar, and
+oracle's exact selection (the kernel ranks float64 scores, which can only
+differ from the exact ranking on scores within float64 rounding of each
+other at the keep boundary; none occur in these inputs), the output against the float64 emulation at the 1e-2 bar, and
 against the exact softmax over the same kept keys with the emulation's own
 distance as the floor (5e-3 margin), the literal 5e-2 outcome printed."""
 import numpy as np

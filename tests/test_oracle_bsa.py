@@ -225,3 +225,27 @@ def test_quantised_single_block_matches_direct_formula():
     # the denominator summed from the encoded P is a different reading
     other = (p8 @ v8) * (vam / 448)[None, :] / p8.sum(axis=1, keepdims=True)
     assert np.max(np.abs(other - ref)) > 1e-6
+
+
+def test_selection_decides_differences_below_float64_resolution():
+    """Scores are compared exactly: two key blocks whose scores differ by
+    2^-60 at magnitude 100 (far below float64 resolution) are told apart.
+    Q block 0 (scale 1) sums to e_0, Q block 1 (scale 2^-60) to e_1; key
+    block 0 sums to 100 e_0, key block 1 to 100 e_0 + e_1, both scales 1, so
+    score_0 = 100 and score_1 = 100 + 2^-60. In float64 both are 100.0 and
+    the tie would go to block 0; the exact ranking keeps block 1."""
+    d = 8
+    q8 = np.zeros((128, 1, d), np.int64)
+    k8 = np.zeros((128, 1, d), np.int64)
+    q8[0, 0, 0] = 1
+    q8[64, 0, 1] = 1
+    k8[0, 0, 0] = 100
+    k8[64, 0, 0] = 100
+    k8[64, 0, 1] = 1
+    qs = np.array([[1.0], [2.0 ** -60]], np.float32)
+    ks = np.array([[1.0], [1.0]], np.float32)
+    assert 1.0 * 100 + float(qs[1, 0]) * 0 == 1.0 * 100 + float(qs[1, 0]) * 1      # equal in float64
+    sel = select_kv_blocks(q8, qs, k8, ks, [0, 128], 0.5)                          # keep 1 of 2
+    assert sel[(0, 0)].tolist() == [1]
+    k8[64, 0, 1] = -1                                                              # now 100 - 2^-60
+    assert select_kv_blocks(q8, qs, k8, ks, [0, 128], 0.5)[(0, 0)].tolist() == [0]
