@@ -40,6 +40,11 @@ def _cu(lens):
     ([0, 1, 2, 63, 64, 65, 127, 128, 129], 3, 128),
     ([129, 128, 127, 65, 64, 63, 2, 1, 0, 65, 64], 2, 64),
     ([5] * 1500 + [7, 0, 3], 2, 4),
+    ([57960], 24, 256),
+    ([93740], 24, 256),
+    ([32260], 24, 256),
+    ([0, 1, 255, 256, 257, 511, 512, 513, 128, 129, 0], 3, 256),
+    ([704, 512], 4, 256),
 ])
 def test_bookkeeping_bit_exact(dev, ops, lens, heads, block_m):
     announce(f"bookkeeping lens[:4]={lens[:4]} B={len(lens)} H={heads} BM={block_m}")
@@ -187,3 +192,83 @@ def test_attention_5s_32k_sampled_rows(dev, ops):
     got = to_np(out)[rows]
     ref = oracle.attn_varlen_ref(inp.q.f32, inp.k.f32, inp.v.f32, inp.cu_seqlens, rows=rows)
     compare(got, ref, "attn 32k sampled")
+
+
+# --------------------------------------------------------------------------
+# peaked attention: the running max rises after the first key tile, so the
+# kernel's lazy rescale (alpha applied to a non-zero O and l) runs
+# --------------------------------------------------------------------------
+
+LOG2E = 1.4426950408889634
+
+
+def _max_rise_log2(q, k, cu, rows=None):
+    """Per (row, head): (max logit over the segment) - (max logit over the
+    segment's first 64 keys), in log2 units of the softmax argument."""
+    n, heads, d = q.shape
+    scale = 1.0 / np.sqrt(d)
+    rises = []
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        r = np.arange(a, b) if rows is None else np.array([t for t in rows if a <= t < b])
+        if r.size == 0:
+            continue
+        for h in range(heads):
+            lg = (q[r, h].astype(np.float64) @ k[a:b, h].astype(np.float64).T) * scale * LOG2E
+            rises.append(lg.max(axis=1) - lg[:, :64].max(axis=1))
+    return np.concatenate(rises)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_attention_frame_local_row_max_moves(dev, ops, head_dim):
+    """Frame-local inputs: queries gain ~12 nats (17 in log2) with keys of
+    their own 1008-token frame, so every query past the first frame meets a
+    much larger logit in a later key tile than in the first; the output must
+    still meet the bar against the exact oracle."""
+    lens = [2600, 0, 1300]
+    cu = _cu(lens)
+    heads = 2
+    announce(f"attention frame-local D={head_dim} lens={lens} (rescale path)")
+    inp = h3synth.frame_local_attention_inputs(cu, heads, head_dim, seed=91)
+    rise = _max_rise_log2(inp.q.f32, inp.k.f32, cu)
+    print(f"[parity] frame-local D={head_dim}: rows with max rise > 16 log2 after tile 0: "
+          f"{(rise > 16).mean():.3f}, largest rise {rise.max():.1f}")
+    assert (rise > 16).mean() > 0.3
+    out = _run_attn(ops, dev, inp, heads, head_dim)
+    ref = oracle.attn_varlen_ref(inp.q.f32, inp.k.f32, inp.v.f32, cu)
+    compare(to_np(out), ref, f"attn frame-local D={head_dim}")
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_attention_dominant_key_in_last_tile(dev, ops, head_dim):
+    """q = lambda k_j for a key j in the last tile of a 1,100-token segment
+    (and of a second, ragged segment): the logit of j rises some 30 log2
+    units above everything seen before, so the rescale runs on the last tile
+    with O and l already accumulated over 17 tiles; the output tends to
+    v_j and must meet the bar elementwise against the exact oracle."""
+    lens = [1100, 1037]
+    cu = _cu(lens)
+    heads = 2
+    n = int(cu[-1])
+    announce(f"attention dominant key in the last tile D={head_dim} lens={lens}")
+    inp = h3synth.attention_inputs(cu, np.zeros((n, 3), np.int32), heads, head_dim, seed=93)
+    q = inp.q.f32.copy()
+    rng = np.random.default_rng(94)
+    for s, j_off in ((0, 1090), (1, 1030)):
+        a = int(cu[s])
+        j = a + j_off
+        rows = a + rng.choice(lens[s], size=lens[s] // 2, replace=False)
+        for h in range(heads):
+            kj = inp.k.f32[j, h].astype(np.float64)
+            lam = 21.0 * np.sqrt(head_dim) / float(kj @ kj)   # q . k_j / sqrt(D) ~ 21 nats
+            q[rows, h] = (lam * kj).astype(np.float32)
+    qb = h3synth.Bf16Array.from_f32(q)
+    rise = _max_rise_log2(qb.f32, inp.k.f32, cu)
+    print(f"[parity] dominant key D={head_dim}: rows with max rise > 16 log2: {(rise > 16).mean():.3f}")
+    assert (rise > 16).mean() > 0.3
+    inp2 = h3synth.AttnInputs(cu, inp.grid, qb, inp.k, inp.v, inp.w_q, inp.w_k, inp.seed)
+    out = _run_attn(ops, dev, inp2, heads, head_dim)
+    ref = oracle.attn_varlen_ref(qb.f32, inp.k.f32, inp.v.f32, cu)
+    compare(to_np(out), ref, f"attn dominant last-tile key D={head_dim}")

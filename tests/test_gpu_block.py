@@ -164,7 +164,7 @@ def test_block_deterministic_and_packing_invariant(dev, ops):
         assert np.array_equal(alone, o1[a:b])
 
 
-@pytest.mark.parametrize("name,nrows", [("block_10s_58k", 24), ("block_15s_94k", 8)])
+@pytest.mark.parametrize("name,nrows", [("block_10s_58k", 24), ("block_15s_94k", 24)])
 def test_block_full_size_sampled_rows(dev, ops, name, nrows):
     """The benchmarked shape and launch; sampled tokens of every stage
     against the exact oracle (keys/values of the whole segment in float64)."""

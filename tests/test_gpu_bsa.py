@@ -16,6 +16,11 @@ pytestmark = pytest.mark.gpu
 
 REL_FP8_EXACT = 5e-2
 FLOOR_MARGIN = 5e-3
+# elementwise bar against the emulation: the fp8 bar (5e-2 of max(1, |ref|));
+# the kernel's softmax denominator is the sum of the encoded P, the
+# emulation's the sum of the unquantised p, which moves single outputs of
+# peaked rows by up to about 2 % (relative Frobenius error held to 1e-2)
+SCALED_ABS_FP8 = 5e-2
 D = 128
 
 
@@ -69,7 +74,7 @@ def _check_output(got, q, k, v, cu, sparsity, name, query_blocks=None, mask=None
     if mask is not None:
         got, emu, exact = (np.where(mask, a, 0.0) for a in (got, emu, exact))
     assert np.all(np.isfinite(got))
-    compare(got, emu, f"{name} vs emulation")
+    compare(got, emu, f"{name} vs emulation", scaled_abs=SCALED_ABS_FP8)
     rg, re_ = _relf(got, exact), _relf(emu, exact)
     print(f"[parity] {name}: relF gpu-vs-exact-sparse={rg:.3e} emulation-vs-exact (floor)={re_:.3e} "
           f"literal 5e-2 bar {'met' if rg <= REL_FP8_EXACT else 'not met (floor)'}")

@@ -167,6 +167,10 @@ ADVERSARIAL = [0, 1, 2, 63, 64, 65, 127, 128, 129]
     (ADVERSARIAL[::-1] + [65, 64], 2, 64),
     ([5, 5, 5, 0, 5], 1, 2),
     ([], 4, 128),
+    ([32260], 24, 256),
+    ([57960], 24, 256),
+    ([93740], 24, 256),
+    ([0, 1, 255, 256, 257, 511, 512, 513, 128, 129, 0], 3, 256),
 ])
 def test_host_schedule_matches_spec(lib, lens, heads, block_m):
     from audio_diffusion_transformer_packed_amd.ops import build_schedule_host
