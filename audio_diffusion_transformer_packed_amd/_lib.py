@@ -26,6 +26,7 @@ EXPORTS = (
     "h3_status_string", "h3_last_error_message", "h3_abi_version", "h3_build_schedule_host",
     "h3_varlen_bookkeeping_workspace_size", "h3_varlen_bookkeeping",
     "h3_attn_varlen_workspace_size", "h3_attn_varlen_num_items", "h3_attn_varlen",
+    "h3_attn_varlen_noalloc",
     "h3_fp8_num_tiles", "h3_fp8_quantize_workspace_size", "h3_fp8_quantize",
     "h3_attn_block_sparse_list_stride", "h3_attn_block_sparse_workspace_size",
     "h3_attn_block_sparse", "h3_qk_rmsnorm_rope", "h3_modulation", "h3_adaln_rmsnorm_modulate", "h3_linear_bf16",
@@ -91,6 +92,8 @@ def _declare(lib):
         "h3_attn_varlen_num_items": (C.c_int, [P, I32, I32, P]),
         "h3_attn_varlen": (C.c_int, [P, P, P, P, I64, I64, I64, I64, P, P, I32, I32, I32, I32, P,
                                      P, SZ, P]),
+        "h3_attn_varlen_noalloc": (C.c_int, [P, P, P, P, I64, I64, I64, I64, P, P, I32, I32, I32,
+                                             I32, P, P]),
         "h3_fp8_num_tiles": (C.c_int, [P, I32, P]),
         "h3_fp8_quantize_workspace_size": (SZ, [I32, I32, I32]),
         "h3_fp8_quantize": (C.c_int, [P, P, P, I64, I64, I64, P, P, I32, I32, I32, I32, P, P, P, P,

@@ -13,10 +13,14 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/h3dit.h"
 #include "h3_internal.hpp"
+
+// Fixed device scratch of h3_attn_varlen_noalloc (see noalloc_scratch below).
+static __device__ __attribute__((aligned(256))) char scratch[H3_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -163,6 +167,73 @@ h3_status check_gemm_shape(int64_t m, int64_t n, int64_t k, int64_t n_mult) {
     return ok();
 }
 
+// Argument checks shared by h3_attn_varlen and h3_attn_varlen_noalloc (all
+// but the workspace); *nothing is set when there is no work (N = 0).
+h3_status check_attn_args(const void* q, const void* k, const void* v, const void* out,
+                          int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                          int64_t o_tok_stride, const int32_t* cu_seqlens_dev,
+                          const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                          int32_t num_heads, int32_t head_dim, const h3_attn_opts* opts,
+                          bool* nothing) {
+    *nothing = false;
+    h3_status st = check_cu(cu_seqlens_host, num_seqs, total_tokens);
+    if (st != H3_OK) return st;
+    if (num_heads <= 0) return fail(H3_ERR_INVALID_ARGUMENT, "num_heads=%d <= 0", num_heads);
+    if (!head_dim_ok(head_dim)) return fail(H3_ERR_UNSUPPORTED, "head_dim=%d (64 or 128 only)", head_dim);
+    st = check_opts(opts, head_dim);
+    if (st != H3_OK) return st;
+    if (total_tokens == 0) {
+        *nothing = true;
+        return ok();
+    }
+    if (!q || !k || !v || !out || !cu_seqlens_dev)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
+    const int64_t row = static_cast<int64_t>(num_heads) * head_dim;
+    if (q_tok_stride < row || k_tok_stride < row || v_tok_stride < row || o_tok_stride < row)
+        return fail(H3_ERR_INVALID_ARGUMENT, "token strides must be >= num_heads * head_dim = %lld",
+                    (long long)row);
+    if ((q_tok_stride | k_tok_stride | v_tok_stride | o_tok_stride) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+         reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out)) & 15)
+        return fail(H3_ERR_UNSUPPORTED, "q/k/v/out must be 16-byte aligned");
+    const int32_t precision = opts ? opts->precision : H3_ATTN_BF16;
+    if (opts && opts->skip_counts && precision != H3_ATTN_FP8_E4M3)
+        return fail(H3_ERR_UNSUPPORTED, "skip_counts needs the fp8 path");
+    return ok();
+}
+
+// ---- fixed scratch of h3_attn_varlen_noalloc ----
+// One copy of the file-scope array `scratch` lives on every GPU the library
+// is loaded onto, for the life of the process. In host code its name is a
+// host-side stand-in, not a device address: kernels get the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device (on the first call with that device current) and kept here.
+constexpr size_t kNoAllocScratchBytes = H3_NOALLOC_SCRATCH_BYTES;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+h3_status noalloc_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(H3_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & (kAlign - 1)))
+            return fail(H3_ERR_HIP, "scratch address %p is not 256-byte aligned", p);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -276,35 +347,48 @@ H3_API h3_status h3_attn_varlen(const void* q, const void* k, const void* v, voi
                                 int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                                 int32_t head_dim, const h3_attn_opts* opts, void* workspace,
                                 size_t workspace_bytes, void* hip_stream) {
-    h3_status st = check_cu(cu_seqlens_host, num_seqs, total_tokens);
-    if (st != H3_OK) return st;
-    if (num_heads <= 0) return fail(H3_ERR_INVALID_ARGUMENT, "num_heads=%d <= 0", num_heads);
-    if (!head_dim_ok(head_dim)) return fail(H3_ERR_UNSUPPORTED, "head_dim=%d (64 or 128 only)", head_dim);
-    st = check_opts(opts, head_dim);
-    if (st != H3_OK) return st;
-    if (total_tokens == 0) return ok();
-    if (!q || !k || !v || !out || !cu_seqlens_dev)
-        return fail(H3_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
-    const int64_t row = static_cast<int64_t>(num_heads) * head_dim;
-    if (q_tok_stride < row || k_tok_stride < row || v_tok_stride < row || o_tok_stride < row)
-        return fail(H3_ERR_INVALID_ARGUMENT, "token strides must be >= num_heads * head_dim = %lld",
-                    (long long)row);
-    if ((q_tok_stride | k_tok_stride | v_tok_stride | o_tok_stride) & 7)
-        return fail(H3_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements");
-    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
-         reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out)) & 15)
-        return fail(H3_ERR_UNSUPPORTED, "q/k/v/out must be 16-byte aligned");
+    bool nothing = false;
+    h3_status st = check_attn_args(q, k, v, out, q_tok_stride, k_tok_stride, v_tok_stride,
+                                   o_tok_stride, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                   total_tokens, num_heads, head_dim, opts, &nothing);
+    if (st != H3_OK || nothing) return st;
     const int32_t precision = opts ? opts->precision : H3_ATTN_BF16;
     const size_t need = attn_plan(num_seqs, total_tokens, num_heads, head_dim, precision).total;
     if (workspace_bytes < need || workspace == nullptr)
         return fail(H3_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
         return fail(H3_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-    if (opts && opts->skip_counts && precision != H3_ATTN_FP8_E4M3)
-        return fail(H3_ERR_UNSUPPORTED, "skip_counts needs the fp8 path");
     return run_attention(q, k, v, out, q_tok_stride, k_tok_stride, v_tok_stride, o_tok_stride,
                          cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens, num_heads,
                          head_dim, opts, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+H3_API h3_status h3_attn_varlen_noalloc(const void* q, const void* k, const void* v, void* out,
+                                        int64_t q_tok_stride, int64_t k_tok_stride,
+                                        int64_t v_tok_stride, int64_t o_tok_stride,
+                                        const int32_t* cu_seqlens_dev,
+                                        const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                        int32_t total_tokens, int32_t num_heads,
+                                        int32_t head_dim, const h3_attn_opts* opts,
+                                        void* hip_stream) {
+    bool nothing = false;
+    h3_status st = check_attn_args(q, k, v, out, q_tok_stride, k_tok_stride, v_tok_stride,
+                                   o_tok_stride, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                   total_tokens, num_heads, head_dim, opts, &nothing);
+    if (st != H3_OK || nothing) return st;
+    const int32_t precision = opts ? opts->precision : H3_ATTN_BF16;
+    const size_t need = attn_plan(num_seqs, total_tokens, num_heads, head_dim, precision).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(H3_ERR_WORKSPACE_TOO_SMALL,
+                    "h3_attn_varlen_noalloc: these sizes need %zu bytes of scratch, more than its "
+                    "fixed %zu bytes; use h3_attn_varlen with a workspace", need,
+                    static_cast<size_t>(kNoAllocScratchBytes));
+    void* ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st != H3_OK) return st;
+    return run_attention(q, k, v, out, q_tok_stride, k_tok_stride, v_tok_stride, o_tok_stride,
+                         cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens, num_heads,
+                         head_dim, opts, ws, static_cast<hipStream_t>(hip_stream));
 }
 
 // ---- block-sparse attention, INT8 Q/K + FP8 V ----

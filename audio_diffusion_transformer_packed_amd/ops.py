@@ -140,6 +140,33 @@ def attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: t
     return out
 
 
+def attn_varlen_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                        cu_host, out: torch.Tensor, precision: str = "bf16",
+                        skip_softmax: bool = False, skip_threshold: float = 8.0,
+                        softmax_scale: float = 0.0,
+                        skip_counts: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """attn_varlen through h3_attn_varlen_noalloc: no workspace, the
+    library's fixed per-GPU scratch instead; `out` must be given, so the
+    call allocates nothing."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _need(t, name, BF16, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    n, heads, d = q.shape
+    strides = [_token_view(t, nm, heads, d) for nm, t in (("q", q), ("k", k), ("v", v), ("out", out))]
+    cu = _host_cu(cu_host)
+    prec = {"bf16": L.H3_ATTN_BF16, "fp8": L.H3_ATTN_FP8_E4M3}[precision]
+    if skip_counts is not None:
+        _need(skip_counts, "skip_counts", torch.int32, dev)
+    opts = AttnOpts(prec, int(skip_softmax), float(skip_threshold), float(softmax_scale),
+                    None if skip_counts is None else skip_counts.data_ptr())
+    with torch.cuda.device(dev):       # the library looks up the scratch of the current device
+        check(lib().h3_attn_varlen_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), *strides,
+                                           _ptr(cu_seqlens), cu.ctypes.data_as(C.c_void_p),
+                                           cu.size - 1, n, heads, d, C.byref(opts), _stream(dev)))
+    return out
+
+
 def fp8_num_tiles(cu_host) -> int:
     """T = sum over segments of ceil(L_s / 64): the key tiles of the fp8 layouts."""
     cu = _host_cu(cu_host)

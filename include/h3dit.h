@@ -166,6 +166,40 @@ H3_API h3_status h3_attn_varlen(const void* q, const void* k, const void* v, voi
                                 size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * h3_attn_varlen without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same computation, arguments,
+ * layouts, validation and errors as h3_attn_varlen (bf16 or fp8, skip
+ * options, skip_counts); the work list, the bookkeeping scratch and the fp8
+ * code buffers live in a library-owned device array of
+ * H3_NOALLOC_SCRATCH_BYTES (64 MiB), one per GPU, reserved when the library
+ * is loaded onto that GPU and held until the process ends. Nothing is
+ * allocated or freed, by the library or any library it calls.
+ *  - The array's device address is looked up once per device, on the first
+ *    call made with that device current (hipGetSymbolAddress); the stream
+ *    must belong to the current device.
+ *  - A call that needs more scratch than the array holds (its need is
+ *    h3_attn_varlen_workspace_size for the same arguments: bf16 fits any
+ *    size the other limits allow up to about 4 million work items; fp8 fits
+ *    while N x H stays below about 170,000 token-heads) returns
+ *    H3_ERR_WORKSPACE_TOO_SMALL before any launch.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (nothing in it needs to start at zero: every word a
+ *    call reads, that call writes first). Calls ordered on one stream are
+ *    safe; calls that overlap in time on one GPU (other streams, other
+ *    threads without ordering) race on the array.
+ * ---------------------------------------------------------------------- */
+#define H3_NOALLOC_SCRATCH_BYTES (64u << 20)
+H3_API h3_status h3_attn_varlen_noalloc(const void* q, const void* k, const void* v, void* out,
+                                        int64_t q_tok_stride, int64_t k_tok_stride,
+                                        int64_t v_tok_stride, int64_t o_tok_stride,
+                                        const int32_t* cu_seqlens_dev,
+                                        const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                        int32_t total_tokens, int32_t num_heads,
+                                        int32_t head_dim, const h3_attn_opts* opts,
+                                        void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * fp8 quantisation of Q, K and V, the first step of the fp8 attention path
  * ([FastH3-EN] sparse & quantized attention bullet; [FastH3-ZH] section
  * "其他加速路径：有损但可控": SAGE runs the attention computation in FP8).

@@ -95,6 +95,28 @@ def test_attention_argument_errors(lib):
     assert _attn(lib, [0], 0, ws_bytes=0) == L.H3_OK
 
 
+def _attn_noalloc(lib, cu_list, n, heads=2, d=128, opts=None, q=0x1000):
+    a, p = _cu(cu_list)
+    st = (heads * d,) * 4
+    return lib.h3_attn_varlen_noalloc(C.c_void_p(q), C.c_void_p(0x2000), C.c_void_p(0x3000),
+                                      C.c_void_p(0x4000), *st, C.c_void_p(0x5000), p, a.size - 1, n,
+                                      heads, d, None if opts is None else C.byref(opts), None)
+
+
+def test_attention_noalloc_argument_errors(lib):
+    """The no-workspace variant applies the same checks before anything
+    else, and rejects sizes beyond its fixed 64 MiB scratch before touching
+    the device."""
+    assert _attn_noalloc(lib, [1, 5], 5) == L.H3_ERR_INVALID_ARGUMENT
+    assert _attn_noalloc(lib, [0, 10], 10, d=96) == L.H3_ERR_UNSUPPORTED
+    assert _attn_noalloc(lib, [0, 10], 10, q=0) == L.H3_ERR_INVALID_ARGUMENT
+    fp8 = L.AttnOpts(L.H3_ATTN_FP8_E4M3, 0, 8.0, 0.0, None)
+    assert lib.h3_attn_varlen_workspace_size(1, 8000, 24, 128, C.byref(fp8)) > (64 << 20)
+    assert _attn_noalloc(lib, [0, 8000], 8000, heads=24, opts=fp8) == L.H3_ERR_WORKSPACE_TOO_SMALL
+    assert b"64" in lib.h3_last_error_message() or b"scratch" in lib.h3_last_error_message()
+    assert _attn_noalloc(lib, [0, 0], 0) == L.H3_OK
+
+
 def test_workspace_sizes(lib):
     small = lib.h3_attn_varlen_workspace_size(1, 100, 2, 128, None)
     big = lib.h3_attn_varlen_workspace_size(1, 100000, 24, 128, None)
