@@ -96,13 +96,16 @@ __device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c) {
 // covers every position once); the work item visits only the kept key
 // blocks of its query block, lists[(head, first 64-row block)][0 .. keep),
 // in ascending order; no skip rule.
-template <bool BSA>
+// SKIP: the skip rule is compiled in (dense path only); a skipped tile
+// saves its exp, convert and rescale and its P V MFMAs (a wave-uniform
+// branch).
+template <bool BSA, bool SKIP>
 __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
     const float* __restrict__ qsc, const float* __restrict__ ksc, const float* __restrict__ vsc,
     uint16_t* __restrict__ o, int64_t os, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ tb, const int4* __restrict__ items, int num_seqs,
-    int total_tokens, int num_heads, int64_t num_tiles, float scale_log2, int skip,
+    int total_tokens, int num_heads, int64_t num_tiles, float scale_log2,
     float thr_log2, int32_t* __restrict__ skip_counts, const int32_t* __restrict__ lists,
     int64_t list_stride, int sp_permille) {
     // K stage 0, K stage 1, V stage 0, V stage 1
@@ -247,10 +250,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     int nskip = 0;
     f32x16 sc[2] = {f32x16{}, f32x16{}};
     i32x8 pf = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-    bool pv_pending = false;  // P of the previous tile waits for its P V (not skipped)
+    bool pv_run = false;      // SKIP: the previous tile was not skipped (wave-uniform)
 
     // MFMA block M(u): S^T(u) from K stage u & 1 (u < T), O += P(u-1) V(u-1)
-    // from V stage (u-1) & 1 (u >= 1, tile not skipped)
+    // from V stage (u-1) & 1 (u >= 1, tile u-1 not skipped)
     auto mfma_block = [&](int u) __attribute__((always_inline)) {
         if (!wave_active) return;
         if (u < nsel) {
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
                         sc[b] = mfma_fp8(read32(kl + 4096 * b + kro[c][0], kl + 4096 * b + kro[c][1]), qf[c], sc[b]);
             }
         }
-        if (u >= 1 && pv_pending) {
+        if (u >= 1 && __builtin_expect(!SKIP || pv_run, 1)) {
             const char* vl = smem + 2 * kKT + ((u - 1) & 1) * kVT;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
@@ -307,24 +310,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float ct = sq * sk;          // exp2 units per raw score
         const float tmax = mx * ct;
+        float m_new = fmaxf(m_run, tmax);
         bool run_tile = true;
-        if (skip && u > 0) {
-            const bool below = !qvalid || tmax < m_run - thr_log2;
-            if (__all(below)) {                       // wave-uniform
-                run_tile = false;
-                ++nskip;
+        if constexpr (SKIP) {
+            if (u > 0) {
+                const bool below = !qvalid || tmax < m_run - thr_log2;
+                if (__builtin_expect(__all(below), 0)) {   // wave-uniform
+                    run_tile = false;
+                    ++nskip;
+                    m_new = m_run;                    // a skipped tile moves no maximum
+                }
             }
         }
-        pv_pending = run_tile;
-        if (run_tile) {
-            const float m_new = fmaxf(m_run, tmax);
-            if (__any(m_new > m_run)) {               // wave-uniform
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                lacc[0] *= alpha;
+        if (__any(m_new > m_run)) {                   // wave-uniform
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            lacc[0] *= alpha;
 #pragma unroll
-                for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-            }
-            m_run = m_new;
+            for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+        }
+        m_run = m_new;
+        if (__builtin_expect(run_tile, 1)) {
             // 448 p = exp2(s ct - m + log2 448); bytes in B-operand order:
             // byte 16 b + r of this lane holds score sc[b][r]
             const float mb = m_new - kLog2_448;
@@ -340,6 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
                 pf[w] = word;
             }
         }
+        if constexpr (SKIP) pv_run = run_tile;
     };
 
     // ---- prologue: K(0) in LDS, every wave one 1 KB block ----
@@ -498,10 +504,10 @@ hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t*
     e = launch_bsa_select(qsum, ksum, qsc, ksc, cu, tb, items, num_items, num_seqs, total_tokens,
                           num_heads, tiles, sp_permille, list_stride, lists, max_blocks, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(static_cast<unsigned>(num_items)), dim3(kThreads), 0,
-                       stream, q8, k8, v8t, qsc, ksc, vsc, o, os, cu, tb,
+    hipLaunchKernelGGL((attn_fp8_kernel<true, false>), dim3(static_cast<unsigned>(num_items)),
+                       dim3(kThreads), 0, stream, q8, k8, v8t, qsc, ksc, vsc, o, os, cu, tb,
                        reinterpret_cast<const int4*>(items), num_seqs, total_tokens, num_heads,
-                       tiles, softmax_scale * kLog2e, 0, 0.f, nullptr, lists, list_stride, sp_permille);
+                       tiles, softmax_scale * kLog2e, 0.f, nullptr, lists, list_stride, sp_permille);
     return hipGetLastError();
 }
 
@@ -533,11 +539,18 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t*
                                        v8t, qsc, ksc, vsc, ws, stream);
     if (e != hipSuccess) return e;
     const int32_t* tb = static_cast<const int32_t*>(ws);   // tile prefix sums from the quantise pass
-    hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3(static_cast<unsigned>(num_items)), dim3(kThreads), 0,
-                       stream, q8, k8, v8t, qsc, ksc, vsc, o, os, cu, tb,
-                       reinterpret_cast<const int4*>(items), num_seqs, total_tokens, num_heads,
-                       tiles, softmax_scale * kLog2e, skip, skip_threshold * kLog2e, skip_counts,
-                       nullptr, int64_t{0}, 0);
+    const dim3 grid(static_cast<unsigned>(num_items));
+    if (skip) {
+        hipLaunchKernelGGL((attn_fp8_kernel<false, true>), grid, dim3(kThreads), 0, stream, q8, k8,
+                           v8t, qsc, ksc, vsc, o, os, cu, tb, reinterpret_cast<const int4*>(items),
+                           num_seqs, total_tokens, num_heads, tiles, softmax_scale * kLog2e,
+                           skip_threshold * kLog2e, skip_counts, nullptr, int64_t{0}, 0);
+    } else {
+        hipLaunchKernelGGL((attn_fp8_kernel<false, false>), grid, dim3(kThreads), 0, stream, q8, k8,
+                           v8t, qsc, ksc, vsc, o, os, cu, tb, reinterpret_cast<const int4*>(items),
+                           num_seqs, total_tokens, num_heads, tiles, softmax_scale * kLog2e,
+                           skip_threshold * kLog2e, skip_counts, nullptr, int64_t{0}, 0);
+    }
     return hipGetLastError();
 }
 

@@ -55,6 +55,25 @@ def gemm_flops(n, c, ffn, b):
     return 2.0 * n * c * (3 * c + c + 2 * ffn) + 2.0 * n * ffn * c + 2.0 * b * c * 6 * c
 
 
+def block_roofline(n, c, ffn, heads, head_dim, lengths, b):
+    """Roofline time of one block, sum over its kernels of max(FLOP / bf16
+    peak, HBM bytes / HBM peak), in ms, with the per-kernel terms."""
+    hd = heads * head_dim
+    p, bw = PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBS * 1e9
+    terms = {
+        "modulation": (2.0 * b * c * 6 * c, 6 * c * c * 2.0),
+        "adaln_x2": (0.0, 2 * 2.0 * n * c * 2),
+        "qkv_gemm": (2.0 * n * c * 3 * c, 2.0 * (n * c + 3 * c * c + 3 * n * c)),
+        "qk_rmsnorm_rope": (0.0, 4.0 * n * c * 2 + 12.0 * n),
+        "attention": (attention_flops(lengths, heads, head_dim), 4.0 * n * hd * 2),
+        "out_proj": (2.0 * n * c * c, 2.0 * (3 * n * c + c * c)),
+        "swiglu_gemm": (2.0 * n * c * 2 * ffn, 2.0 * (n * c + 2 * ffn * c + n * ffn)),
+        "down_gemm": (2.0 * n * ffn * c, 2.0 * (n * ffn + ffn * c + 2 * n * c)),
+    }
+    ms = {k: max(f / p, by / bw) * 1e3 for k, (f, by) in terms.items()}
+    return sum(ms.values()), ms
+
+
 def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
@@ -177,6 +196,8 @@ def main():
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-mx", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the other workloads (5 s attention, 15 s block, frame-local fp8)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this hot path runs on one GPU; --gpus must be 1 "
@@ -301,6 +322,26 @@ def main():
                                                    out=taps["h2"])),
             flops=2.0 * n * wl.ffn * c)
 
+        # The vendor library (torch.nn.functional.linear -> hipBLASLt) on the
+        # same four products, without the fused epilogues: the comparison
+        # for the fused GEMMs above (SwiGLU: the gate and up products as one
+        # [N, 2I] GEMM; the residual GEMMs: the plain product).
+        import torch.nn.functional as F
+        w_gu = torch.cat([w["w_gate"], w["w_up"]], dim=0)
+        lib_cmp = {}
+        for nm, a_in, w_in, ours in (("qkv_gemm", taps["h"], w["w_qkv"], "qkv_gemm"),
+                                     ("out_proj", taps["o"], w["w_o"], "out_proj_gated_residual"),
+                                     ("swiglu_gate_up", taps["h2"], w_gu, "swiglu_gemm"),
+                                     ("down", taps["a"], w["w_down"], "down_gated_residual")):
+            fl = 2.0 * a_in.shape[0] * a_in.shape[1] * w_in.shape[0]
+            t = sampler(lambda: F.linear(a_in, w_in), it, False)
+            lib_cmp[nm] = {"library_ms": round(t["median"], 4),
+                           "library_tflops": round(fl / (t["median"] * 1e-3) / 1e12, 2),
+                           "fused_ms": stages[ours]["ms"],
+                           "fused_over_library": round(t["median"] / stages[ours]["ms"], 4)}
+        del w_gu
+        stages["gemm_library_comparison"] = lib_cmp
+
     # Attention at one rank's share of an 8-way head split (3 of the 24 heads,
     # all 57,960 tokens): 681 work items on 256 CUs, where the last partial
     # wave of work items shows.
@@ -361,6 +402,7 @@ def main():
                "attention_kernel_ms": round(ms_k, 4),
                "attention_kernel_frac_fp8_peak": round(f_attn / (ms_k * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
                "skip_attention_ms": round(ms_fp8_skip, 4),
+               "skip_cost_when_nothing_skipped": round(ms_fp8_skip / ms_fp8 - 1.0, 4),
                "skip_fraction": round(skipped / pairs, 5),
                "skip_threshold": 8.0}
         rec("fp8_quantize", tq, nbytes=q_bytes)
@@ -466,6 +508,87 @@ def main():
             "speedup_vs_mxfp8_block": round(ms_mx / ms_l, 3)}
         del blk_mx, ws_mx, out_mx, blk_l, ws_l
 
+    # Other workloads of the method, timed as one leg each.
+    legs = {}
+    if not args.no_legs:
+        rl_ms, rl_terms = block_roofline(n, c, wl.ffn, wl.heads, wl.head_dim, wl.lengths, b)
+        legs["block_10s_58k_roofline"] = {"roofline_ms": round(rl_ms, 3),
+                                          "frac_roofline": round(rl_ms / ms_step, 4),
+                                          "terms_ms": {k: round(v, 4) for k, v in rl_terms.items()}}
+        # attention only, 5 s clip: 32,260 tokens, 24 x 128, i.i.d. N(0,1)
+        log("leg attn_5s_32k")
+        w1 = h3synth.WORKLOADS["attn_5s_32k"]
+        a1 = h3synth.workload_attention_inputs(w1.name)
+        cu1 = a1.cu_seqlens
+        q1, k1, v1 = dev_bf16(a1.q), dev_bf16(a1.k), dev_bf16(a1.v)
+        cu1_d = torch.from_numpy(cu1).to(dev)
+        o1 = torch.empty_like(q1)
+        ws1 = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        f1 = attention_flops(w1.lengths, w1.heads, w1.head_dim)
+        att1 = lambda: ops.attn_varlen(q1, k1, v1, cu1_d, cu1, out=o1, workspace=ws1)
+        for _ in range(args.warmup):
+            att1()
+        ms1 = timer(att1, max(3, args.steps))
+        legs["attn_5s_32k"] = {"workload": f"attn_5s_32k: one request of {int(cu1[-1])} tokens, "
+                                           f"{w1.heads} heads x {w1.head_dim}, bf16",
+                               "attention_ms": round(ms1, 4),
+                               "attention_tflops": round(f1 / (ms1 * 1e-3) / 1e12, 2),
+                               "attention_frac_bf16_peak": round(f1 / (ms1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del q1, k1, v1, o1, a1
+
+        # 15 s clip: the whole block at 93,740 tokens
+        log("leg block_15s_94k")
+        w3 = h3synth.WORKLOADS["block_15s_94k"]
+        b3 = h3synth.workload_block_inputs(w3.name)
+        wt3 = {nm: dev_bf16(getattr(b3, nm)) for nm in ops.WEIGHT_NAMES}
+        blk3 = ops.DitBlock(wt3, w3.heads, w3.head_dim, w3.ffn, h3synth.rope_split_for(w3.head_dim))
+        cu3 = b3.cu_seqlens
+        n3 = w3.total_tokens
+        x3, cond3 = dev_bf16(b3.x), dev_bf16(b3.cond)
+        cu3_d, grid3_d = torch.from_numpy(cu3).to(dev), torch.from_numpy(b3.grid).to(dev)
+        out3 = torch.empty_like(x3)
+        ws3 = torch.empty(blk3.workspace_bytes(len(cu3) - 1, n3), dtype=torch.uint8, device=dev)
+        step3 = lambda: blk3.forward(x3, cond3, cu3_d, cu3, grid3_d, out=out3, workspace=ws3)
+        for _ in range(args.warmup):
+            step3()
+        ms3 = timer(step3, args.steps)
+        f3 = attention_flops(w3.lengths, w3.heads, w3.head_dim) + gemm_flops(n3, w3.hidden, w3.ffn, len(cu3) - 1)
+        rl3, _ = block_roofline(n3, w3.hidden, w3.ffn, w3.heads, w3.head_dim, w3.lengths, len(cu3) - 1)
+        legs["block_15s_94k"] = {"workload": f"block_15s_94k: {n3} tokens, same block dims",
+                                 "block_ms": round(ms3, 4), "block_tflop": round(f3 / 1e12, 4),
+                                 "block_tflops": round(f3 / (ms3 * 1e-3) / 1e12, 2),
+                                 "roofline_ms": round(rl3, 3), "frac_roofline": round(rl3 / ms3, 4)}
+        del x3, cond3, out3, ws3, wt3, blk3, b3
+        torch.cuda.empty_cache()
+
+        # fp8 attention with skip-softmax on the labelled frame-local variant
+        # of the 10 s shape (q, k += mu u_frame per 1008-token block, a +12
+        # logit bonus inside a block), skip off and on
+        log("leg fp8 frame-local")
+        a4 = h3synth.frame_local_attention_inputs(cu, wl.heads, wl.head_dim, seed=inp.seed)
+        q4, k4, v4 = dev_bf16(a4.q), dev_bf16(a4.k), dev_bf16(a4.v)
+        o4 = torch.empty_like(q4)
+        ws4 = torch.empty(ops.attn_workspace_bytes(cu, n, wl.heads, wl.head_dim, "fp8"),
+                          dtype=torch.uint8, device=dev)
+        items4 = ops.attn_num_items(cu, wl.heads)
+        cnt4 = torch.zeros(items4, dtype=torch.int32, device=dev)
+        fp8_4 = lambda sk: ops.attn_varlen(q4, k4, v4, cu_d, cu, out=o4, precision="fp8", skip_softmax=sk,
+                                           skip_counts=cnt4, workspace=ws4)
+        fp8_4(False)
+        ms4_off = timer(lambda: fp8_4(False), max(3, args.steps))
+        fp8_4(True)
+        ms4_on = timer(lambda: fp8_4(True), max(3, args.steps))
+        pairs4 = wl.heads * sum(((L + 31) // 32) * ((L + 63) // 64) for L in wl.lengths)
+        frac4 = int(cnt4.sum().item()) / pairs4
+        legs["fp8_attention_frame_local"] = {
+            "workload": f"{wl.name} shape, labelled frame-local variant (+12 logit bonus within 1008-token "
+                        "blocks), fp8 e4m3 attention, skip threshold 8",
+            "skip_off_ms": round(ms4_off, 4), "skip_on_ms": round(ms4_on, 4),
+            "skip_fraction": round(frac4, 4), "speedup_from_skip": round(ms4_off / ms4_on, 4),
+            "dense_equiv_tflops_skip_on": round(f_attn / (ms4_on * 1e-3) / 1e12, 2)}
+        del q4, k4, v4, o4, ws4, a4
+        torch.cuda.empty_cache()
+
     traffic = load_traffic()
     result = {
         "metric": METRIC,
@@ -497,6 +620,7 @@ def main():
         "fp8_attention": fp8,
         "block_sparse_attention": bsa,
         "mxfp8_linears": mxr,
+        "legs": legs,
         "timed_wall_s": round(t_wall, 3),
     }
     if not args.no_cpu_baseline:
