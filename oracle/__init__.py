@@ -11,7 +11,8 @@ invariants, special cases or brute force):
   silu, swiglu_ref, gated_residual_ref, dit_block_ref, dit_block_rows_ref,
   e4m3_round, fp8_attn_emulated_ref, bf16_round (storage emulation),
   mx_scale_exponents, mx_quantize, mx_dequantize, mx_fake_quant, mx_linear_ref
-  (MXFP8 linears, OCP MX v1.0 reading), frames_to_uint8_values,
+  (MXFP8 linears, OCP MX v1.0 reading), e2m1_round, mxfp4_scale_exponents,
+  mxfp4_quantize, mxfp4_codes, mxfp4_fake_quant, mxfp4_linear_ref (MXFP4), frames_to_uint8_values,
   frames_to_uint8_bthwc (decoded-frame compaction), int8_quantize_qk_blocks,
   keep_count, select_kv_blocks, bsa_attn_emulated_ref, dense_fallback
   (block-sparse attention with INT8 Q/K and FP8 V).
@@ -25,8 +26,9 @@ from .h3_oracle import (MOD_CHUNKS, adaln_modulate_ref, bf16_round, attn_varlen_
                         segment_ids, silu, split_modulation, swiglu_ref, tile_offsets)
 from .fp8_attention import (e4m3_round, fp8_attn_emulated_ref, quantize_qk_blocks,
                             quantize_v_channels)
-from .mx_linear import (mx_dequantize, mx_fake_quant, mx_linear_ref, mx_quantize,
-                        mx_scale_exponents)
+from .mx_linear import (E2M1_VALUES, e2m1_round, mx_dequantize, mx_fake_quant, mx_linear_ref,
+                        mx_quantize, mx_scale_exponents, mxfp4_codes, mxfp4_fake_quant,
+                        mxfp4_linear_ref, mxfp4_quantize, mxfp4_scale_exponents)
 from .output_compaction import frames_to_uint8_bthwc, frames_to_uint8_values
 from .block_sparse_attention import (bsa_attn_emulated_ref, dense_fallback, int8_quantize_qk_blocks,
                                      keep_count, select_kv_blocks)
@@ -37,6 +39,7 @@ __all__ = [
     "rel_frobenius", "rmsnorm", "rope_3d", "schedule_ref", "segment_ids", "silu",
     "split_modulation", "swiglu_ref", "tile_offsets", "e4m3_round", "fp8_attn_emulated_ref",
     "quantize_qk_blocks", "quantize_v_channels", "mx_dequantize", "mx_fake_quant", "mx_linear_ref",
-    "mx_quantize", "mx_scale_exponents", "frames_to_uint8_bthwc", "frames_to_uint8_values",
+    "mx_quantize", "mx_scale_exponents", "E2M1_VALUES", "e2m1_round", "mxfp4_codes",
+    "mxfp4_fake_quant", "mxfp4_linear_ref", "mxfp4_quantize", "mxfp4_scale_exponents", "frames_to_uint8_bthwc", "frames_to_uint8_values",
     "bsa_attn_emulated_ref", "dense_fallback", "int8_quantize_qk_blocks", "keep_count", "select_kv_blocks",
 ]
