@@ -36,6 +36,8 @@ EXPORTS = (
     "h3_linear_mxfp8", "h3_linear_swiglu_mxfp8", "h3_linear_gated_residual_mxfp8",
     "h3_dit_block_workspace_size", "h3_dit_block_forward", "h3_dit_block_mx_workspace_size",
     "h3_dit_block_forward_mxfp8", "h3_dit_block_mx_bsa_workspace_size", "h3_dit_block_forward_mxfp8_bsa",
+    "h3_mx4_quantize_bf16", "h3_linear_mxfp4", "h3_linear_swiglu_mxfp4", "h3_linear_gated_residual_mxfp4",
+    "h3_dit_block_mx4_workspace_size", "h3_dit_block_forward_mxfp4",
 )
 
 
@@ -112,6 +114,13 @@ def _declare(lib):
         "h3_frames_to_uint8_bthwc": (C.c_int, [P, P, I64, I64, I64, I64, I64, P]),
         "h3_adaln_rmsnorm_modulate_mxfp8": (C.c_int, [P, P, P, P, P, I64, P, P, I32, I32, I32, F32,
                                                       P]),
+        "h3_mx4_quantize_bf16": (C.c_int, [P, I64, I64, I64, P, P, P]),
+        "h3_linear_mxfp4": (C.c_int, [P, P, P, P, P, I64, I64, I64, P]),
+        "h3_linear_swiglu_mxfp4": (C.c_int, [P, P, P, P, P, P, P, I64, I64, I64, P]),
+        "h3_linear_gated_residual_mxfp4": (C.c_int, [P, P, P, P, P, P, I64, P, I64, I64, I64, P, P, I32,
+                                                     P]),
+        "h3_dit_block_mx4_workspace_size": (SZ, [P, I32, I32]),
+        "h3_dit_block_forward_mxfp4": (C.c_int, [P, P, P, P, P, P, P, I32, I32, P, P, SZ, P]),
         "h3_mx_quantize_bf16": (C.c_int, [P, I64, I64, I64, P, P, P]),
         "h3_linear_mxfp8": (C.c_int, [P, P, P, P, P, I64, I64, I64, P]),
         "h3_linear_swiglu_mxfp8": (C.c_int, [P, P, P, P, P, P, P, P, I64, I64, I64, P]),

@@ -106,6 +106,17 @@ __device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, f32x16 c, int sa, in
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OP, sa, OP, sb);
 }
 
+// MXFP4 operands (E2M1, cbsz = blgp = 4): 32 elements (16 bytes) per lane,
+// the low half of the operand registers.
+template <int OP>
+__device__ __forceinline__ f32x16 mfma_mx4(uint4 a, uint4 b, f32x16 c, int sa, int sb) {
+    const i32x8 av = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z),
+                      static_cast<int>(a.w), 0, 0, 0, 0};
+    const i32x8 bv = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z),
+                      static_cast<int>(b.w), 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, OP, sa, OP, sb);
+}
+
 __device__ __forceinline__ i32x8 cat16(uint4 x, uint4 y) {
     return i32x8{static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z), static_cast<int>(x.w),
                  static_cast<int>(y.x), static_cast<int>(y.y), static_cast<int>(y.z), static_cast<int>(y.w)};
@@ -144,9 +155,16 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int mt, int nt
     tn = w / gm;
 }
 
-template <int EPI, bool MX>
+// operand formats
+constexpr int kFmtBf16 = 0, kFmtFp8 = 1, kFmtFp4 = 2;
+
+template <int EPI, int FMT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * (kStageBytes + (MX ? 2048 : 0))];
+    constexpr bool MX = FMT != kFmtBf16;
+    constexpr bool FP4 = FMT == kFmtFp4;
+    // scale bytes per row and K step: 4 E8M0 bytes (fp8), 8 (fp4)
+    constexpr int kSB = FP4 ? 8 : 4;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * (kStageBytes + (MX ? 256 * kSB * 2 : 0))];
     const char* __restrict__ A = static_cast<const char*>(p.a);
     const char* __restrict__ W = static_cast<const char*>(p.w);
     const char* __restrict__ W2 = static_cast<const char*>(p.w2);
@@ -157,8 +175,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
     const int32_t* __restrict__ cu = p.cu;
     const int num_seqs = p.num_seqs, mtiles = p.mtiles, ntiles = p.ntiles;
     uint16_t* __restrict__ Y = static_cast<uint16_t*>(p.y);
-    constexpr int kElem = MX ? 1 : 2;                  // bytes per operand element
-    const int64_t row_bytes = K * kElem;
+    // bytes per operand row: bf16 2, fp8 1, fp4 1/2 per element
+    const int64_t row_bytes = FP4 ? K / 2 : (MX ? K : 2 * K);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -216,16 +234,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
     // rows past the matrix read past-the-end zeros or the next K step's
     // first rows; their data rows load as zeros and are never stored.
     const int64_t ks_total = row_bytes / kStepBytes;
-    const int sa_bytes = MX ? static_cast<int>((ks_total * M - m0) * 4) : 0;
-    const int sw_bytes = MX ? static_cast<int>((ks_total * N - n0) * 4) : 0;
+    const int sa_bytes = MX ? static_cast<int>((ks_total * M - m0) * kSB) : 0;
+    const int sw_bytes = MX ? static_cast<int>((ks_total * N - n0) * kSB) : 0;
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(p.a_sc) + (MX ? m0 * 4 : 0), 0, sa_bytes, kBufferWord3);
+        const_cast<uint8_t*>(p.a_sc) + (MX ? m0 * kSB : 0), 0, sa_bytes, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rsw1 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(p.w_sc) + (MX ? n0 * 4 : 0), 0, sw_bytes, kBufferWord3);
+        const_cast<uint8_t*>(p.w_sc) + (MX ? n0 * kSB : 0), 0, sw_bytes, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rsw2 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(EPI == kEpiSwiGLU ? p.w2_sc : p.w_sc) + (MX ? n0 * 4 : 0), 0, sw_bytes,
+        const_cast<uint8_t*>(EPI == kEpiSwiGLU ? p.w2_sc : p.w_sc) + (MX ? n0 * kSB : 0), 0, sw_bytes,
         kBufferWord3);
-    constexpr int kScaleBytes = MX ? 2048 : 0;
+    // per stage: the W rows' scale records, then the activation rows'
+    constexpr int kScaleBytes = MX ? 2 * 256 * kSB : 0;
     constexpr int kStage = kStageBytes + kScaleBytes;
 
     // per-wave constant sources (selected once, so they stay in scalar registers)
@@ -234,9 +253,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
     // MX scales: every wave moves 256 B per K step (4 per lane, no branch):
     // waves 0-3 the W rows' dwords (SwiGLU: waves 0-1 gate rows, 2-3 up
     // rows), waves 4-7 the activation rows'
-    const bool wpart = wave < 4;
-    const __amdgpu_buffer_rsrc_t rsx = wpart ? ((EPI == kEpiSwiGLU && wave >= 2) ? rsw2 : rsw1) : rsa;
-    const uint32_t sc_voff = 4 * (64 * (EPI == kEpiSwiGLU && wpart ? (wave & 1) : (wave & 3)) + lane);
+    // MXFP4: 8-byte records, 16 B per lane; waves 0-1 the W rows' 2 KB
+    // (SwiGLU: wave 0 the gate rows, wave 1 the up rows), waves 2-3 the
+    // activation rows', waves 4-7 none
+    const bool wpart = FP4 ? wave < 2 : wave < 4;
+    const __amdgpu_buffer_rsrc_t rsx =
+        FP4 ? (wpart ? ((EPI == kEpiSwiGLU && wave == 1) ? rsw2 : rsw1) : rsa)
+            : (wpart ? ((EPI == kEpiSwiGLU && wave >= 2) ? rsw2 : rsw1) : rsa);
+    const uint32_t sc_voff =
+        FP4 ? static_cast<uint32_t>(16 * lane + ((EPI == kEpiSwiGLU && wpart) ? 0 : 1024 * (wave & 1)))
+            : static_cast<uint32_t>(4 * (64 * (EPI == kEpiSwiGLU && wpart ? (wave & 1) : (wave & 3)) + lane));
     const int64_t sc_rows = wpart ? N : M;
 
     auto issue = [&](int stage, int64_t kt) __attribute__((always_inline)) {
@@ -247,13 +273,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
             buf_dma16(rwx, woff[i], kb, base + (kDmaPerWave * wave + i) * 1024);
             buf_dma16(ra, aoff[i], kb, base + kTileBytes + (kDmaPerWave * wave + i) * 1024);
         }
-        if constexpr (MX)
+        if constexpr (FP4) {
+            if (wave < 4)
+                buf_dma16(rsx, sc_voff, static_cast<int>(kt * sc_rows * 8), base + kStageBytes + 1024 * wave);
+        } else if constexpr (MX) {
             buf_dma4(rsx, sc_voff, static_cast<int>(kt * sc_rows * 4), base + kStageBytes + 256 * wave);
+        }
     };
     // this lane's scale dwords in a stage (shifted by 8 g, see the header)
     uint32_t asc[kWM], wsc[kWN];
     auto take_scales = [&](int stage) __attribute__((always_inline)) {
         const uint32_t* sw = reinterpret_cast<const uint32_t*>(smem + stage * kStage + kStageBytes);
+        if constexpr (FP4) {
+            // record of a row: dword g holds the blocks g, g + 2, g + 4, g + 6
+            // of the step, which this lane's MFMAs of chunks 0..3 take
+            const uint32_t* sa = sw + 512;
+#pragma unroll
+            for (int b = 0; b < kWM; ++b) asc[b] = sa[2 * (128 * wm + 32 * b + l32) + g];
+#pragma unroll
+            for (int b = 0; b < kWN; ++b)
+                wsc[b] = sw[2 * (EPI == kEpiSwiGLU ? 128 * b + 32 * wn + l32 : 64 * wn + 32 * b + l32) + g];
+            return;
+        }
         const uint32_t* sa = sw + 256;
 #pragma unroll
         for (int b = 0; b < kWM; ++b) asc[b] = sa[128 * wm + 32 * b + l32] >> (8 * g);
@@ -284,7 +325,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
         if (kt + 1 < ksteps) issue(stage ^ 1, kt + 1);
         const char* wt = smem + stage * kStage;
         const char* at = wt + kTileBytes;
-        if constexpr (MX) {
+        if constexpr (FP4) {
+            // four 64-element chunks c (32 bytes of a row each): lane (l, g)
+            // reads 16-byte chunk 2c + g, the 32 elements of block 2c + g,
+            // scaled by byte c of its scale dword
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int off = 16 * ((2 * c + g) ^ rsw);
+                bf16x8 wf[kWN], af[kWM];
+#pragma unroll
+                for (int b = 0; b < kWN; ++b) wf[b] = *reinterpret_cast<const bf16x8*>(wt + wrow0 + b * 32 * 128 + off);
+#pragma unroll
+                for (int b = 0; b < kWM; ++b) af[b] = *reinterpret_cast<const bf16x8*>(at + arow0 + b * 32 * 128 + off);
+#pragma unroll
+                for (int bi = 0; bi < kWN; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < kWM; ++bj) {
+                        const uint4 wa = __builtin_bit_cast(uint4, wf[bi]);
+                        const uint4 aa = __builtin_bit_cast(uint4, af[bj]);
+                        const int sw = static_cast<int>(wsc[bi]), sa = static_cast<int>(asc[bj]);
+                        switch (c) {
+                            case 0: acc[bi][bj] = mfma_mx4<0>(wa, aa, acc[bi][bj], sw, sa); break;
+                            case 1: acc[bi][bj] = mfma_mx4<1>(wa, aa, acc[bi][bj], sw, sa); break;
+                            case 2: acc[bi][bj] = mfma_mx4<2>(wa, aa, acc[bi][bj], sw, sa); break;
+                            default: acc[bi][bj] = mfma_mx4<3>(wa, aa, acc[bi][bj], sw, sa); break;
+                        }
+                    }
+            }
+        } else if constexpr (MX) {
             // two 64-element chunks c: lane reads 16-byte chunks 4c + g and
             // 4c + 2 + g. The fragments are read as bf16x8 (reinterpreted as
             // fp8 bytes): read as uint4 the compiler could not tell them from
@@ -376,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
             const uint4 v = *reinterpret_cast<const uint4*>(ep + r * 128 + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
             if (mw + r < M && n < N) store8(Y + (mw + r) * N + n, v);
         }
-    } else if (EPI == kEpiSwiGLU && MX) {
+    } else if (EPI == kEpiSwiGLU && FMT == kFmtFp8) {
         // bi = 0 is the gate block, bi = 1 the up block of output columns
         // n0 + 32 wn + [0, 32), exactly one MX block per row: fp32 staging
         // (128 rows x 32 fp32 per wave), then 4 lanes per row take the
@@ -512,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
     }
 }
 
-template <bool MX>
+template <int FMT>
 hipError_t launch_gemm_args(int epilogue, GemmArgs& p, hipStream_t stream) {
     if (p.M == 0) return hipSuccess;
     const int out_n = epilogue == kEpiSwiGLU ? kBN / 2 : kBN;
@@ -521,13 +589,13 @@ hipError_t launch_gemm_args(int epilogue, GemmArgs& p, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.mtiles * p.ntiles));
     switch (epilogue) {
         case kEpiStore:
-            hipLaunchKernelGGL((gemm_kernel<kEpiStore, MX>), grid, dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<kEpiStore, FMT>), grid, dim3(kThreads), 0, stream, p);
             break;
         case kEpiSwiGLU:
-            hipLaunchKernelGGL((gemm_kernel<kEpiSwiGLU, MX>), grid, dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<kEpiSwiGLU, FMT>), grid, dim3(kThreads), 0, stream, p);
             break;
         default:
-            hipLaunchKernelGGL((gemm_kernel<kEpiGatedResidual, MX>), grid, dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<kEpiGatedResidual, FMT>), grid, dim3(kThreads), 0, stream, p);
             break;
     }
     return hipGetLastError();
@@ -543,7 +611,7 @@ hipError_t launch_gemm(int epilogue, const uint16_t* a, const uint16_t* w, const
     p.a = a; p.w = w; p.w2 = w2; p.y = y;
     p.M = m; p.N = n; p.K = k;
     p.res = res; p.gate = gate; p.gate_stride = gate_stride; p.cu = cu; p.num_seqs = num_seqs;
-    return launch_gemm_args<false>(epilogue, p, stream);
+    return launch_gemm_args<kFmtBf16>(epilogue, p, stream);
 }
 
 hipError_t launch_gemm_mx(int epilogue, const uint8_t* a, const uint8_t* a_sc, const uint8_t* w,
@@ -556,7 +624,19 @@ hipError_t launch_gemm_mx(int epilogue, const uint8_t* a, const uint8_t* a_sc, c
     p.y = y; p.y_sc = y_sc;
     p.M = m; p.N = n; p.K = k;
     p.res = res; p.gate = gate; p.gate_stride = gate_stride; p.cu = cu; p.num_seqs = num_seqs;
-    return launch_gemm_args<true>(epilogue, p, stream);
+    return launch_gemm_args<kFmtFp8>(epilogue, p, stream);
+}
+
+hipError_t launch_gemm_mx4(int epilogue, const uint8_t* a, const uint8_t* a_sc, const uint8_t* w,
+                           const uint8_t* w_sc, const uint8_t* w2, const uint8_t* w2_sc, void* y,
+                           int64_t m, int64_t n, int64_t k, const uint16_t* res, const float* gate,
+                           int64_t gate_stride, const int32_t* cu, int num_seqs, hipStream_t stream) {
+    GemmArgs p{};
+    p.a = a; p.a_sc = a_sc; p.w = w; p.w_sc = w_sc; p.w2 = w2; p.w2_sc = w2_sc;
+    p.y = y;
+    p.M = m; p.N = n; p.K = k;
+    p.res = res; p.gate = gate; p.gate_stride = gate_stride; p.cu = cu; p.num_seqs = num_seqs;
+    return launch_gemm_args<kFmtFp4>(epilogue, p, stream);
 }
 
 }  // namespace h3

@@ -117,4 +117,29 @@ __device__ __forceinline__ int64_t mx_scale_offset(int64_t r, int64_t j, int64_t
     return ((j >> 2) * rows + r) * 4 + (j & 3);
 }
 
+// ---- MXFP4 (OCP MX v1.0: 32-element blocks, E8M0 scale, E2M1 elements) ----
+// E8M0 byte of a block's scale 2^(floor(log2 amax) - 2) from its fp32 amax:
+// the exponent field minus 2, clamped at 0.
+__device__ __forceinline__ uint32_t mx4_scale_byte(float amax) {
+    const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xff);
+    return static_cast<uint32_t>(max(e - 2, 0));
+}
+// 4-bit E2M1 code of v (already divided by the scale, |v| < 8): the index of
+// the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, midpoints to the even index,
+// saturating at 6 (index 7), plus 8 when v is negative (its sign bit).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+    const float a = fabsf(v);
+    const uint32_t idx = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                         static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                         static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                         static_cast<uint32_t>(a > 5.0f);
+    return idx | ((__float_as_uint(v) >> 31) << 3);
+}
+// Byte offset of the scale of row r, block j in the MXFP4 K-step-major
+// layout: 8 bytes per row and 256-element K step, the step's even blocks
+// (0, 2, 4, 6) in its first dword and the odd ones in the second.
+__device__ __forceinline__ int64_t mx4_scale_offset(int64_t r, int64_t j, int64_t rows) {
+    return ((j >> 3) * rows + r) * 8 + (j & 1) * 4 + ((j & 7) >> 1);
+}
+
 }  // namespace h3

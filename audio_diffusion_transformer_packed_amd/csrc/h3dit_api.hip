@@ -891,6 +891,116 @@ H3_API h3_status h3_linear_gated_residual_mxfp8(const void* a, const void* a_sca
 
 namespace {
 
+// MXFP4 GEMM operands: k a multiple of 256 (one K step of 128 bytes per row),
+// codes 16-byte and scales 8-byte aligned, scale arrays within 2^31 bytes.
+h3_status check_mx4_gemm(int64_t m, int64_t n, int64_t k, int64_t n_mult) {
+    h3_status st = check_gemm_shape(m, n, k, n_mult);
+    if (st != H3_OK) return st;
+    if (k % 256) return fail(H3_ERR_UNSUPPORTED, "k=%lld must be a multiple of 256 (MXFP4)", (long long)k);
+    if (std::max(m, n) > INT32_MAX / (k / 32))
+        return fail(H3_ERR_UNSUPPORTED, "m or n times k/32 exceeds 2^31 (MX scale arrays)");
+    return ok();
+}
+
+bool mx4_aligned(const void* codes, const void* scales) {
+    return !((reinterpret_cast<uintptr_t>(codes) & 15) || (reinterpret_cast<uintptr_t>(scales) & 7));
+}
+
+}  // namespace
+
+extern "C" {
+
+H3_API h3_status h3_mx4_quantize_bf16(const void* x, int64_t x_row_stride, int64_t rows, int64_t k,
+                                      void* codes, void* scales, void* hip_stream) {
+    if (rows < 0 || k <= 0) return fail(H3_ERR_INVALID_ARGUMENT, "rows=%lld k=%lld", (long long)rows, (long long)k);
+    if (k % 256) return fail(H3_ERR_UNSUPPORTED, "k=%lld must be a multiple of 256", (long long)k);
+    if (x_row_stride < k || x_row_stride % 8)
+        return fail(H3_ERR_INVALID_ARGUMENT, "x_row_stride must be >= k and a multiple of 8");
+    if (rows == 0) return ok();
+    if (rows > (static_cast<int64_t>(1) << 40) / k) return fail(H3_ERR_UNSUPPORTED, "rows * k too large");
+    if (!x || !codes || !scales) return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes)) & 15 ||
+        reinterpret_cast<uintptr_t>(scales) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "x and codes must be 16-byte, scales 8-byte aligned");
+    hipError_t e = h3::launch_mx4_quantize(static_cast<const uint16_t*>(x), x_row_stride, rows, k,
+                                           static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                                           static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "mxfp4 quantize launch");
+    return ok();
+}
+
+H3_API h3_status h3_linear_mxfp4(const void* a, const void* a_scales, const void* w,
+                                 const void* w_scales, void* y, int64_t m, int64_t n, int64_t k,
+                                 void* hip_stream) {
+    h3_status st = check_mx4_gemm(m, n, k, 8);
+    if (st != H3_OK) return st;
+    if (m == 0) return ok();
+    if (!a || !a_scales || !w || !w_scales || !y) return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!mx4_aligned(a, a_scales) || !mx4_aligned(w, w_scales) || reinterpret_cast<uintptr_t>(y) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "codes 16-byte, scales 8-byte and y 8-byte aligned");
+    hipError_t e = h3::launch_gemm_mx4(h3::kEpiStore, static_cast<const uint8_t*>(a),
+                                       static_cast<const uint8_t*>(a_scales), static_cast<const uint8_t*>(w),
+                                       static_cast<const uint8_t*>(w_scales), nullptr, nullptr, y, m, n, k,
+                                       nullptr, nullptr, 0, nullptr, 1, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "mxfp4 gemm launch");
+    return ok();
+}
+
+H3_API h3_status h3_linear_swiglu_mxfp4(const void* a, const void* a_scales, const void* w_gate,
+                                        const void* w_gate_scales, const void* w_up,
+                                        const void* w_up_scales, void* y, int64_t m, int64_t n,
+                                        int64_t k, void* hip_stream) {
+    h3_status st = check_mx4_gemm(m, n, k, 128);
+    if (st != H3_OK) return st;
+    if (m == 0) return ok();
+    if (!a || !a_scales || !w_gate || !w_gate_scales || !w_up || !w_up_scales || !y)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!mx4_aligned(a, a_scales) || !mx4_aligned(w_gate, w_gate_scales) || !mx4_aligned(w_up, w_up_scales) ||
+        reinterpret_cast<uintptr_t>(y) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "codes 16-byte, scales 8-byte and y 8-byte aligned");
+    hipError_t e = h3::launch_gemm_mx4(h3::kEpiSwiGLU, static_cast<const uint8_t*>(a),
+                                       static_cast<const uint8_t*>(a_scales), static_cast<const uint8_t*>(w_gate),
+                                       static_cast<const uint8_t*>(w_gate_scales),
+                                       static_cast<const uint8_t*>(w_up), static_cast<const uint8_t*>(w_up_scales),
+                                       y, m, n, k, nullptr, nullptr, 0, nullptr, 1,
+                                       static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "mxfp4 gemm launch");
+    return ok();
+}
+
+H3_API h3_status h3_linear_gated_residual_mxfp4(const void* a, const void* a_scales, const void* w,
+                                                const void* w_scales, const void* res,
+                                                const float* gate, int64_t gate_row_stride, void* y,
+                                                int64_t m, int64_t n, int64_t k,
+                                                const int32_t* cu_seqlens_dev,
+                                                const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                void* hip_stream) {
+    h3_status st = check_mx4_gemm(m, n, k, 8);
+    if (st != H3_OK) return st;
+    if (m > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "m too large");
+    st = check_cu(cu_seqlens_host, num_seqs, static_cast<int32_t>(m));
+    if (st != H3_OK) return st;
+    if (m == 0) return ok();
+    if (!a || !a_scales || !w || !w_scales || !res || !gate || !y || !cu_seqlens_dev)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (gate_row_stride < n) return fail(H3_ERR_INVALID_ARGUMENT, "gate_row_stride < n");
+    if (gate_row_stride & 3) return fail(H3_ERR_UNSUPPORTED, "gate_row_stride must be a multiple of 4");
+    if (!mx4_aligned(a, a_scales) || !mx4_aligned(w, w_scales) || reinterpret_cast<uintptr_t>(gate) & 15 ||
+        (reinterpret_cast<uintptr_t>(res) | reinterpret_cast<uintptr_t>(y)) & 7)
+        return fail(H3_ERR_UNSUPPORTED, "codes/gate 16-byte, scales 8-byte, res/y 8-byte aligned");
+    hipError_t e = h3::launch_gemm_mx4(h3::kEpiGatedResidual, static_cast<const uint8_t*>(a),
+                                       static_cast<const uint8_t*>(a_scales), static_cast<const uint8_t*>(w),
+                                       static_cast<const uint8_t*>(w_scales), nullptr, nullptr, y, m, n, k,
+                                       static_cast<const uint16_t*>(res), gate, gate_row_stride,
+                                       cu_seqlens_dev, num_seqs, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "mxfp4 gemm launch");
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
 struct BlockPlan {
     size_t mod, h, qkv, o, x1, h2, a, attn, total;
 };
@@ -1231,6 +1341,157 @@ H3_API h3_status h3_dit_block_forward_mxfp8_bsa(const void* x, void* x_out, cons
     if (!sparsity_ok(sparsity)) return fail(H3_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1)");
     return block_forward_mx(x, x_out, cond, weights, dims, cu_seqlens_dev, cu_seqlens_host, num_seqs,
                             total_tokens, rope_grid, sparsity, workspace, workspace_bytes, hip_stream);
+}
+
+}  // extern "C"
+
+// ---- the block with MXFP4 linears ----
+
+namespace {
+
+struct BlockPlanMX4 {
+    size_t mod, h, h4, hs, qkv, o, o4, os, x1, a, a4, as, attn, total;
+};
+
+BlockPlanMX4 block_plan_mx4(const h3_dit_dims* d, int32_t num_seqs, int32_t total_tokens) {
+    BlockPlanMX4 p;
+    const size_t n = static_cast<size_t>(total_tokens), c = static_cast<size_t>(d->hidden);
+    const size_t f = static_cast<size_t>(d->ffn_dim);
+    p.mod = align_up(static_cast<size_t>(num_seqs) * 6 * c * sizeof(float));
+    p.h = align_up(n * c * 2);           // h, then h2 (bf16)
+    p.h4 = align_up(n * c / 2);          // their MXFP4 codes
+    p.hs = align_up(n * c / 32);
+    p.qkv = align_up(n * 3 * c * 2);
+    p.o = align_up(n * c * 2);
+    p.o4 = align_up(n * c / 2);
+    p.os = align_up(n * c / 32);
+    p.x1 = align_up(n * c * 2);
+    p.a = align_up(n * f * 2);
+    p.a4 = align_up(n * f / 2);
+    p.as = align_up(n * f / 32);
+    p.attn = attn_plan(num_seqs, total_tokens, d->num_heads, d->head_dim, H3_ATTN_BF16).total;
+    p.total = p.mod + p.h + p.h4 + p.hs + p.qkv + p.o + p.o4 + p.os + p.x1 + p.a + p.a4 + p.as + p.attn;
+    return p;
+}
+
+h3_status check_dims_mx4(const h3_dit_dims* d, int32_t total_tokens) {
+    h3_status st = check_dims(d);
+    if (st != H3_OK) return st;
+    if (d->ffn_dim % 256) return fail(H3_ERR_UNSUPPORTED, "ffn_dim=%d must be a multiple of 256 (MXFP4)", d->ffn_dim);
+    const int64_t widest = std::max<int64_t>(3 * static_cast<int64_t>(d->hidden), d->ffn_dim);
+    if (static_cast<int64_t>(total_tokens) * widest / 32 > INT32_MAX ||
+        widest * std::max(d->hidden, d->ffn_dim) / 32 > INT32_MAX)
+        return fail(H3_ERR_UNSUPPORTED, "MX scale arrays exceed 2^31 bytes");
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+H3_API size_t h3_dit_block_mx4_workspace_size(const h3_dit_dims* dims, int32_t num_seqs,
+                                              int32_t total_tokens) {
+    if (dims == nullptr || num_seqs < 0 || total_tokens < 0) return 0;
+    if (check_dims_mx4(dims, total_tokens) != H3_OK) return 0;
+    return block_plan_mx4(dims, num_seqs, total_tokens).total;
+}
+
+H3_API h3_status h3_dit_block_forward_mxfp4(const void* x, void* x_out, const void* cond,
+                                            const h3_dit_mx_weights* weights,
+                                            const h3_dit_dims* dims,
+                                            const int32_t* cu_seqlens_dev,
+                                            const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                            int32_t total_tokens, const int32_t* rope_grid,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* hip_stream) {
+    h3_status st = check_dims_mx4(dims, total_tokens);
+    if (st != H3_OK) return st;
+    st = check_cu(cu_seqlens_host, num_seqs, total_tokens);
+    if (st != H3_OK) return st;
+    if (total_tokens == 0) return ok();
+    if (!x || !x_out || !cond || !weights || !cu_seqlens_dev || !rope_grid)
+        return fail(H3_ERR_INVALID_ARGUMENT, "NULL pointer");
+    const h3_dit_mx_weights& w = *weights;
+    const h3_mx_matrix* mats[5] = {&w.w_qkv, &w.w_o, &w.w_gate, &w.w_up, &w.w_down};
+    if (!w.w_mod || !w.q_norm || !w.k_norm) return fail(H3_ERR_INVALID_ARGUMENT, "NULL weight pointer");
+    for (const h3_mx_matrix* m : mats) {
+        if (!m->codes || !m->scales) return fail(H3_ERR_INVALID_ARGUMENT, "NULL MX weight pointer");
+        if (!mx4_aligned(m->codes, m->scales))
+            return fail(H3_ERR_UNSUPPORTED, "MXFP4 weight codes 16-byte and scales 8-byte aligned");
+    }
+    if (x == x_out) return fail(H3_ERR_INVALID_ARGUMENT, "x and x_out may not alias");
+    const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(x_out) |
+                         reinterpret_cast<uintptr_t>(cond) | reinterpret_cast<uintptr_t>(w.w_mod) |
+                         reinterpret_cast<uintptr_t>(w.q_norm) | reinterpret_cast<uintptr_t>(w.k_norm);
+    if (al & 15) return fail(H3_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+    const BlockPlanMX4 p = block_plan_mx4(dims, num_seqs, total_tokens);
+    if (workspace_bytes < p.total || workspace == nullptr)
+        return fail(H3_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, p.total);
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+        return fail(H3_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    char* ws = static_cast<char*>(workspace);
+    auto carve = [&](size_t bytes) { char* r = ws; ws += bytes; return r; };
+    float* mod = reinterpret_cast<float*>(carve(p.mod));
+    uint16_t* hb = reinterpret_cast<uint16_t*>(carve(p.h));
+    uint8_t* h4 = reinterpret_cast<uint8_t*>(carve(p.h4));
+    uint8_t* hs = reinterpret_cast<uint8_t*>(carve(p.hs));
+    uint16_t* qkv = reinterpret_cast<uint16_t*>(carve(p.qkv));
+    uint16_t* obuf = reinterpret_cast<uint16_t*>(carve(p.o));
+    uint8_t* o4 = reinterpret_cast<uint8_t*>(carve(p.o4));
+    uint8_t* os = reinterpret_cast<uint8_t*>(carve(p.os));
+    uint16_t* x1 = reinterpret_cast<uint16_t*>(carve(p.x1));
+    uint16_t* ab = reinterpret_cast<uint16_t*>(carve(p.a));
+    uint8_t* a4 = reinterpret_cast<uint8_t*>(carve(p.a4));
+    uint8_t* as = reinterpret_cast<uint8_t*>(carve(p.as));
+    void* attn_ws = carve(p.attn);
+
+    const int64_t n = total_tokens, c = dims->hidden, ffn = dims->ffn_dim;
+    const int64_t ms = 6 * c;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    uint16_t* yb = static_cast<uint16_t*>(x_out);
+    auto u8 = [](const void* ptr) { return static_cast<const uint8_t*>(ptr); };
+    hipError_t e;
+#define H3_TRY(call, what)                          \
+    e = (call);                                     \
+    if (e != hipSuccess) return hip_fail(e, what);
+
+    H3_TRY(h3::launch_modulation(static_cast<const uint16_t*>(cond),
+                                 static_cast<const uint16_t*>(w.w_mod), mod, num_seqs,
+                                 static_cast<int>(c), stream), "modulation");
+    H3_TRY(h3::launch_adaln(xb, hb, mod + 0 * c, mod + 1 * c, ms, cu_seqlens_dev, num_seqs, total_tokens,
+                            static_cast<int>(c), dims->eps, stream), "adaln 1");
+    H3_TRY(h3::launch_mx4_quantize(hb, c, n, c, h4, hs, stream), "h quantize");
+    H3_TRY(h3::launch_gemm_mx4(h3::kEpiStore, h4, hs, u8(w.w_qkv.codes), u8(w.w_qkv.scales), nullptr,
+                               nullptr, qkv, n, 3 * c, c, nullptr, nullptr, 0, nullptr, 1, stream),
+           "qkv gemm");
+    H3_TRY(h3::launch_qk_norm_rope(qkv, qkv + c, 3 * c, 3 * c,
+                                   static_cast<const uint16_t*>(w.q_norm),
+                                   static_cast<const uint16_t*>(w.k_norm), rope_grid,
+                                   total_tokens, dims->num_heads, dims->head_dim,
+                                   dims->rope_split, dims->rope_theta, dims->eps, stream),
+           "qk norm rope");
+    h3_status ast = run_attention(qkv, qkv + c, qkv + 2 * c, obuf, 3 * c, 3 * c, 3 * c, c,
+                                  cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                                  dims->num_heads, dims->head_dim, nullptr, attn_ws, stream);
+    if (ast != H3_OK) return ast;
+    H3_TRY(h3::launch_mx4_quantize(obuf, c, n, c, o4, os, stream), "o quantize");
+    H3_TRY(h3::launch_gemm_mx4(h3::kEpiGatedResidual, o4, os, u8(w.w_o.codes), u8(w.w_o.scales), nullptr,
+                               nullptr, x1, n, c, c, xb, mod + 2 * c, ms, cu_seqlens_dev, num_seqs, stream),
+           "out-proj gemm");
+    H3_TRY(h3::launch_adaln(x1, hb, mod + 3 * c, mod + 4 * c, ms, cu_seqlens_dev, num_seqs, total_tokens,
+                            static_cast<int>(c), dims->eps, stream), "adaln 2");
+    H3_TRY(h3::launch_mx4_quantize(hb, c, n, c, h4, hs, stream), "h2 quantize");
+    H3_TRY(h3::launch_gemm_mx4(h3::kEpiSwiGLU, h4, hs, u8(w.w_gate.codes), u8(w.w_gate.scales),
+                               u8(w.w_up.codes), u8(w.w_up.scales), ab, n, ffn, c, nullptr, nullptr, 0,
+                               nullptr, 1, stream), "gate/up gemm");
+    H3_TRY(h3::launch_mx4_quantize(ab, ffn, n, ffn, a4, as, stream), "a quantize");
+    H3_TRY(h3::launch_gemm_mx4(h3::kEpiGatedResidual, a4, as, u8(w.w_down.codes), u8(w.w_down.scales),
+                               nullptr, nullptr, yb, n, c, ffn, x1, mod + 5 * c, ms, cu_seqlens_dev,
+                               num_seqs, stream), "down gemm");
+#undef H3_TRY
+    return ok();
 }
 
 }  // extern "C"

@@ -11,6 +11,15 @@
 // major, the scale of row r and block j at byte ((j / 4) rows + r) 4 + j % 4.
 // For bf16 x every step is exact in fp32 (amax, the power-of-two scaling),
 // so the codes equal the definition bit for bit.
+//
+// MXFP4 ("MiniMax H3 on Ascend 950PR / 950DT", section "MXFP4 online
+// quantization", OCP MX v1.0 MXFP4): scale 2^(floor(log2 amax) - 2) and
+// E2M1 elements (nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, midpoints to the
+// even index, saturating at 6; sign bit 3 from the input), two per byte
+// (codes [rows, k / 2], element 2i in the low nibble of byte i); scales
+// 8 bytes per row and 256-element K step, the step's even blocks in the
+// first dword and its odd blocks in the second (the order in which the
+// matrix core's lanes take them).
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -51,7 +60,52 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
     }
 }
 
+// MXFP4: the same lane layout; a lane's 8 elements become one dword of
+// codes (element 2i in the low nibble of byte i).
+__global__ __launch_bounds__(256) void mx4_quant_kernel(const uint16_t* __restrict__ x, int64_t ld,
+                                                        int64_t rows, int64_t k,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+    const int64_t per_row = k >> 3;
+    const int64_t nchunk = rows * per_row;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < nchunk; c += stride) {
+        const int64_t r = c / per_row, ch = c - r * per_row;
+        const uint4 raw = load_stream16(x + r * ld + ch * 8);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+        am = fmaxf(am, __shfl_xor(am, 1, 64));
+        am = fmaxf(am, __shfl_xor(am, 2, 64));
+        const uint32_t sb = mx4_scale_byte(am);
+        const float inv = mx_inv_scale(sb);
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_code(v[i] * inv) << (4 * i);
+        *reinterpret_cast<uint32_t*>(codes + r * (k >> 1) + ch * 4) = word;
+        if ((ch & 3) == 0) scales[mx4_scale_offset(r, ch >> 2, rows)] = static_cast<uint8_t>(sb);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_mx4_quantize(const uint16_t* x, int64_t ld, int64_t rows, int64_t k, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    const int64_t nchunk = rows * (k / 8);
+    const int64_t want = (nchunk + 255) / 256;
+    const int64_t blocks = want < 256 * 32 ? want : 256 * 32;
+    hipLaunchKernelGGL(mx4_quant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, x, ld,
+                       rows, k, codes, scales);
+    return hipGetLastError();
+}
 
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t ld, int64_t rows, int64_t k, uint8_t* codes,
                               uint8_t* scales, hipStream_t stream) {

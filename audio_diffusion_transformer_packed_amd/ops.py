@@ -648,3 +648,148 @@ class DitBlockMX:
         else:
             check(lib().h3_dit_block_forward_mxfp8(*common, _ptr(ws), ws.numel(), _stream(dev)))
         return out
+
+
+# --------------------------------------------------------------------------
+# MXFP4 linears and the block with them
+# --------------------------------------------------------------------------
+
+class MX4:
+    """An MXFP4 matrix [rows, k]: `codes` uint8 [rows, k / 2] (two E2M1
+    codes per byte, element 2i in the low nibble) and `scales` uint8
+    [rows * k / 32] (E8M0, 8 bytes per row and 256-element K step)."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, k: int):
+        if codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or codes.dim() != 2:
+            raise TypeError("MX4 codes must be uint8 [rows, k / 2] and scales uint8")
+        rows = codes.shape[0]
+        if k % 256 or codes.shape[1] * 2 != k or scales.numel() != rows * k // 32 or not codes.is_contiguous():
+            raise ValueError("MX4: k must be a multiple of 256, codes contiguous [rows, k/2], scales rows*k/32")
+        self.codes, self.scales, self.k = codes, scales, k
+
+    @property
+    def shape(self):
+        return (self.codes.shape[0], self.k)
+
+    @staticmethod
+    def empty(rows: int, k: int, device) -> "MX4":
+        return MX4(torch.empty((rows, k // 2), dtype=torch.uint8, device=device),
+                   torch.empty(rows * k // 32, dtype=torch.uint8, device=device), k)
+
+
+def mx4_quantize(x: torch.Tensor, out: Optional[MX4] = None) -> MX4:
+    """MXFP4 codes and scales of bf16 x [rows, k] (rows may be strided)."""
+    _need(x, "x", BF16)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [rows, k] with contiguous rows")
+    rows, k = x.shape
+    out = MX4.empty(rows, k, x.device) if out is None else out
+    if out.shape != (rows, k):
+        raise ValueError("out has the wrong shape")
+    check(lib().h3_mx4_quantize_bf16(_ptr(x), x.stride(0), rows, k, _ptr(out.codes), _ptr(out.scales),
+                                     _stream(x.device)))
+    return out
+
+
+def _mx4_args(a: MX4, ws) -> torch.device:
+    dev = a.codes.device
+    for t in [a] + list(ws):
+        if not isinstance(t, MX4):
+            raise TypeError("MX4 operands expected")
+        if t.codes.device != dev:
+            raise ValueError("operands on different devices")
+        if t.shape[1] != a.shape[1]:
+            raise ValueError("operands must share k")
+    return dev
+
+
+def linear_mx4(a: MX4, w: MX4, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = dq(a) dq(w)^T in bf16 (MXFP4 operands)."""
+    dev = _mx4_args(a, [w])
+    m, k = a.shape
+    n = w.shape[0]
+    y = torch.empty((m, n), dtype=BF16, device=dev) if out is None else out
+    check(lib().h3_linear_mxfp4(_ptr(a.codes), _ptr(a.scales), _ptr(w.codes), _ptr(w.scales), _ptr(y),
+                                m, n, k, _stream(dev)))
+    return y
+
+
+def linear_swiglu_mx4(a: MX4, w_gate: MX4, w_up: MX4, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """silu(dq(a) dq(w_gate)^T) * (dq(a) dq(w_up)^T) in bf16 (MXFP4 operands)."""
+    dev = _mx4_args(a, [w_gate, w_up])
+    m, k = a.shape
+    n = w_gate.shape[0]
+    if w_up.shape != w_gate.shape:
+        raise ValueError("w_gate and w_up must have the same shape")
+    y = torch.empty((m, n), dtype=BF16, device=dev) if out is None else out
+    check(lib().h3_linear_swiglu_mxfp4(_ptr(a.codes), _ptr(a.scales), _ptr(w_gate.codes),
+                                       _ptr(w_gate.scales), _ptr(w_up.codes), _ptr(w_up.scales),
+                                       _ptr(y), m, n, k, _stream(dev)))
+    return y
+
+
+def linear_gated_residual_mx4(a: MX4, w: MX4, res: torch.Tensor, gate: torch.Tensor,
+                              cu_seqlens: torch.Tensor, cu_host,
+                              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dev = _mx4_args(a, [w])
+    _need(res, "res", BF16, dev)
+    _need(gate, "gate", torch.float32, dev)
+    m, k = a.shape
+    n = w.shape[0]
+    if gate.stride(1) != 1:
+        raise ValueError("gate rows must be contiguous")
+    y = torch.empty((m, n), dtype=BF16, device=dev) if out is None else out
+    cu = _host_cu(cu_host)
+    check(lib().h3_linear_gated_residual_mxfp4(_ptr(a.codes), _ptr(a.scales), _ptr(w.codes),
+                                               _ptr(w.scales), _ptr(res.contiguous()), _ptr(gate),
+                                               gate.stride(0), _ptr(y), m, n, k, _ptr(cu_seqlens),
+                                               cu.ctypes.data_as(C.c_void_p), cu.size - 1,
+                                               _stream(dev)))
+    return y
+
+
+class DitBlockMX4:
+    """The block with MXFP4 linears: the five linear weights are quantised
+    once here (h3_mx4_quantize_bf16); forward() calls h3_dit_block_forward_mxfp4."""
+
+    def __init__(self, weights: Dict[str, torch.Tensor], heads: int, head_dim: int,
+                 ffn_dim: int, rope_split: Sequence[int], rope_theta: float = 10000.0,
+                 eps: float = 1e-6):
+        hidden = heads * head_dim
+        for nm in WEIGHT_NAMES:
+            _need(weights[nm], nm, BF16)
+            if not weights[nm].is_contiguous():
+                raise ValueError(f"{nm} must be contiguous")
+        self.bf16 = {nm: weights[nm] for nm in ("w_mod", "q_norm", "k_norm")}
+        self.mx = {nm: mx4_quantize(weights[nm]) for nm in MX_WEIGHT_NAMES}
+        self.dims = DitDims(hidden, heads, head_dim, ffn_dim, (C.c_int32 * 3)(*rope_split),
+                            float(rope_theta), float(eps))
+        mats = [MxMatrix(self.mx[nm].codes.data_ptr(), self.mx[nm].scales.data_ptr())
+                for nm in MX_WEIGHT_NAMES]
+        self.c_weights = DitMxWeights(self.bf16["w_mod"].data_ptr(), self.bf16["q_norm"].data_ptr(),
+                                      self.bf16["k_norm"].data_ptr(), *mats)
+        self.hidden, self.ffn = hidden, ffn_dim
+
+    def workspace_bytes(self, num_seqs: int, total_tokens: int) -> int:
+        return lib().h3_dit_block_mx4_workspace_size(C.byref(self.dims), num_seqs, total_tokens)
+
+    def forward(self, x: torch.Tensor, cond: torch.Tensor, cu_seqlens: torch.Tensor, cu_host,
+                rope_grid: torch.Tensor, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        dev = x.device
+        _need(x, "x", BF16, dev)
+        _need(cond, "cond", BF16, dev)
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        _need(rope_grid, "rope_grid", torch.int32, dev)
+        if not (x.is_contiguous() and cond.is_contiguous() and rope_grid.is_contiguous()):
+            raise ValueError("x, cond and rope_grid must be contiguous")
+        cu = _host_cu(cu_host)
+        b, n = cu.size - 1, x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        ws = _workspace(self.workspace_bytes(b, n), dev, workspace)
+        check(lib().h3_dit_block_forward_mxfp4(_ptr(x), _ptr(out), _ptr(cond), C.byref(self.c_weights),
+                                               C.byref(self.dims), _ptr(cu_seqlens),
+                                               cu.ctypes.data_as(C.c_void_p), b, n, _ptr(rope_grid),
+                                               _ptr(ws), ws.numel(), _stream(dev)))
+        return out

@@ -38,6 +38,7 @@ METRIC = "varlen attention TFLOP/s + DiT-block ms at 58k packed tokens; % MFMA p
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 / fp6 MFMA
 ATTN_SRC = os.path.join(ROOT, "audio_diffusion_transformer_packed_amd", "csrc", "attn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_block_10s_58k_traffic.json")
 
@@ -508,6 +509,62 @@ def main():
             "speedup_vs_mxfp8_block": round(ms_mx / ms_l, 3)}
         del blk_mx, ws_mx, out_mx, blk_l, ws_l
 
+    # The same block with MXFP4 (OCP MX v1.0, E2M1) linears: weights
+    # quantised once before timing; a step quantises its activations.
+    mx4r = None
+    if not args.no_mx:
+        log("timing mxfp4 block")
+        blk4 = ops.DitBlockMX4(weights, wl.heads, wl.head_dim, wl.ffn, split)
+        ws4 = torch.empty(blk4.workspace_bytes(b, n), dtype=torch.uint8, device=dev)
+        out4 = torch.empty_like(x)
+        step4 = lambda: blk4.forward(x, cond, cu_d, cu, grid_d, out=out4, workspace=ws4)
+        for _ in range(args.warmup):
+            step4()
+        ms4 = timer(step4, args.steps)
+        st4 = {}
+        if not args.no_stages:
+            mod = taps["mod"]
+            w4 = blk4.mx
+            h4 = ops.mx4_quantize(taps["h"])
+            o4 = ops.mx4_quantize(taps["o"])
+            h24 = ops.mx4_quantize(taps["h2"])
+            a4 = ops.mx4_quantize(taps["a"])
+            y4 = torch.empty((n, 3 * c), dtype=torch.bfloat16, device=dev)
+            ya = torch.empty((n, wl.ffn), dtype=torch.bfloat16, device=dev)
+            yx = torch.empty_like(x)
+
+            def rec4(name, t, flops=None, nbytes=None):
+                e = {"ms": round(t["median"], 4), "p10_ms": round(t["p10"], 4), "p90_ms": round(t["p90"], 4),
+                     "launches": t["n"], "mall_flushed": t["flush"]}
+                if flops is not None:
+                    tf = flops / (t["median"] * 1e-3) / 1e12
+                    e["tflops"] = round(tf, 2)
+                    e["frac_fp4_peak"] = round(tf / PEAK_FP4_TFLOPS, 4)
+                if nbytes is not None:
+                    gbs = nbytes / (t["median"] * 1e-3) / 1e9
+                    e["gbs"] = round(gbs, 1)
+                    e["frac_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+                st4[name] = e
+            it = stage_iters
+            rec4("h_quantize_mx4", sampler(lambda: ops.mx4_quantize(taps["h"], out=h4), it, True),
+                 nbytes=n * c * 2 + n * c // 2 + n * c // 32)
+            rec4("qkv_gemm_mx4", sampler(lambda: ops.linear_mx4(h4, w4["w_qkv"], out=y4), it, False),
+                 flops=2.0 * n * c * 3 * c)
+            rec4("out_proj_gated_residual_mx4", sampler(lambda: ops.linear_gated_residual_mx4(
+                o4, w4["w_o"], x, mod[:, 2 * c:3 * c], cu_d, cu, out=yx), it, False), flops=2.0 * n * c * c)
+            rec4("swiglu_gemm_mx4", sampler(lambda: ops.linear_swiglu_mx4(h24, w4["w_gate"], w4["w_up"], out=ya),
+                                            it, False), flops=2.0 * n * c * 2 * wl.ffn)
+            rec4("down_gated_residual_mx4", sampler(lambda: ops.linear_gated_residual_mx4(
+                a4, w4["w_down"], taps["x1"], mod[:, 5 * c:6 * c], cu_d, cu, out=yx), it, False),
+                flops=2.0 * n * wl.ffn * c)
+            del h4, o4, h24, a4, y4, ya, yx
+        mx4r = {"workload": f"{wl.name} with MXFP4 (OCP MX v1.0, E2M1, 32-element K blocks) linears",
+                "block_ms": round(ms4, 4),
+                "block_tflops": round((f_attn + f_gemm) / (ms4 * 1e-3) / 1e12, 2),
+                "speedup_vs_bf16_block": round(ms_step / ms4, 4),
+                "stages": st4}
+        del blk4, ws4, out4
+
     # Other workloads of the method, timed as one leg each.
     legs = {}
     if not args.no_legs:
@@ -620,6 +677,7 @@ def main():
         "fp8_attention": fp8,
         "block_sparse_attention": bsa,
         "mxfp8_linears": mxr,
+        "mxfp4_linears": mx4r,
         "legs": legs,
         "timed_wall_s": round(t_wall, 3),
     }

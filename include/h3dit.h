@@ -555,6 +555,77 @@ H3_API h3_status h3_dit_block_forward_mxfp8_bsa(const void* x, void* x_out, cons
                                                 float sparsity, void* workspace,
                                                 size_t workspace_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------------------
+ * MXFP4 linears ([H3-950PR] section "MXFP4 online quantization": the DiT's
+ * linears switch from MXFP8 to MXFP4 online quantisation; the pages give no
+ * format). The OCP Microscaling (MX) v1.0 MXFP4 format with E2M1 elements:
+ *   - blocks of 32 consecutive elements along k share one E8M0 scale
+ *     2^(floor(log2 amax) - 2), never below 2^-127 (byte 0 for all-zero
+ *     blocks);
+ *   - elements are E2M1(x / scale): the nearest of 0, 0.5, 1, 1.5, 2, 3, 4,
+ *     6 (index 0..7), a midpoint going to the even index, saturating at 6;
+ *     the 4-bit code is index + 8 when x is negative (its sign bit, also
+ *     where the value rounds to zero);
+ *   - an MXFP4 matrix [rows, k] is codes, uint8 [rows, k / 2] (element 2i
+ *     in the low nibble of byte i), and scales, rows * k / 32 bytes in
+ *     K-step-major order with 8 bytes per row and 256-element K step: the
+ *     scale of row r and block j at byte ((j / 8) * rows + r) * 8 +
+ *     (j % 2) * 4 + (j % 8) / 2 (the step's even blocks in its first
+ *     dword, the odd blocks in its second, the order in which the matrix
+ *     core's lanes take them). k is a multiple of 256; codes are 16-byte and
+ *     scales 8-byte aligned; rows * k / 32 < 2^31.
+ *
+ *   h3_mx4_quantize_bf16: bf16 x [rows, k] (row stride x_row_stride
+ *       elements, >= k and a multiple of 8, x 16-byte aligned) -> MXFP4
+ *       codes + scales, equal to the definition above for every bf16 input.
+ *   h3_linear_mxfp4: y = dq(a) . dq(W)^T, y bf16 [m, n] (8-byte aligned),
+ *       a MXFP4 [m, k], W MXFP4 [n, k]; n a multiple of 8; fp32 accumulation
+ *       in the matrix core, one bf16 rounding.
+ *   h3_linear_swiglu_mxfp4: y = silu(dq(a) . dq(W_gate)^T) * (dq(a) .
+ *       dq(W_up)^T) in bf16 [m, n]; n a multiple of 128.
+ *   h3_linear_gated_residual_mxfp4: y = res + gate[seg(t)] * (dq(a) .
+ *       dq(W)^T), as h3_linear_gated_residual_bf16.
+ * Errors as for the bf16 linears; all buffers are the caller's.
+ * ---------------------------------------------------------------------- */
+H3_API h3_status h3_mx4_quantize_bf16(const void* x, int64_t x_row_stride, int64_t rows, int64_t k,
+                                      void* codes, void* scales, void* hip_stream);
+H3_API h3_status h3_linear_mxfp4(const void* a, const void* a_scales, const void* w,
+                                 const void* w_scales, void* y, int64_t m, int64_t n, int64_t k,
+                                 void* hip_stream);
+H3_API h3_status h3_linear_swiglu_mxfp4(const void* a, const void* a_scales, const void* w_gate,
+                                        const void* w_gate_scales, const void* w_up,
+                                        const void* w_up_scales, void* y, int64_t m, int64_t n,
+                                        int64_t k, void* hip_stream);
+H3_API h3_status h3_linear_gated_residual_mxfp4(const void* a, const void* a_scales, const void* w,
+                                                const void* w_scales, const void* res,
+                                                const float* gate, int64_t gate_row_stride, void* y,
+                                                int64_t m, int64_t n, int64_t k,
+                                                const int32_t* cu_seqlens_dev,
+                                                const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                                void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * The block with MXFP4 linears ([H3-950PR] section "MXFP4 online
+ * quantization"): as h3_dit_block_forward_mxfp8, with the five linear
+ * weights given as MXFP4 matrices (h3_mx_matrix: codes and scales in the
+ * MXFP4 layouts above, quantised once by the caller with
+ * h3_mx4_quantize_bf16) and every activation that enters a linear (h, o,
+ * h2, a) quantised to MXFP4 from its bf16 value by h3_mx4_quantize_bf16's
+ * kernel. hidden and ffn_dim multiples of 256. Needs a workspace of
+ * h3_dit_block_mx4_workspace_size(...) bytes (256-byte aligned; 0 for
+ * unsupported dims).
+ * ---------------------------------------------------------------------- */
+H3_API size_t h3_dit_block_mx4_workspace_size(const h3_dit_dims* dims, int32_t num_seqs,
+                                              int32_t total_tokens);
+H3_API h3_status h3_dit_block_forward_mxfp4(const void* x, void* x_out, const void* cond,
+                                            const h3_dit_mx_weights* weights,
+                                            const h3_dit_dims* dims,
+                                            const int32_t* cu_seqlens_dev,
+                                            const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                            int32_t total_tokens, const int32_t* rope_grid,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif
