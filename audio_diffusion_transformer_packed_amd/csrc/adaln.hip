@@ -4,12 +4,11 @@
 //
 //  * modulation GEMV: mod[b, :] = cond[b, :] . W_mod^T in fp32; HBM-bound on
 //    the 6C x C weight, one wave per weight row (streamed once), every
-//    segment's cond (staged in LDS per workgroup) applied to the row while
-//    it is in registers;
+//    segment's cond applied to the row while it is in registers;
 //  * RMSNorm + modulate: h[t] = RMSNorm(x[t]) * (1 + scale[seg(t)]) +
 //    shift[seg(t)]; one wave per row (its sum of squares is a wave
-//    reduction, no workgroup barrier), two rows in flight per wave, one
-//    bf16 rounding.
+//    reduction), the modulation values of the workgroup's segment staged in
+//    LDS, one bf16 rounding.
 #include "h3_common.hpp"
 #include "h3_internal.hpp"
 
@@ -18,66 +17,50 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Segments of cond staged in LDS per pass of the modulation kernel.
-constexpr int kCondChunk = 4;
-
+// Modulation GEMV, one wave per weight row: the row (hidden bf16) is loaded
+// once into registers, then every segment's cond row is read (a 6 KB row at
+// hidden 3072, served from L2 after the first wave) and dotted with it. No
+// LDS and no barriers: at 6 x 3072 x 3072 this measured 20 us (70 % of
+// 8 TB/s) against 24 us with cond staged in LDS behind workgroup barriers.
 template <int NCH>
 __global__ __launch_bounds__(kThreads) void modulation_kernel(
     const uint16_t* __restrict__ cond, const uint16_t* __restrict__ w, float* __restrict__ mod,
     int num_seqs, int hidden, int rows) {
-    // cond rows are shared by the workgroup's four waves: staged once in LDS
-    // (kCondChunk segments per pass) instead of re-read from L2 per wave
-    __shared__ __attribute__((aligned(16))) uint16_t cs[kCondChunk * NCH * 512];
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    const bool active = row < rows;                 // every wave stays for the barriers
-    float wr[NCH * 8];
-    if (active) {
-        const uint16_t* wp = w + static_cast<int64_t>(row) * hidden;
+    if (row >= rows) return;                        // whole wave: no barrier below
+    Chunk16 wr[NCH];
+    const uint16_t* wp = w + static_cast<int64_t>(row) * hidden;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) wr[i].u = load_stream16(wp + (i * 64 + lane) * 8);
+    for (int b = 0; b < num_seqs; ++b) {
+        const uint16_t* cp = cond + static_cast<int64_t>(b) * hidden;
+        float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             Chunk16 c;
-            c.u = load_stream16(wp + (i * 64 + lane) * 8);
+            c.u = *reinterpret_cast<const uint4*>(cp + (i * 64 + lane) * 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) wr[i * 8 + e] = bf2f(c.h[e]);
+            for (int e = 0; e < 8; ++e) acc = fmaf(bf2f(c.h[e]), bf2f(wr[i].h[e]), acc);
         }
-    }
-    for (int b0 = 0; b0 < num_seqs; b0 += kCondChunk) {
-        const int nb = min(kCondChunk, num_seqs - b0);
-        __syncthreads();
-        for (int c = threadIdx.x; c < nb * hidden / 8; c += kThreads)
-            reinterpret_cast<uint4*>(cs)[c] =
-                *reinterpret_cast<const uint4*>(cond + static_cast<int64_t>(b0) * hidden + 8 * c);
-        __syncthreads();
-        if (!active) continue;
-        for (int b = 0; b < nb; ++b) {
-            const uint16_t* cp = cs + b * hidden;
-            float acc = 0.f;
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                Chunk16 c;
-                c.u = *reinterpret_cast<const uint4*>(cp + (i * 64 + lane) * 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(bf2f(c.h[e]), wr[i * 8 + e], acc);
-            }
-            acc = wave_sum(acc);
-            if (lane == 0) mod[static_cast<int64_t>(b0 + b) * rows + row] = acc;
-        }
+        acc = wave_sum(acc);
+        if (lane == 0) mod[static_cast<int64_t>(b) * rows + row] = acc;
     }
 }
 
 // RMSNorm + modulate, one wave per row: lane i owns 16-byte chunks i,
 // i + 64, ... (NCH = hidden / 512 of them) of the row, so the row's sum of
-// squares is a wave reduction and no workgroup barrier stands between a
-// wave's loads and its stores. Each wave takes kRowsPerWave consecutive rows
-// and issues all of their loads before the first reduction. The lane's
-// shift / scale values stay in registers across its rows (reloaded only
-// where a row changes segment) when they fit (NCH <= 8), otherwise they are
-// read per row from cache. x and h are streamed with nontemporal loads /
-// stores (each byte is touched once). At 57,960 x 3072 with the Infinity
-// Cache flushed this runs at ~0.9x of a plain device copy of the same bytes.
-constexpr int kRowsPerWave = 2;
-constexpr int kAdalnWaves = 4;
+// squares is a wave reduction. A workgroup of kAdalnWaves waves takes
+// kAdalnWaves consecutive rows; it stages (1 + scale) and shift of its first
+// row's segment in LDS (one read of 2 x hidden floats shared by all its
+// waves), and a row of another segment (only where a workgroup straddles a
+// segment boundary) reads its own from memory instead, in the same fp32
+// arithmetic. One row per wave keeps the register count low, so many waves
+// are resident and many loads are in flight. x and h are streamed with
+// nontemporal loads / stores (each byte is touched once). At 57,960 x 3072
+// with the Infinity Cache flushed: 121 us (73 % of 8 TB/s) against 126 us
+// for two rows per wave with the modulation values held in registers.
+constexpr int kAdalnWaves = 8;
 
 // With MX the output is MXFP8 instead of bf16 (codes into h, E8M0 scales
 // into hsc, K-step-major with total_tokens rows; "MiniMax H3 on Ascend 950PR
@@ -89,82 +72,72 @@ __global__ __launch_bounds__(64 * kAdalnWaves) void adaln_kernel(
     const float* __restrict__ shift, const float* __restrict__ scale, int64_t mod_stride,
     const int32_t* __restrict__ cu, int num_seqs, int total_tokens, float eps) {
     constexpr int hidden = NCH * 512;
-    constexpr bool kCacheMod = NCH <= 8;
+    __shared__ float4 lsh[hidden / 4], lsc[hidden / 4];
     const int lane = threadIdx.x & 63;
-    const int64_t t0 =
-        (static_cast<int64_t>(blockIdx.x) * kAdalnWaves + (threadIdx.x >> 6)) * kRowsPerWave;
-    Chunk16 xc[kRowsPerWave][NCH];
+    const int64_t tb = static_cast<int64_t>(blockIdx.x) * kAdalnWaves;   // first row of the workgroup
+    const int64_t t = tb + (threadIdx.x >> 6);
+    Chunk16 xc[NCH];
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r)
+    for (int i = 0; i < NCH; ++i)
+        if (t < total_tokens) xc[i].u = load_stream16(x + t * hidden + (i * 64 + lane) * 8);
+    const int bseg = num_seqs == 1 ? 0 : find_segment(cu, num_seqs, tb);
+    for (int c = threadIdx.x; c < hidden / 4; c += 64 * kAdalnWaves) {
+        const float4 a = reinterpret_cast<const float4*>(shift + static_cast<int64_t>(bseg) * mod_stride)[c];
+        float4 b = reinterpret_cast<const float4*>(scale + static_cast<int64_t>(bseg) * mod_stride)[c];
+        b.x += 1.0f; b.y += 1.0f; b.z += 1.0f; b.w += 1.0f;
+        lsh[c] = a;
+        lsc[c] = b;
+    }
+    __syncthreads();
+    if (t >= total_tokens) return;
+    float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < NCH; ++i)
-            if (t0 + r < total_tokens)
-                xc[r][i].u = load_stream16(x + (t0 + r) * hidden + (i * 64 + lane) * 8);
-    int seg_loaded = -1;
-    float shv[kCacheMod ? NCH : 1][8], scv[kCacheMod ? NCH : 1][8];
-    auto load_mod = [&](int seg, int i, float (&sh)[8], float (&sc)[8]) __attribute__((always_inline)) {
-        const float* shp = shift + static_cast<int64_t>(seg) * mod_stride + (i * 64 + lane) * 8;
-        const float* scp = scale + static_cast<int64_t>(seg) * mod_stride + (i * 64 + lane) * 8;
-        const float4 sh0 = *reinterpret_cast<const float4*>(shp);
-        const float4 sh1 = *reinterpret_cast<const float4*>(shp + 4);
-        const float4 sc0 = *reinterpret_cast<const float4*>(scp);
-        const float4 sc1 = *reinterpret_cast<const float4*>(scp + 4);
-        sh[0] = sh0.x; sh[1] = sh0.y; sh[2] = sh0.z; sh[3] = sh0.w;
-        sh[4] = sh1.x; sh[5] = sh1.y; sh[6] = sh1.z; sh[7] = sh1.w;
-        sc[0] = 1.0f + sc0.x; sc[1] = 1.0f + sc0.y; sc[2] = 1.0f + sc0.z; sc[3] = 1.0f + sc0.w;
-        sc[4] = 1.0f + sc1.x; sc[5] = 1.0f + sc1.y; sc[6] = 1.0f + sc1.z; sc[7] = 1.0f + sc1.w;
-    };
+    for (int i = 0; i < NCH; ++i)
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-        const int64_t t = t0 + r;
-        if (t >= total_tokens) break;
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float f = bf2f(xc[r][i].h[e]);
-                ss = fmaf(f, f, ss);
-            }
-        ss = wave_sum(ss);
-        const float rinv = 1.0f / sqrtf(fmaf(ss, 1.0f / hidden, eps));
-        const int seg = num_seqs == 1 ? 0 : find_segment(cu, num_seqs, t);
-        if (kCacheMod && seg != seg_loaded) {
-#pragma unroll
-            for (int i = 0; i < (kCacheMod ? NCH : 1); ++i) load_mod(seg, i, shv[i], scv[i]);
-            seg_loaded = seg;
+        for (int e = 0; e < 8; ++e) {
+            const float f = bf2f(xc[i].h[e]);
+            ss = fmaf(f, f, ss);
         }
+    ss = wave_sum(ss);
+    const float rinv = 1.0f / sqrtf(fmaf(ss, 1.0f / hidden, eps));
+    const int seg = num_seqs == 1 ? 0 : find_segment(cu, num_seqs, t);
+    const float4* gsh = reinterpret_cast<const float4*>(shift + static_cast<int64_t>(seg) * mod_stride);
+    const float4* gsc = reinterpret_cast<const float4*>(scale + static_cast<int64_t>(seg) * mod_stride);
+    const bool own = seg == bseg;                    // wave-uniform
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            float sh[8], sc[8];
-            if (kCacheMod) {
+    for (int i = 0; i < NCH; ++i) {
+        const int c4 = (i * 64 + lane) * 2;
+        float4 sh0, sh1, sc0, sc1;
+        if (own) {
+            sh0 = lsh[c4]; sh1 = lsh[c4 + 1]; sc0 = lsc[c4]; sc1 = lsc[c4 + 1];
+        } else {
+            sh0 = gsh[c4]; sh1 = gsh[c4 + 1]; sc0 = gsc[c4]; sc1 = gsc[c4 + 1];
+            sc0.x += 1.0f; sc0.y += 1.0f; sc0.z += 1.0f; sc0.w += 1.0f;
+            sc1.x += 1.0f; sc1.y += 1.0f; sc1.z += 1.0f; sc1.w += 1.0f;
+        }
+        const float sh[8] = {sh0.x, sh0.y, sh0.z, sh0.w, sh1.x, sh1.y, sh1.z, sh1.w};
+        const float sc[8] = {sc0.x, sc0.y, sc0.z, sc0.w, sc1.x, sc1.y, sc1.z, sc1.w};
+        float o[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) { sh[e] = shv[kCacheMod ? i : 0][e]; sc[e] = scv[kCacheMod ? i : 0][e]; }
-            } else {
-                load_mod(seg, i, sh, sc);
-            }
-            float o[8];
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(bf2f(xc[i].h[e]) * rinv, sc[e], sh[e]);
+        if constexpr (MX) {
+            float am = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = fmaf(bf2f(xc[r][i].h[e]) * rinv, sc[e], sh[e]);
-            if constexpr (MX) {
-                float am = 0.f;
+            for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(o[e]));
+            am = fmaxf(am, __shfl_xor(am, 1, 64));
+            am = fmaxf(am, __shfl_xor(am, 2, 64));
+            const uint32_t sb = mx_scale_byte(am);
+            const float inv = mx_inv_scale(sb);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(o[e]));
-                am = fmaxf(am, __shfl_xor(am, 1, 64));
-                am = fmaxf(am, __shfl_xor(am, 2, 64));
-                const uint32_t sb = mx_scale_byte(am);
-                const float inv = mx_inv_scale(sb);
+            for (int e = 0; e < 8; ++e) o[e] *= inv;
+            const int ch = i * 64 + lane;
+            *reinterpret_cast<uint2*>(static_cast<uint8_t*>(hout) + t * hidden + ch * 8) = mx_codes8(o);
+            if ((lane & 3) == 0) hsc[mx_scale_offset(t, ch >> 2, total_tokens)] = static_cast<uint8_t>(sb);
+        } else {
+            Chunk16 out;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] *= inv;
-                const int ch = i * 64 + lane;
-                *reinterpret_cast<uint2*>(static_cast<uint8_t*>(hout) + t * hidden + ch * 8) = mx_codes8(o);
-                if ((lane & 3) == 0) hsc[mx_scale_offset(t, ch >> 2, total_tokens)] = static_cast<uint8_t>(sb);
-            } else {
-                Chunk16 out;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out.w[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
-                store_stream16(static_cast<uint16_t*>(hout) + t * hidden + (i * 64 + lane) * 8, out.u);
-            }
+            for (int e = 0; e < 4; ++e) out.w[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+            store_stream16(static_cast<uint16_t*>(hout) + t * hidden + (i * 64 + lane) * 8, out.u);
         }
     }
 }
@@ -225,8 +198,7 @@ hipError_t launch_adaln(const uint16_t* x, uint16_t* h, const float* shift, cons
                         int hidden, float eps, hipStream_t stream) {
     if (total_tokens == 0) return hipSuccess;
     if (hidden % 512 != 0 || hidden > 8192) return hipErrorInvalidValue;
-    constexpr int rows_per_block = kRowsPerWave * kAdalnWaves;
-    const dim3 grid((total_tokens + rows_per_block - 1) / rows_per_block);
+    const dim3 grid((total_tokens + kAdalnWaves - 1) / kAdalnWaves);
     return launch_adaln_nch<false>(hidden / 512, grid, stream, x, static_cast<void*>(h),
                                    static_cast<uint8_t*>(nullptr), shift, scale, mod_stride, cu,
                                    num_seqs, total_tokens, eps);
@@ -237,8 +209,7 @@ hipError_t launch_adaln_mx(const uint16_t* x, uint8_t* h8, uint8_t* h_sc, const 
                            int total_tokens, int hidden, float eps, hipStream_t stream) {
     if (total_tokens == 0) return hipSuccess;
     if (hidden % 512 != 0 || hidden > 8192) return hipErrorInvalidValue;
-    constexpr int rows_per_block = kRowsPerWave * kAdalnWaves;
-    const dim3 grid((total_tokens + rows_per_block - 1) / rows_per_block);
+    const dim3 grid((total_tokens + kAdalnWaves - 1) / kAdalnWaves);
     return launch_adaln_nch<true>(hidden / 512, grid, stream, x, static_cast<void*>(h8), h_sc, shift,
                                   scale, mod_stride, cu, num_seqs, total_tokens, eps);
 }

@@ -116,9 +116,15 @@ class Sampler:
     before every launch (outside the events), so an HBM-bound kernel reads its
     inputs from HBM rather than from the 256 MiB Infinity Cache."""
 
-    def __init__(self, torch, flush_bytes=512 << 20):
+    def __init__(self, torch, flush_bytes=512 << 20, spin_cycles=2_000_000):
         self.torch = torch
         self.scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+        # a GPU-side busy wait (~1 ms) between the flush and the start event,
+        # so the host has enqueued the event and the timed launch before the
+        # GPU reaches them: the event pair then brackets the kernel alone,
+        # not the host's launch overhead
+        self.spin = getattr(torch.cuda, "_sleep", None)
+        self.spin_cycles = spin_cycles
 
     def __call__(self, fn, n, flush):
         t = self.torch
@@ -129,6 +135,8 @@ class Sampler:
         for i, (start, end) in enumerate(pairs):
             if flush:
                 self.scratch.fill_(i & 0xff)
+            if self.spin is not None:
+                self.spin(self.spin_cycles)
             start.record()
             fn()
             end.record()
