@@ -177,6 +177,71 @@ def cpu_baseline(inp, wl, rows_count=16):
                        f"TFLOP algorithmic in {dt:.1f} s")}
 
 
+def _attn_chunk_worker(task):
+    """One (head, 128-row query chunk) of the oracle's varlen attention, on
+    q/k/v float32 [N, H, D] held in shared memory; BLAS single-threaded."""
+    from multiprocessing import shared_memory
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        pass
+    import oracle
+    names, shape, cu, head, rows = task
+    shms = [shared_memory.SharedMemory(name=nm) for nm in names]
+    try:
+        q, k, v = (np.ndarray(shape, dtype=np.float32, buffer=sh.buf) for sh in shms)
+        out = oracle.attn_varlen_ref(q[:, head:head + 1], k[:, head:head + 1], v[:, head:head + 1], cu,
+                                     rows=rows)
+        return float(np.abs(out).sum())
+    finally:
+        for sh in shms:
+            sh.close()
+
+
+def cpu_attention_pool(wl, chunks_per_head=16):
+    """The oracle's varlen attention (attn_varlen_ref, float64) on the
+    workload's attention shape, timed over a process pool of one worker per
+    host core, one task per (head, 128-row query chunk): every head, and
+    `chunks_per_head` query chunks spread over the segment."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    import h3synth
+    cu, _ = h3synth.pack(wl.requests)
+    n, heads, d = int(cu[-1]), wl.heads, wl.head_dim
+    inp = h3synth.attention_inputs(cu, np.zeros((n, 3), np.int32), heads, d, wl.seed)
+    shms, names = [], []
+    for a in (inp.q.f32, inp.k.f32, inp.v.f32):
+        sh = shared_memory.SharedMemory(create=True, size=a.nbytes)
+        np.ndarray(a.shape, dtype=np.float32, buffer=sh.buf)[...] = a
+        shms.append(sh)
+        names.append(sh.name)
+    del inp
+    try:
+        starts = np.linspace(0, (n - 128) // 128, chunks_per_head).astype(np.int64) * 128
+        tasks = [(names, (n, heads, d), cu, h, np.arange(t0, min(n, t0 + 128)))
+                 for h in range(heads) for t0 in starts]
+        workers = len(os.sched_getaffinity(0))
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers) as pool:
+            pool.map_async(_attn_chunk_worker, tasks[:workers]).get(timeout=300)   # workers up
+            t0 = time.perf_counter()
+            pool.map_async(_attn_chunk_worker, tasks, chunksize=1).get(timeout=600)
+            dt = time.perf_counter() - t0
+    finally:
+        for sh in shms:
+            sh.close()
+            sh.unlink()
+    rows = sum(t[4].size for t in tasks)
+    flops = 4.0 * n * d * rows                      # 4 L D per (query row, head), one segment
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(workers),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": (f"float64 numpy oracle attention (attn_varlen_ref) at {n} tokens x {heads} heads x {d}: "
+                       f"{chunks_per_head} query chunks of 128 rows per head against the whole segment, "
+                       f"{len(tasks)} (head, chunk) tasks over a pool of {workers} single-threaded worker "
+                       f"processes; {flops / 1e12:.3f} TFLOP in {dt:.1f} s")}
+
+
 def bsa_kept_flops(lists, lengths, head_dim, sparsity) -> float:
     """4 D x (query rows x kept keys), summed over heads and 256-row query
     blocks, from kept-block lists [H, T, stride] (row = first 64-token block
@@ -691,7 +756,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(inp, wl)
+        cb = cpu_attention_pool(wl)
+        cb["block_sample"] = cpu_baseline(inp, wl)
+        result["cpu_baseline"] = cb
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
