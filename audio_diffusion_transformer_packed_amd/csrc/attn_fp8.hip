@@ -13,9 +13,9 @@
 //   MFMA against an all-ones operand, in place of 32 fp32 adds per tile),
 //   O = (sum P8 V8) s_v / (448 l).
 // Skip rule: for the 32 query rows of a wave, a key tile other than the
-// segment's first is skipped (no exp, no P V) when every valid row has its
-// tile maximum more than `threshold` (natural-log units) below its running
-// maximum. Each work item reports its number of skipped (32-row group, key
+// segment's first is skipped (no exp, no P V contribution) when every
+// valid row has its tile maximum more than `threshold` (natural-log units)
+// below its running maximum. Each work item reports its number of skipped (32-row group, key
 // tile) pairs; the count is summed in LDS, no atomics.
 //
 // Design (CDNA4): the bf16 kernel's layout with v_mfma_f32_32x32x64_f8f6f4.
@@ -97,8 +97,8 @@ __device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c) {
 // blocks of its query block, lists[(head, first 64-row block)][0 .. keep),
 // in ascending order; no skip rule.
 // SKIP: the skip rule is compiled in (dense path only); a skipped tile
-// saves its exp, convert and rescale and its P V MFMAs (a wave-uniform
-// branch).
+// saves its exp, convert and rescale (a wave-uniform branch) and leaves P
+// zero, so the P V MFMAs, still issued, add nothing.
 template <bool BSA, bool SKIP>
 __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
@@ -247,15 +247,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     f32x16 lacc = f32x16{};
     const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};
-    int nskip = 0;
+    // SKIP: this wave's skipped-tile count, kept in a vector register (a
+    // scalar counter adds to the kernel's scalar register pressure, which
+    // then spills inside the tile loop); the empty asm defines it per lane
+    int nskip;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(nskip));
+    // per lane: padding rows never keep a tile (their cut is +inf)
+    const float thr_eff = qvalid ? thr_log2 : -INFINITY;
     f32x16 sc[2] = {f32x16{}, f32x16{}};
     i32x8 pf = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-    bool pv_run = false;      // SKIP: the previous tile was not skipped (wave-uniform)
 
     // MFMA block M(u): S^T(u) from K stage u & 1 (u < T), O += P(u-1) V(u-1)
-    // from V stage (u-1) & 1 (u >= 1, tile u-1 not skipped)
-    auto mfma_block = [&](int u) __attribute__((always_inline)) {
-        if (!wave_active) return;
+    // from V stage (u-1) & 1 (u >= 1). A tile the skip rule drops leaves P
+    // zero, so its P V adds nothing: the block has no branch around the P V
+    // MFMAs (such a branch cost 3-4 % of the kernel when nothing is skipped,
+    // more than the MFMAs it saves when tiles are).
+    auto mfma_qk = [&](int u) __attribute__((always_inline)) {
         if (u < nsel) {
             const char* kl = smem + (u & 1) * kKT;
             if constexpr (BSA) {
@@ -282,13 +289,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
                         sc[b] = mfma_fp8(read32(kl + 4096 * b + kro[c][0], kl + 4096 * b + kro[c][1]), qf[c], sc[b]);
             }
         }
-        if (u >= 1 && __builtin_expect(!SKIP || pv_run, 1)) {
-            const char* vl = smem + 2 * kKT + ((u - 1) & 1) * kVT;
+    };
+    auto mfma_pv = [&](int u) __attribute__((always_inline)) {
+        const char* vl = smem + 2 * kKT + ((u - 1) & 1) * kVT;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-                oacc[db] = mfma_fp8(read32(vl + 2048 * db + vro[0], vl + 2048 * db + vro[1]), pf, oacc[db]);
-            lacc = mfma_fp8(ones, pf, lacc);
-        }
+        for (int db = 0; db < 4; ++db)
+            oacc[db] = mfma_fp8(read32(vl + 2048 * db + vro[0], vl + 2048 * db + vro[1]), pf, oacc[db]);
+        lacc = mfma_fp8(ones, pf, lacc);
+    };
+    auto mfma_block = [&](int u) __attribute__((always_inline)) {
+        if (!wave_active) return;
+        mfma_qk(u);
+        if (u >= 1) mfma_pv(u);
     };
     // softmax block S(u): tile max, skip rule, rescale, P of tile u
     auto softmax_block = [&](int u) __attribute__((always_inline)) {
@@ -314,8 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
         bool run_tile = true;
         if constexpr (SKIP) {
             if (u > 0) {
-                const bool below = !qvalid || tmax < m_run - thr_log2;
-                if (__builtin_expect(__all(below), 0)) {   // wave-uniform
+                if (__builtin_expect(__all(tmax < m_run - thr_eff), 0)) {   // wave-uniform
                     run_tile = false;
                     ++nskip;
                     m_new = m_run;                    // a skipped tile moves no maximum
@@ -345,7 +356,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
                 pf[w] = word;
             }
         }
-        if constexpr (SKIP) pv_run = run_tile;
+        if constexpr (SKIP) {
+            if (!run_tile) pf = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
     };
 
     // ---- prologue: K(0) in LDS, every wave one 1 KB block ----

@@ -110,6 +110,17 @@ class Timer:
         return start.elapsed_time(end) / n
 
 
+def alternate(timer, fa, fb, n, rounds=4):
+    """Average durations of two callables timed in alternating rounds of n
+    launches each, so that drift of the shader clock during the run falls on
+    both alike (used where their ratio is reported)."""
+    ta = tb = 0.0
+    for _ in range(rounds):
+        ta += timer(fa, n)
+        tb += timer(fb, n)
+    return ta / rounds, tb / rounds
+
+
 class Sampler:
     """Per-launch durations of a callable: a HIP event pair around each launch on
     the current torch stream. With flush=True a 512 MiB scratch buffer is written
@@ -454,9 +465,8 @@ def main():
             return ops.attn_varlen(qv, kv, vv, cu_d, cu, out=o8, precision="fp8",
                                    skip_softmax=skip, skip_counts=counts, workspace=fp8_ws)
         fp8_attn(False)
-        ms_fp8 = timer(lambda: fp8_attn(False), it)
         fp8_attn(True)
-        ms_fp8_skip = timer(lambda: fp8_attn(True), it)
+        ms_fp8, ms_fp8_skip = alternate(timer, lambda: fp8_attn(False), lambda: fp8_attn(True), it)
         skipped = int(counts.sum().item())
         pairs = wl.heads * sum(((L + 31) // 32) * ((L + 63) // 64) for L in wl.lengths)
         qbufs = ops.fp8_quantize(qv, kv, vv, cu_d, cu)
@@ -705,9 +715,8 @@ def main():
         fp8_4 = lambda sk: ops.attn_varlen(q4, k4, v4, cu_d, cu, out=o4, precision="fp8", skip_softmax=sk,
                                            skip_counts=cnt4, workspace=ws4)
         fp8_4(False)
-        ms4_off = timer(lambda: fp8_4(False), max(3, args.steps))
         fp8_4(True)
-        ms4_on = timer(lambda: fp8_4(True), max(3, args.steps))
+        ms4_off, ms4_on = alternate(timer, lambda: fp8_4(False), lambda: fp8_4(True), max(3, args.steps))
         pairs4 = wl.heads * sum(((L + 31) // 32) * ((L + 63) // 64) for L in wl.lengths)
         frac4 = int(cnt4.sum().item()) / pairs4
         legs["fp8_attention_frame_local"] = {
