@@ -61,7 +61,9 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
 }
 
 // MXFP4: the same lane layout; a lane's 8 elements become one dword of
-// codes (element 2i in the low nibble of byte i).
+// codes (element 2i in the low nibble of byte i), rounded by the hardware
+// fp4 conversion (e2m1x8; a chain of seven compares per element instead
+// measured 137 against 83 us at 57,960 x 3072).
 __global__ __launch_bounds__(256) void mx4_quant_kernel(const uint16_t* __restrict__ x, int64_t ld,
                                                         int64_t rows, int64_t k,
                                                         uint8_t* __restrict__ codes,
@@ -86,10 +88,9 @@ __global__ __launch_bounds__(256) void mx4_quant_kernel(const uint16_t* __restri
         am = fmaxf(am, __shfl_xor(am, 2, 64));
         const uint32_t sb = mx4_scale_byte(am);
         const float inv = mx_inv_scale(sb);
-        uint32_t word = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) word |= e2m1_code(v[i] * inv) << (4 * i);
-        *reinterpret_cast<uint32_t*>(codes + r * (k >> 1) + ch * 4) = word;
+        for (int i = 0; i < 8; ++i) v[i] *= inv;
+        *reinterpret_cast<uint32_t*>(codes + r * (k >> 1) + ch * 4) = e2m1x8(v);
         if ((ch & 3) == 0) scales[mx4_scale_offset(r, ch >> 2, rows)] = static_cast<uint8_t>(sb);
     }
 }
