@@ -119,7 +119,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const int tid = threadIdx.x;
     // work-item fields and segment bounds are workgroup-uniform: keep them in
     // scalar registers (so the tile buffer descriptors are scalar too)
-    const int4 it = items[blockIdx.x];
+    // BSA: work items go to the XCDs (workgroup ids are dealt round-robin
+    // over the 8) in chunks of 16 consecutive items, XCD x taking chunks x,
+    // x + 8, ...: the items an XCD runs at one time are neighbouring query
+    // blocks of a head, whose kept key blocks overlap in its L2, while every
+    // XCD still samples the whole (longest segment first) list. Ids past the
+    // last whole round of 8 x 16 map to themselves. Measured at 57,960 tokens:
+    // 3.7 % faster on frame-local input, 0.9 % on i.i.d. input.
+    unsigned item = blockIdx.x;
+    if constexpr (BSA) {
+        constexpr unsigned kChunk = 16;
+        const unsigned full = gridDim.x / (8 * kChunk) * (8 * kChunk);
+        if (blockIdx.x < full) {
+            const unsigned x = blockIdx.x % 8, k = blockIdx.x / 8;
+            item = (8 * (k / kChunk) + x) * kChunk + k % kChunk;
+        }
+    }
+    const int4 it = items[item];
     const int head = __builtin_amdgcn_readfirstlane(it.x);
     const int seg = __builtin_amdgcn_readfirstlane(it.y);
     const int q0 = __builtin_amdgcn_readfirstlane(it.z);
@@ -129,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const int kv1 = ok ? min(total_tokens, __builtin_amdgcn_readfirstlane(cu[seg + 1])) : 0;
     ok = ok && q0 >= kv0 && qlen > 0 && q0 + qlen <= kv1;
     if (!ok) {
-        if (skip_counts && tid == 0) skip_counts[blockIdx.x] = 0;
+        if (skip_counts && tid == 0) skip_counts[item] = 0;
         return;
     }
     const int len = kv1 - kv0;
@@ -430,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
             int32_t s = 0;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) s += wskip[w];
-            skip_counts[blockIdx.x] = s;
+            skip_counts[item] = s;
         }
     }
 }
