@@ -36,7 +36,9 @@
 // attention ("MiniMax H3 on Ascend 950PR / 950DT", section "Recommended
 // lossy configuration (Ascend 950PR / 950DT)": EQBSA, Q/K in INT8 and V in
 // FP8): Q and K hold INT8 codes (fp8_quant.hip's INT8 variant), S^T runs on
-// v_mfma_i32_32x32x32_i8 and is converted to fp32, and each work item walks
+// v_mfma_i32_32x32x32_i8 accumulating onto the bits of 1.5 * 2^23 (read as
+// fp32 that is the score plus an exact offset, folded into the exp2
+// argument's constant: no int-to-float converts), and each work item walks
 // only its query block's kept key tiles (bsa_select.hip), staged with their
 // K scales in LDS before the loop; V, P and the softmax are the fp8 path's.
 #include "h3_common.hpp"
@@ -52,6 +54,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kKT = kBN * kD;              // bytes of a K tile
 constexpr int kVT = kD * kBN;              // bytes of a V^T tile
 constexpr float kLog2_448 = 8.807354922057604f;
+constexpr float kBsaMagic = 12582912.0f;   // 1.5 * 2^23, the BSA score offset
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -282,7 +285,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
         if (u < nsel) {
             const char* kl = smem + (u & 1) * kKT;
             if constexpr (BSA) {
-                i32x16 si[2] = {i32x16{}, i32x16{}};
+                // accumulate onto the bits of 1.5 * 2^23: |S| <= 127 * 127 * 128 < 2^22,
+                // so each result, read as fp32, is exactly 1.5 * 2^23 + S (no convert)
+                constexpr int kMagicBits = 0x4B400000;
+                i32x16 si[2];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) si[0][r] = si[1][r] = kMagicBits;
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sc[b][r] = static_cast<float>(si[b][r]);
+                    for (int r = 0; r < 16; ++r) sc[b][r] = __int_as_float(si[b][r]);
             } else {
                 sc[0] = f32x16{};
                 sc[1] = f32x16{};
@@ -337,7 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float ct = sq * sk;          // exp2 units per raw score
-        const float tmax = mx * ct;
+        // BSA scores carry the 1.5 * 2^23 offset (exact to remove from the max)
+        const float tmax = (BSA ? mx - kBsaMagic : mx) * ct;
         float m_new = fmaxf(m_run, tmax);
         bool run_tile = true;
         if constexpr (SKIP) {
@@ -359,7 +368,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
         if (__builtin_expect(run_tile, 1)) {
             // 448 p = exp2(s ct - m + log2 448); bytes in B-operand order:
             // byte 16 b + r of this lane holds score sc[b][r]
-            const float mb = m_new - kLog2_448;
+            // BSA: the offset's share, 1.5 * 2^23 ct, moves into the constant
+            // (one fp32 rounding of that product, below an ulp of it)
+            const float mb = BSA ? fmaf(kBsaMagic, ct, m_new - kLog2_448) : m_new - kLog2_448;
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
                 const int b = w >> 2, r = 4 * (w & 3);
