@@ -42,12 +42,13 @@
 // T, 8]: channel chunk-major, so that consecutive key blocks' 16-byte chunks
 // are adjacent), int16 (|sum| <= 64 * 127), the block means the block
 // selection ranks by.
-// All HBM-bound: q and k are streamed once by quant_qk_kernel, v twice, by
-// vamax_kernel (its per-tile channel amax) and by quant_v_kernel (V's scale
-// needs the whole segment first), with 16-byte nontemporal loads. Reading V
-// in its own pass measured 2 % faster than folding its amax into
-// quant_qk_kernel: the third tile of registers took that kernel from 86
-// to 97 VGPRs, past the 96 that five waves per SIMD allow. Work items are ordered head-fastest, so the
+// All HBM-bound: q and k are streamed once by one quant_qk_kernel launch
+// each, v twice, by vamax_kernel (its per-tile channel amax) and by
+// quant_v_kernel (V's scale needs the whole segment first), with 16-byte
+// nontemporal loads. One tensor per launch keeps one tile in registers
+// (46-52 VGPRs, eight waves per SIMD): Q and K together in one kernel
+// (86 VGPRs, five waves) measured 2 % slower over the pass, and with V's
+// amax folded in as well (97 VGPRs, four waves) 4 % slower. Work items are ordered head-fastest, so the
 // workgroups resident at one time read whole token rows. Q and K codes are
 // stored nontemporally; V code rows are 64 bytes, half a cache line, so
 // they are stored through L2, which merges the two halves before write-back
@@ -190,103 +191,85 @@ __device__ __forceinline__ u32x2 i8_codes8(uint4 raw, float amax, int (&s)[8]) {
     return out;
 }
 
-// One workgroup per (key tile, head), head-fastest: Q and K codes + block
-// scales. I8: Q and K as INT8 (scale amax / 127) instead of e4m3, plus the tile's
-// per-channel code sums of Q (qsum [T, H, 128]) and K (ksum [H, 16, T, 8],
-// channel chunk-major), int16.
-template <bool I8>
+// One workgroup per (key tile, head), head-fastest: the codes and block
+// scale of one of Q (IS_K false: codes token-major like q, rows past the
+// segment end not written) or K (IS_K true: the 64 x 128 key tile, rows
+// past the segment end 0). I8: INT8 codes (scale amax / 127) instead of
+// e4m3, plus the tile's per-channel code sums, int16: qsum [T, H, 128] or
+// ksum [H, 16, T, 8] (channel chunk-major).
+template <bool I8, bool IS_K>
 __global__ __launch_bounds__(256) void quant_qk_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t qs, int64_t ks,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ tb, int num_seqs, int num_heads,
-    int64_t num_tiles, uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, float* __restrict__ qsc,
-    float* __restrict__ ksc, int16_t* __restrict__ qsum, int16_t* __restrict__ ksum) {
-    __shared__ float red[2][4];
-    __shared__ int32_t isum[I8 ? 2 : 1][4][I8 ? kD : 1];
+    const uint16_t* __restrict__ x, int64_t xs, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ tb, int num_seqs, int num_heads, int64_t num_tiles,
+    uint8_t* __restrict__ x8, float* __restrict__ xsc, int16_t* __restrict__ xsum) {
+    __shared__ float red[4];
+    __shared__ int32_t isum[4][I8 ? kD : 1];
     const int tile = static_cast<int>(blockIdx.x / static_cast<unsigned>(num_heads));
     const int h = static_cast<int>(blockIdx.x - static_cast<unsigned>(tile) * num_heads);
     int seg, t0, rows;
     tile_origin(cu, tb, num_seqs, tile, seg, t0, rows);
     const int tid = threadIdx.x, wave = tid >> 6;
     const int64_t row_bytes = static_cast<int64_t>(num_heads) * kD;
-    uint4 xq[4], xk[4];
-    load_tile(q, qs, t0, rows, h, xq);
-    load_tile(k, ks, t0, rows, h, xk);
-    float mq = 0.f, mk = 0.f;
+    uint4 xv[4];
+    load_tile(x, xs, t0, rows, h, xv);
+    float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        mq = fmaxf(mq, absmax8(xq[i]));
-        mk = fmaxf(mk, absmax8(xk[i]));
-    }
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, absmax8(xv[i]));
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        mq = fmaxf(mq, __shfl_xor(mq, off, 64));
-        mk = fmaxf(mk, __shfl_xor(mk, off, 64));
-    }
-    if ((tid & 63) == 0) {
-        red[0][wave] = mq;
-        red[1][wave] = mk;
-    }
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((tid & 63) == 0) red[wave] = m;
     __syncthreads();
-    const float amax_q = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    const float amax_k = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-    uint8_t* kt = k8 + ((static_cast<int64_t>(h) * num_tiles + tile) * kTB) * kD;
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    uint8_t* kt = x8 + ((static_cast<int64_t>(h) * num_tiles + tile) * kTB) * kD;
+    const int64_t sidx = static_cast<int64_t>(tile) * num_heads + h;
     if constexpr (I8) {
         // rows past the segment end load as 0, so they add nothing to the sums
-        int sq[8] = {0, 0, 0, 0, 0, 0, 0, 0}, sk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int sm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = tid + 256 * i;
             const int tok = c >> 4, dc = c & 15;
-            const u32x2 cq = i8_codes8(xq[i], amax_q, sq);
-            const u32x2 ck = i8_codes8(xk[i], amax_k, sk);
-            if (tok < rows)
-                __builtin_nontemporal_store(cq, reinterpret_cast<u32x2*>(q8 + (t0 + tok) * row_bytes + h * kD + 8 * dc));
-            __builtin_nontemporal_store(ck, reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc));
+            const u32x2 cw = i8_codes8(xv[i], amax, sm);
+            if constexpr (IS_K)
+                __builtin_nontemporal_store(cw, reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc));
+            else if (tok < rows)
+                __builtin_nontemporal_store(cw, reinterpret_cast<u32x2*>(x8 + (t0 + tok) * row_bytes + h * kD + 8 * dc));
         }
         // channel chunk tid % 16 is shared with lanes tid ^ 16 and tid ^ 32
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            sq[j] += __shfl_xor(sq[j], 16, 64);
-            sq[j] += __shfl_xor(sq[j], 32, 64);
-            sk[j] += __shfl_xor(sk[j], 16, 64);
-            sk[j] += __shfl_xor(sk[j], 32, 64);
+            sm[j] += __shfl_xor(sm[j], 16, 64);
+            sm[j] += __shfl_xor(sm[j], 32, 64);
         }
         if ((tid & 63) < 16) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                isum[0][wave][8 * (tid & 15) + j] = sq[j];
-                isum[1][wave][8 * (tid & 15) + j] = sk[j];
-            }
+            for (int j = 0; j < 8; ++j) isum[wave][8 * (tid & 15) + j] = sm[j];
         }
         __syncthreads();
-        const int which = tid >> 7, d = tid & 127;
-        const int32_t tot = isum[which][0][d] + isum[which][1][d] + isum[which][2][d] + isum[which][3][d];
-        // |sum| <= 64 * 127 = 8128: int16
-        if (which == 0)
-            qsum[(static_cast<int64_t>(tile) * num_heads + h) * kD + d] = static_cast<int16_t>(tot);
-        else   // chunk-major: [H][16 channel chunks][T][8]
-            ksum[((static_cast<int64_t>(h) * (kD / 8) + d / 8) * num_tiles + tile) * 8 + d % 8] =
-                static_cast<int16_t>(tot);
-        if (tid == 0) {
-            qsc[static_cast<int64_t>(tile) * num_heads + h] = amax_q > 0.f ? amax_q / 127.0f : 1.0f;
-            ksc[static_cast<int64_t>(tile) * num_heads + h] = amax_k > 0.f ? amax_k / 127.0f : 1.0f;
+        if (tid < kD) {
+            const int d = tid;
+            const int32_t tot = isum[0][d] + isum[1][d] + isum[2][d] + isum[3][d];
+            // |sum| <= 64 * 127 = 8128: int16
+            if constexpr (IS_K)   // chunk-major: [H][16 channel chunks][T][8]
+                xsum[((static_cast<int64_t>(h) * (kD / 8) + d / 8) * num_tiles + tile) * 8 + d % 8] =
+                    static_cast<int16_t>(tot);
+            else
+                xsum[sidx * kD + d] = static_cast<int16_t>(tot);
         }
+        if (tid == 0) xsc[sidx] = amax > 0.f ? amax / 127.0f : 1.0f;
     } else {
-        const Fp8Mul mulq = fp8_mul_of(amax_q), mulk = fp8_mul_of(amax_k);
+        const Fp8Mul mul = fp8_mul_of(amax);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = tid + 256 * i;
             const int tok = c >> 4, dc = c & 15;
-            if (tok < rows)
-                __builtin_nontemporal_store(codes8(xq[i], mulq),
-                                            reinterpret_cast<u32x2*>(q8 + (t0 + tok) * row_bytes + h * kD + 8 * dc));
-            // K rows past the segment end are 0
-            __builtin_nontemporal_store(codes8(xk[i], mulk), reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc));
+            if constexpr (IS_K)   // K rows past the segment end are 0
+                __builtin_nontemporal_store(codes8(xv[i], mul), reinterpret_cast<u32x2*>(kt + tok * kD + 8 * dc));
+            else if (tok < rows)
+                __builtin_nontemporal_store(codes8(xv[i], mul),
+                                            reinterpret_cast<u32x2*>(x8 + (t0 + tok) * row_bytes + h * kD + 8 * dc));
         }
-        if (tid == 0) {
-            qsc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_q);
-            ksc[static_cast<int64_t>(tile) * num_heads + h] = fp8_scale_of(amax_k);
-        }
+        if (tid == 0) xsc[sidx] = fp8_scale_of(amax);
     }
 }
 
@@ -424,12 +407,17 @@ hipError_t launch_fp8_quantize(const uint16_t* q, const uint16_t* k, const uint1
     float* vpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + tb_bytes + va_bytes);
     hipLaunchKernelGGL(tile64_scan_kernel, dim3(1), dim3(1024), 0, stream, cu, num_seqs, tb);
     const unsigned items = static_cast<unsigned>(num_tiles * num_heads);
-    if (qsum != nullptr)
-        hipLaunchKernelGGL(quant_qk_kernel<true>, dim3(items), dim3(256), 0, stream, q, k, qs, ks, cu, tb,
-                           num_seqs, num_heads, num_tiles, q8, k8, qsc, ksc, qsum, ksum);
-    else
-        hipLaunchKernelGGL(quant_qk_kernel<false>, dim3(items), dim3(256), 0, stream, q, k, qs, ks, cu, tb,
-                           num_seqs, num_heads, num_tiles, q8, k8, qsc, ksc, qsum, ksum);
+    if (qsum != nullptr) {
+        hipLaunchKernelGGL((quant_qk_kernel<true, false>), dim3(items), dim3(256), 0, stream, q, qs, cu, tb,
+                           num_seqs, num_heads, num_tiles, q8, qsc, qsum);
+        hipLaunchKernelGGL((quant_qk_kernel<true, true>), dim3(items), dim3(256), 0, stream, k, ks, cu, tb,
+                           num_seqs, num_heads, num_tiles, k8, ksc, ksum);
+    } else {
+        hipLaunchKernelGGL((quant_qk_kernel<false, false>), dim3(items), dim3(256), 0, stream, q, qs, cu, tb,
+                           num_seqs, num_heads, num_tiles, q8, qsc, nullptr);
+        hipLaunchKernelGGL((quant_qk_kernel<false, true>), dim3(items), dim3(256), 0, stream, k, ks, cu, tb,
+                           num_seqs, num_heads, num_tiles, k8, ksc, nullptr);
+    }
     hipLaunchKernelGGL(vamax_kernel, dim3(items), dim3(256), 0, stream, v, vs, cu, tb, num_seqs, num_heads,
                        vpart);
     hipLaunchKernelGGL(vscale_kernel, dim3(num_seqs, num_heads * kD / 32), dim3(1024), 0, stream,
