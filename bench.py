@@ -459,23 +459,44 @@ def main():
             flops=2.0 * n * wl.ffn * c)
 
         # The vendor library (torch.nn.functional.linear -> hipBLASLt) on the
-        # same four products, without the fused epilogues: the comparison
-        # for the fused GEMMs above (SwiGLU: the gate and up products as one
-        # [N, 2I] GEMM; the residual GEMMs: the plain product).
+        # same four products, without the fused epilogues (SwiGLU: the gate
+        # and up products as one [N, 2I] GEMM; the residual GEMMs: the plain
+        # product), and the same products followed by the epilogue in torch
+        # (the residual GEMMs: addcmul of the segment's gate row, one segment
+        # here, given to torch in bf16 so that its elementwise kernel runs in
+        # one dtype; SwiGLU: silu(gate) * up), the unfused path the fused
+        # kernels replace.
         import torch.nn.functional as F
         w_gu = torch.cat([w["w_gate"], w["w_up"]], dim=0)
+        ffn = wl.ffn
         lib_cmp = {}
-        for nm, a_in, w_in, ours in (("qkv_gemm", taps["h"], w["w_qkv"], "qkv_gemm"),
-                                     ("out_proj", taps["o"], w["w_o"], "out_proj_gated_residual"),
-                                     ("swiglu_gate_up", taps["h2"], w_gu, "swiglu_gemm"),
-                                     ("down", taps["a"], w["w_down"], "down_gated_residual")):
+        epi_out = torch.empty(n, c, dtype=torch.bfloat16, device=dev)
+        gate_o = mod[0, 2 * c:3 * c].to(torch.bfloat16)
+        gate_d = mod[0, 5 * c:6 * c].to(torch.bfloat16)
+
+        def swiglu_lib():
+            gu = F.linear(taps["h2"], w_gu)
+            return F.silu(gu[:, :ffn]) * gu[:, ffn:]
+
+        for nm, a_in, w_in, ours, with_epi in (
+                ("qkv_gemm", taps["h"], w["w_qkv"], "qkv_gemm", None),
+                ("out_proj", taps["o"], w["w_o"], "out_proj_gated_residual",
+                 lambda: torch.addcmul(x, F.linear(taps["o"], w["w_o"]), gate_o, out=epi_out)),
+                ("swiglu_gate_up", taps["h2"], w_gu, "swiglu_gemm", swiglu_lib),
+                ("down", taps["a"], w["w_down"], "down_gated_residual",
+                 lambda: torch.addcmul(taps["x1"], F.linear(taps["a"], w["w_down"]), gate_d, out=epi_out))):
             fl = 2.0 * a_in.shape[0] * a_in.shape[1] * w_in.shape[0]
             t = sampler(lambda: F.linear(a_in, w_in), it, False)
-            lib_cmp[nm] = {"library_ms": round(t["median"], 4),
-                           "library_tflops": round(fl / (t["median"] * 1e-3) / 1e12, 2),
-                           "fused_ms": stages[ours]["ms"],
-                           "fused_over_library": round(t["median"] / stages[ours]["ms"], 4)}
-        del w_gu
+            e = {"library_ms": round(t["median"], 4),
+                 "library_tflops": round(fl / (t["median"] * 1e-3) / 1e12, 2),
+                 "fused_ms": stages[ours]["ms"],
+                 "fused_over_library": round(t["median"] / stages[ours]["ms"], 4)}
+            if with_epi is not None:
+                te = sampler(with_epi, it, False)
+                e["library_with_torch_epilogue_ms"] = round(te["median"], 4)
+                e["fused_over_library_with_epilogue"] = round(te["median"] / stages[ours]["ms"], 4)
+            lib_cmp[nm] = e
+        del w_gu, epi_out, gate_o, gate_d
         stages["gemm_library_comparison"] = lib_cmp
 
     # Attention at one rank's share of an 8-way head split (3 of the 24 heads,
