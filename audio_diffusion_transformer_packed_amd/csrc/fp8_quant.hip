@@ -191,10 +191,13 @@ __device__ __forceinline__ u32x2 i8_codes8(uint4 raw, float amax, int (&s)[8]) {
     return out;
 }
 
-// One workgroup per (key tile, head), head-fastest: the codes and block
-// scale of one of Q (IS_K false: codes token-major like q, rows past the
-// segment end not written) or K (IS_K true: the 64 x 128 key tile, rows
-// past the segment end 0). I8: INT8 codes (scale amax / 127) instead of
+// One workgroup per (key tile, head): the codes and block scale of one of
+// Q (IS_K false: head-fastest, codes token-major like q, rows past the
+// segment end not written) or K (IS_K true: tile-fastest, the 64 x 128 key
+// tile, rows past the segment end 0). The K codes of one head are one
+// contiguous run of tiles, so tile-fastest workgroups write adjacent 8 KB
+// blocks (head-fastest, 7 MB apart at 57,960 tokens, measured 100 against
+// 91 us; the transposed V tiles, ordered the same way, gained nothing). I8: INT8 codes (scale amax / 127) instead of
 // e4m3, plus the tile's per-channel code sums, int16: qsum [T, H, 128] or
 // ksum [H, 16, T, 8] (channel chunk-major).
 template <bool I8, bool IS_K>
@@ -204,8 +207,14 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(
     uint8_t* __restrict__ x8, float* __restrict__ xsc, int16_t* __restrict__ xsum) {
     __shared__ float red[4];
     __shared__ int32_t isum[4][I8 ? kD : 1];
-    const int tile = static_cast<int>(blockIdx.x / static_cast<unsigned>(num_heads));
-    const int h = static_cast<int>(blockIdx.x - static_cast<unsigned>(tile) * num_heads);
+    int tile, h;
+    if constexpr (IS_K) {   // tile-fastest: consecutive workgroups write adjacent key tiles
+        h = static_cast<int>(blockIdx.x / static_cast<unsigned>(num_tiles));
+        tile = static_cast<int>(blockIdx.x - static_cast<unsigned>(h) * static_cast<unsigned>(num_tiles));
+    } else {
+        tile = static_cast<int>(blockIdx.x / static_cast<unsigned>(num_heads));
+        h = static_cast<int>(blockIdx.x - static_cast<unsigned>(tile) * num_heads);
+    }
     int seg, t0, rows;
     tile_origin(cu, tb, num_seqs, tile, seg, t0, rows);
     const int tid = threadIdx.x, wave = tid >> 6;
