@@ -340,10 +340,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
                 for (int r = 0; r < 16; ++r)
                     if (32 * b + 8 * (r >> 2) + 4 * g + (r & 3) >= keys_left) sc[b][r] = -INFINITY;
         }
+        // the tile max as a chain of NaN-propagating maxima (v_maximum3_f32,
+        // two scores per instruction): scores are finite or -inf, and fmaxf
+        // here made the compiler quiet every MFMA result first (one more
+        // instruction per score)
         float mx = sc[0][0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int r = 0; r < 16; ++r)
+            mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[0][r]), sc[1][r]);
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
         const float ct = sq * sk;          // exp2 units per raw score
         // BSA scores carry the 1.5 * 2^23 offset (exact to remove from the max)
         const float tmax = (BSA ? mx - kBsaMagic : mx) * ct;
