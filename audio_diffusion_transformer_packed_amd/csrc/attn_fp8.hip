@@ -264,8 +264,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     // operand (e4m3 1.0 = 0x38) puts every row's sum into each of the lane's
     // 16 accumulators; only element 0 is read (and rescaled)
     f32x16 lacc = f32x16{};
-    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                        0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                  0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    // opaque from here on: kept in its eight registers through the tile loop
+    // (as a known constant the compiler rebuilt it from one register with
+    // seven moves per tile)
+    asm volatile("" : "+v"(ones));
     // SKIP: this wave's skipped-tile count, kept in a vector register (a
     // scalar counter adds to the kernel's scalar register pressure, which
     // then spills inside the tile loop); the empty asm defines it per lane
@@ -383,7 +387,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 1], ct, -mb));
                 const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 2], ct, -mb));
                 const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[b][r + 3], ct, -mb));
-                int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                // the second convert overwrites the upper half: the word's
+                // previous value as the first one's "old" saves zeroing it
+                int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pf[w], false);
                 word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
                 pf[w] = word;
             }
