@@ -270,6 +270,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     // (as a known constant the compiler rebuilt it from one register with
     // seven moves per tile)
     asm volatile("" : "+v"(ones));
+    // BSA: the INT8 score accumulators start from this block (the bits of
+    // 1.5 * 2^23 in every element), opaque for the same reason (set per
+    // tile it cost eight 64-bit moves)
+    i32x16 magic;
+    if constexpr (BSA) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) magic[r] = 0x4B400000;
+        asm volatile("" : "+v"(magic));
+    }
     // SKIP: this wave's skipped-tile count, kept in a vector register (a
     // scalar counter adds to the kernel's scalar register pressure, which
     // then spills inside the tile loop); the empty asm defines it per lane
@@ -289,18 +298,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
         if (u < nsel) {
             const char* kl = smem + (u & 1) * kKT;
             if constexpr (BSA) {
-                // accumulate onto the bits of 1.5 * 2^23: |S| <= 127 * 127 * 128 < 2^22,
-                // so each result, read as fp32, is exactly 1.5 * 2^23 + S (no convert)
-                constexpr int kMagicBits = 0x4B400000;
+                // accumulate onto the bits of 1.5 * 2^23 (`magic`, the first
+                // MFMA's accumulator input): |S| <= 127 * 127 * 128 < 2^22, so
+                // each result, read as fp32, is exactly 1.5 * 2^23 + S (no convert)
                 i32x16 si[2];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) si[0][r] = si[1][r] = kMagicBits;
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
                     for (int b = 0; b < 2; ++b) {
                         const i32x8 kf = read32(kl + 4096 * b + kro[c][0], kl + 4096 * b + kro[c][1]);
-                        si[b] = mfma_i8(kf.lo, qf[c].lo, si[b]);
+                        si[b] = mfma_i8(kf.lo, qf[c].lo, c == 0 ? magic : si[b]);
                         si[b] = mfma_i8(kf.hi, qf[c].hi, si[b]);
                     }
 #pragma unroll
