@@ -359,11 +359,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[0][r]), sc[1][r]);
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+        // lanes l and l ^ 32 hold the same row: one v_permlane32_swap leaves
+        // the pair's two values in the two outputs (in either order), with no
+        // LDS round trip on the way to the exponentials
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         const float ct = sq * sk;          // exp2 units per raw score
         // BSA scores carry the 1.5 * 2^23 offset (exact to remove from the max)
         const float tmax = (BSA ? mx - kBsaMagic : mx) * ct;
-        float m_new = fmaxf(m_run, tmax);
+        float m_new = __builtin_elementwise_maximum(m_run, tmax);
         bool run_tile = true;
         if constexpr (SKIP) {
             if (u > 0) {
