@@ -231,15 +231,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(v8t + (static_cast<int64_t>(head) * num_tiles + tbs) * kVT), 0,
         ntiles * kVT, kBufferWord3);
-    // step u's tiles go to stage u & 1
-    auto dma_k = [&](int u) __attribute__((always_inline)) {
-        char* dst = smem + (u & 1) * kKT + 2048 * wg;
+    // step u's tiles go to stage u & 1, passed as a compile-time parity
+    // (par_c, an integral_constant) so that stage offsets are immediates
+    auto dma_k = [&](int u, auto par_c) __attribute__((always_inline)) {
+        constexpr int par = decltype(par_c)::value;
+        char* dst = smem + par * kKT + 2048 * wg;
         const int tile = tile_at(u);
         buf_dma16(rk, ksrc0, tile * kKT, dst);
         buf_dma16(rk, ksrc1, tile * kKT, dst + 1024);
     };
-    auto dma_v = [&](int u) __attribute__((always_inline)) {
-        char* dst = smem + 2 * kKT + (u & 1) * kVT + 2048 * wg;
+    auto dma_v = [&](int u, auto par_c) __attribute__((always_inline)) {
+        constexpr int par = decltype(par_c)::value;
+        char* dst = smem + 2 * kKT + par * kVT + 2048 * wg;
         const int tile = tile_at(u);
         buf_dma16(rv, vsrc0, tile * kVT, dst);
         buf_dma16(rv, vsrc1, tile * kVT, dst + 1024);
@@ -294,9 +297,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     // zero, so its P V adds nothing: the block has no branch around the P V
     // MFMAs (such a branch cost 3-4 % of the kernel when nothing is skipped,
     // more than the MFMAs it saves when tiles are).
-    auto mfma_qk = [&](int u) __attribute__((always_inline)) {
+    auto mfma_qk = [&](int u, auto par_c) __attribute__((always_inline)) {
+        constexpr int par = decltype(par_c)::value;   // u & 1
         if (u < nsel) {
-            const char* kl = smem + (u & 1) * kKT;
+            const char* kl = smem + par * kKT;
             if constexpr (BSA) {
                 // accumulate onto the bits of 1.5 * 2^23 (`magic`, the first
                 // MFMA's accumulator input): |S| <= 127 * 127 * 128 < 2^22, so
@@ -325,17 +329,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
             }
         }
     };
-    auto mfma_pv = [&](int u) __attribute__((always_inline)) {
-        const char* vl = smem + 2 * kKT + ((u - 1) & 1) * kVT;
+    auto mfma_pv = [&](auto par_c) __attribute__((always_inline)) {
+        constexpr int par = decltype(par_c)::value;   // u & 1; V(u-1) is in stage 1 - par
+        const char* vl = smem + 2 * kKT + (1 - par) * kVT;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
             oacc[db] = mfma_fp8(read32(vl + 2048 * db + vro[0], vl + 2048 * db + vro[1]), pf, oacc[db]);
         lacc = mfma_fp8(ones, pf, lacc);
     };
-    auto mfma_block = [&](int u) __attribute__((always_inline)) {
+    auto mfma_block = [&](int u, auto par_c) __attribute__((always_inline)) {
         if (!wave_active) return;
-        mfma_qk(u);
-        if (u >= 1) mfma_pv(u);
+        mfma_qk(u, par_c);
+        if (u >= 1) mfma_pv(par_c);
     };
     // softmax block S(u): tile max, skip rule, rescale, P of tile u
     auto softmax_block = [&](int u) __attribute__((always_inline)) {
@@ -427,32 +432,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     // barrier 2u+2: their stages held K(u), V(u-1), which M(u) of both
     // groups has read. They are next read in M(u+2), from half-tile 2u+4 on;
     // the group waits for its DMA at the end of its M(u+1), before barrier 2u+4.
-    auto issue_dma = [&](int u) __attribute__((always_inline)) {
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    auto issue_dma = [&](int u, auto par_c) __attribute__((always_inline)) {
+        constexpr int par = decltype(par_c)::value;
         if (!g0) {
-            if (u + 2 < nsel) dma_k(u + 2);
-            if (u + 1 < nsel) dma_v(u + 1);
+            if (u + 2 < nsel) dma_k(u + 2, par_c);
+            if (u + 1 < nsel) dma_v(u + 1, std::integral_constant<int, 1 - par>{});
         }
     };
     if (!g0) {
-        if (1 < nsel) dma_k(1);
-        dma_v(0);
+        if (1 < nsel) dma_k(1, Odd{});
+        dma_v(0, Even{});
         bar();
     }
-    mfma_block(0);
-    dma_wait();
-    bar();
-    issue_dma(0);
-    softmax_block(0);
-    bar();
-    for (int u = 1; u < nsel; ++u) {
-        mfma_block(u);
+    auto step = [&](int u, auto par_c) __attribute__((always_inline)) {
+        mfma_block(u, par_c);
         dma_wait();
         bar();
-        issue_dma(u);
+        issue_dma(u, par_c);
         softmax_block(u);
         bar();
+    };
+    step(0, Even{});
+    // two tiles per iteration, odd then even, so every stage is a constant
+    int u = 1;
+    for (; u + 1 < nsel; u += 2) {
+        step(u, Odd{});
+        step(u + 1, Even{});
     }
-    mfma_block(nsel);
+    if (u < nsel) step(u++, Odd{});
+    // the last P V (u == nsel): V(nsel - 1) is in stage 1 - (nsel & 1)
+    if (u & 1) mfma_block(u, Odd{});
+    else mfma_block(u, Even{});
     if (g0) bar();
 
     // ---- O = acc s_v / l; lane holds channels 32 db + 8 r4 + 4 g + [0, 4) ----
