@@ -119,6 +119,10 @@ size_t bookkeeping_scratch_bytes(int num_seqs) {
     return (b + 255) & ~static_cast<size_t>(255);
 }
 
+const int32_t* bookkeeping_rank_prefix(const void* scratch, int num_seqs) {
+    return static_cast<const int32_t*>(scratch) + num_seqs;
+}
+
 hipError_t launch_bookkeeping(const int32_t* cu, int num_seqs, int total_tokens, int num_heads,
                               int block_m, int32_t* seg_id, int32_t* tile_cu, int32_t* items,
                               int64_t items_capacity, void* scratch, hipStream_t stream) {

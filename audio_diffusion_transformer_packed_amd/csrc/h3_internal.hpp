@@ -11,6 +11,10 @@ namespace h3 {
 
 // Varlen bookkeeping (bookkeeping.hip)
 size_t bookkeeping_scratch_bytes(int num_seqs);
+// The schedule's per-segment query-tile prefix in work-list order (segments
+// by descending length), num_seqs + 1 entries, inside that scratch; valid
+// on the stream once launch_bookkeeping has written the list.
+const int32_t* bookkeeping_rank_prefix(const void* scratch, int num_seqs);
 hipError_t launch_bookkeeping(const int32_t* cu, int num_seqs, int total_tokens, int num_heads,
                               int block_m, int32_t* seg_id, int32_t* tile_cu, int32_t* items,
                               int64_t items_capacity, void* scratch, hipStream_t stream);
@@ -20,7 +24,7 @@ hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t
                             uint16_t* o, int64_t qs, int64_t ks, int64_t vs, int64_t os,
                             const int32_t* cu, const int32_t* items, int64_t num_items,
                             int num_seqs, int total_tokens, int num_heads, int head_dim,
-                            float softmax_scale, hipStream_t stream);
+                            float softmax_scale, const int32_t* rank_prefix, hipStream_t stream);
 
 // fp8 quantisation (fp8_quant.hip): Q/K block codes, V channel codes, scales
 size_t fp8_tiles_upper_bound(int num_seqs, int total_tokens);

@@ -152,7 +152,8 @@ h3_status run_attention(const void* q, const void* k, const void* v, void* out, 
     e = h3::launch_attn_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                              static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), qs, ks,
                              vs, os, cu_dev, items, n_items, num_seqs, total_tokens, num_heads,
-                             head_dim, scale, stream);
+                             head_dim, scale, h3::bookkeeping_rank_prefix(bk_scratch, num_seqs),
+                             stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     return ok();
 }

@@ -89,6 +89,19 @@ def test_attention_ragged_segments(dev, ops, head_dim):
     compare(to_np(out), ref, f"attn ragged D={head_dim}")
 
 
+@pytest.mark.parametrize("heads,head_dim", [(8, 64), (16, 128)])
+def test_attention_ragged_segments_heads_multiple_of_8(dev, ops, heads, head_dim):
+    """With a head count divisible by 8 the kernel hands each XCD the items
+    of every eighth head; ragged and empty segments in several sizes."""
+    lens = [1, 300, 0, 65, 1000, 64, 257, 0, 2, 513]
+    announce(f"attention ragged heads={heads} D={head_dim} lens={lens}")
+    cu = _cu(lens)
+    inp = h3synth.attention_inputs(cu, np.zeros((cu[-1], 3), np.int32), heads, head_dim, seed=78)
+    out = _run_attn(ops, dev, inp, heads, head_dim)
+    ref = oracle.attn_varlen_ref(inp.q.f32, inp.k.f32, inp.v.f32, cu)
+    compare(to_np(out), ref, f"attn ragged heads={heads} D={head_dim}")
+
+
 def test_attention_length_one_returns_v(dev, ops):
     announce("attention length-1 segments")
     cu = _cu([1, 1, 1, 3, 1])
