@@ -124,15 +124,27 @@ __global__ __launch_bounds__(64 * kAdalnWaves) void adaln_kernel(
             float am = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(o[e]));
-            am = fmaxf(am, __shfl_xor(am, 1, 64));
-            am = fmaxf(am, __shfl_xor(am, 2, 64));
+            // the block's 4 lanes form a DPP quad: swap within pairs, then
+            // halves (quad_perm [1,0,3,2] and [2,3,0,1]; no LDS permute)
+            am = fmaxf(am, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                               __builtin_bit_cast(int, am), 0xB1, 0xF, 0xF, true)));
+            am = fmaxf(am, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                               __builtin_bit_cast(int, am), 0x4E, 0xF, 0xF, true)));
             const uint32_t sb = mx_scale_byte(am);
             const float inv = mx_inv_scale(sb);
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] *= inv;
             const int ch = i * 64 + lane;
             *reinterpret_cast<uint2*>(static_cast<uint8_t*>(hout) + t * hidden + ch * 8) = mx_codes8(o);
-            if ((lane & 3) == 0) hsc[mx_scale_offset(t, ch >> 2, total_tokens)] = static_cast<uint8_t>(sb);
+            // the four blocks of a 128-element K step are the quads of a
+            // 16-lane row: each quad's byte moved to its place in the step's
+            // scale dword, the row OR-combined with two DPP rotations (by 4
+            // and 8 lanes), one dword store per row of lanes
+            uint32_t sw = sb << (8 * ((lane >> 2) & 3));
+            sw |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(sw), 0x124, 0xF, 0xF, false));
+            sw |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(sw), 0x128, 0xF, 0xF, false));
+            if ((lane & 15) == 0)
+                *reinterpret_cast<uint32_t*>(hsc + mx_scale_offset(t, ch >> 2, total_tokens)) = sw;
         } else {
             Chunk16 out;
 #pragma unroll
