@@ -32,7 +32,9 @@ def _inputs(lens, heads, d, seed):
 
 
 @pytest.mark.parametrize("precision,cases", [
-    ("bf16", [([900, 0, 517], 4, 128), ([300, 65], 2, 64)]),
+    # 8 heads: work items dealt to the XCDs by head, located through the
+    # schedule's tile prefix, which lives in the scratch / workspace
+    ("bf16", [([900, 0, 517], 8, 128), ([300, 65], 2, 64)]),
     ("fp8", [([700, 129, 1], 3, 128), ([200], 2, 128)]),
 ])
 def test_noalloc_equals_workspace_entry_point(dev, ops, precision, cases):
