@@ -9,8 +9,9 @@
 // pass (fp8_quant.hip):
 //   S = (Q8 K8^T) s_q s_k * scale, online softmax over 64-key tiles in
 //   ascending order with the exact running row max m,
-//   P8 = e4m3(448 p), p = exp(S - m), l = the row sum of P8 (one more P V
-//   MFMA against an all-ones operand, in place of 32 fp32 adds per tile),
+//   P8 = e4m3(448 p), p = exp(S - m), l = the row sum of P8 (one
+//   16x16x128 MFMA per tile against a 0/1 operand, in place of 32 fp32
+//   adds),
 //   O = (sum P8 V8) s_v / (448 l).
 // Skip rule: for the 32 query rows of a wave, a key tile other than the
 // segment's first is skipped (no exp, no P V contribution) when every
@@ -62,6 +63,9 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_fp8_16(i32x8 a, i32x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // Buffer resource word 3 for raw (untyped, stride 0) access on gfx9-family
@@ -263,14 +267,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) oacc[b] = f32x16{};
     float m_run = -1e30f;     // running row max, exp2 units (finite start: no inf - inf)
-    // row sums of P8 = e4m3(448 p): one more P V MFMA with an all-ones A
-    // operand (e4m3 1.0 = 0x38) puts every row's sum into each of the lane's
-    // 16 accumulators; only element 0 is read (and rescaled)
-    f32x16 lacc = f32x16{};
-    i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                  0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    // row sums of P8 = e4m3(448 p): one v_mfma_f32_16x16x128_f8f6f4 per
+    // tile with P (as held for the P V MFMA) as its B operand. Read that way
+    // lane l supplies query l % 32 as column l % 16 of k-group l / 16, so an
+    // A operand of e4m3 ones (0x38) where the k-group's parity equals the
+    // row's parity, zeros elsewhere, makes even output rows the sums of query
+    // l % 16 and odd rows those of query l % 16 + 16: lacc[0] and lacc[1]
+    // (read and rescaled; [2] and [3] repeat them). Half the matrix-core
+    // cycles of a 32x32x64 MFMA against an all-ones operand.
+    f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int pat = ((lane >> 4) & 1) == (lane & 1) ? 0x38383838 : 0;
+    i32x8 ones = {pat, pat, pat, pat, pat, pat, pat, pat};
     // opaque from here on: kept in its eight registers through the tile loop
-    // (as a known constant the compiler rebuilt it from one register with
+    // (as a known value the compiler rebuilt it from one register with
     // seven moves per tile)
     asm volatile("" : "+v"(ones));
     // BSA: the INT8 score accumulators start from this block (the bits of
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
 #pragma unroll
         for (int db = 0; db < 4; ++db)
             oacc[db] = mfma_fp8(read32(vl + 2048 * db + vro[0], vl + 2048 * db + vro[1]), pf, oacc[db]);
-        lacc = mfma_fp8(ones, pf, lacc);
+        lacc = mfma_fp8_16(ones, pf, lacc);
     };
     auto mfma_block = [&](int u, auto par_c) __attribute__((always_inline)) {
         if (!wave_active) return;
@@ -385,7 +394,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
         }
         if (__any(m_new > m_run)) {                   // wave-uniform
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            lacc[0] *= alpha;
+            lacc[0] *= __shfl(alpha, lane & 15, 64);
+            lacc[1] *= __shfl(alpha, (lane & 15) + 16, 64);
 #pragma unroll
             for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
         }
@@ -468,7 +478,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     if (g0) bar();
 
     // ---- O = acc s_v / l; lane holds channels 32 db + 8 r4 + 4 g + [0, 4) ----
-    const float inv = 1.f / lacc[0];
+    const float la = __shfl(lacc[0], lane & 15, 64), lb = __shfl(lacc[1], lane & 15, 64);
+    const float inv = 1.f / (l32 < 16 ? la : lb);
     if (qvalid) {
         uint16_t* op = o + static_cast<int64_t>(q0 + qrow_local) * os + static_cast<int64_t>(head) * kD;
         const float* svp = vsc + (static_cast<int64_t>(seg) * num_heads + head) * kD;
