@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const int32_t* __restrict__ tb, const int4* __restrict__ items, int num_seqs,
     int total_tokens, int num_heads, int64_t num_tiles, float scale_log2,
     float thr_log2, int32_t* __restrict__ skip_counts, const int32_t* __restrict__ lists,
-    int64_t list_stride, int sp_permille) {
+    int64_t list_stride, int sp_permille, const int32_t* __restrict__ rank_prefix) {
     // K stage 0, K stage 1, V stage 0, V stage 1
     __shared__ __attribute__((aligned(1024))) char smem[2 * kKT + 2 * kVT];
     __shared__ int32_t wskip[kWaves];
@@ -133,7 +133,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     // XCD still samples the whole (longest segment first) list. Ids past the
     // last whole round of 8 x 16 map to themselves. Measured at 57,960 tokens:
     // 3.7 % faster on frame-local input, 0.9 % on i.i.d. input.
-    unsigned item = blockIdx.x;
+    // dense: items go to the XCDs by head (xcd_item), as in the bf16 kernel
+    unsigned item = BSA ? blockIdx.x
+                        : static_cast<unsigned>(xcd_item(blockIdx.x, rank_prefix, num_seqs, num_heads));
     if constexpr (BSA) {
         constexpr unsigned kChunk = 16;
         const unsigned full = gridDim.x / (8 * kChunk) * (8 * kChunk);
@@ -592,7 +594,8 @@ hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t*
     hipLaunchKernelGGL((attn_fp8_kernel<true, false>), dim3(static_cast<unsigned>(num_items)),
                        dim3(kThreads), 0, stream, q8, k8, v8t, qsc, ksc, vsc, o, os, cu, tb,
                        reinterpret_cast<const int4*>(items), num_seqs, total_tokens, num_heads,
-                       tiles, softmax_scale * kLog2e, 0.f, nullptr, lists, list_stride, sp_permille);
+                       tiles, softmax_scale * kLog2e, 0.f, nullptr, lists, list_stride, sp_permille,
+                       static_cast<const int32_t*>(nullptr));
     return hipGetLastError();
 }
 
@@ -606,7 +609,8 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* cu_host, const int32_t* items, int64_t num_items,
                            int num_seqs, int total_tokens, int num_heads, int head_dim,
                            float softmax_scale, int skip, float skip_threshold,
-                           int32_t* skip_counts, void* scratch, hipStream_t stream) {
+                           int32_t* skip_counts, void* scratch, const int32_t* rank_prefix,
+                           hipStream_t stream) {
     if (head_dim != kD) return hipErrorInvalidValue;
     if (num_items <= 0 || num_seqs <= 0) return hipSuccess;
     int64_t tiles = 0;
@@ -629,12 +633,12 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t*
         hipLaunchKernelGGL((attn_fp8_kernel<false, true>), grid, dim3(kThreads), 0, stream, q8, k8,
                            v8t, qsc, ksc, vsc, o, os, cu, tb, reinterpret_cast<const int4*>(items),
                            num_seqs, total_tokens, num_heads, tiles, softmax_scale * kLog2e,
-                           skip_threshold * kLog2e, skip_counts, nullptr, int64_t{0}, 0);
+                           skip_threshold * kLog2e, skip_counts, nullptr, int64_t{0}, 0, rank_prefix);
     } else {
         hipLaunchKernelGGL((attn_fp8_kernel<false, false>), grid, dim3(kThreads), 0, stream, q8, k8,
                            v8t, qsc, ksc, vsc, o, os, cu, tb, reinterpret_cast<const int4*>(items),
                            num_seqs, total_tokens, num_heads, tiles, softmax_scale * kLog2e,
-                           skip_threshold * kLog2e, skip_counts, nullptr, int64_t{0}, 0);
+                           skip_threshold * kLog2e, skip_counts, nullptr, int64_t{0}, 0, rank_prefix);
     }
     return hipGetLastError();
 }

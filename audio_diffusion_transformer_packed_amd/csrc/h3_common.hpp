@@ -75,6 +75,37 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Work list index of workgroup b. Workgroup ids are dealt round-robin over
+// the 8 XCDs (b runs on XCD b % 8), each with its own L2. With a list in
+// (segment, head, query tile) order, consecutive ids would put the items of
+// one head on all eight XCDs at once, and each XCD's L2 would fetch that
+// head's K and V. When num_heads % 8 == 0 (and rank_prefix, the schedule's
+// per-segment tile prefix in list order, is given) XCD x instead takes the
+// items of heads x, x + 8, ... in list order, its (b / 8)-th such item being
+// workgroup b's: the workgroups an XCD runs at one time then stream one
+// head's K and V through its L2 together, and every segment's work still
+// splits evenly over the XCDs. Otherwise the list order is kept. (Used by
+// the dense attention kernels.)
+__device__ __forceinline__ int64_t xcd_item(unsigned b, const int32_t* __restrict__ rank_prefix,
+                                            int num_seqs, int num_heads) {
+    if (rank_prefix == nullptr || (num_heads & 7) != 0) return b;
+    const int x = static_cast<int>(b & 7);
+    const int64_t kk = b >> 3;
+    const int hpx = num_heads >> 3;
+    // segment rank r: the largest with rank_prefix[r] * hpx <= kk
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(rank_prefix[mid])) * hpx <= kk) lo = mid;
+        else hi = mid - 1;
+    }
+    const int p0 = __builtin_amdgcn_readfirstlane(rank_prefix[lo]);
+    const int tiles = __builtin_amdgcn_readfirstlane(rank_prefix[lo + 1]) - p0;
+    const int64_t j = kk - static_cast<int64_t>(p0) * hpx;
+    const int64_t h = 8 * (j / tiles) + x;
+    return static_cast<int64_t>(p0) * num_heads + h * tiles + j % tiles;
+}
+
 // Segment of token t: largest s with cu[s] <= t (cu non-decreasing, cu[0] = 0).
 __device__ __forceinline__ int find_segment(const int32_t* __restrict__ cu, int num_seqs,
                                             int64_t t) {

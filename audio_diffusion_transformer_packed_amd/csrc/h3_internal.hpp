@@ -42,7 +42,8 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* cu, const int32_t* cu_host, const int32_t* items,
                            int64_t num_items, int num_seqs, int total_tokens, int num_heads,
                            int head_dim, float softmax_scale, int skip, float skip_threshold,
-                           int32_t* skip_counts, void* scratch, hipStream_t stream);
+                           int32_t* skip_counts, void* scratch, const int32_t* rank_prefix,
+                           hipStream_t stream);
 
 // Block-sparse attention, INT8 Q/K + FP8 V (bsa_select.hip, attn_fp8.hip).
 // Lists: int32 [H, T, list_stride], row (head, first 64-token block of a

@@ -145,7 +145,8 @@ h3_status run_attention(const void* q, const void* k, const void* v, void* out, 
                                 static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), qs,
                                 ks, vs, os, cu_dev, cu_host, items, n_items, num_seqs,
                                 total_tokens, num_heads, head_dim, scale, opts->skip_softmax,
-                                thr, opts->skip_counts, fp8_scratch, stream);
+                                thr, opts->skip_counts, fp8_scratch,
+                                h3::bookkeeping_rank_prefix(bk_scratch, num_seqs), stream);
         if (e != hipSuccess) return hip_fail(e, "fp8 attention launch");
         return ok();
     }
