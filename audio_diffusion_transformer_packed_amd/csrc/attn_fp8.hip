@@ -126,17 +126,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
     const int tid = threadIdx.x;
     // work-item fields and segment bounds are workgroup-uniform: keep them in
     // scalar registers (so the tile buffer descriptors are scalar too)
-    // BSA: work items go to the XCDs (workgroup ids are dealt round-robin
-    // over the 8) in chunks of 16 consecutive items, XCD x taking chunks x,
-    // x + 8, ...: the items an XCD runs at one time are neighbouring query
-    // blocks of a head, whose kept key blocks overlap in its L2, while every
-    // XCD still samples the whole (longest segment first) list. Ids past the
-    // last whole round of 8 x 16 map to themselves. Measured at 57,960 tokens:
-    // 3.7 % faster on frame-local input, 0.9 % on i.i.d. input.
-    // dense: items go to the XCDs by head (xcd_item), as in the bf16 kernel
-    unsigned item = BSA ? blockIdx.x
-                        : static_cast<unsigned>(xcd_item(blockIdx.x, rank_prefix, num_seqs, num_heads));
-    if constexpr (BSA) {
+    // Work items go to the XCDs by head (xcd_item, as in the bf16 kernel):
+    // the items an XCD runs at one time are neighbouring query blocks of one
+    // head, whose K/V (and, block-sparse, whose overlapping kept key blocks)
+    // stream through its L2 together. Where that mapping does not apply (head
+    // count not a multiple of 8) the block-sparse pass deals chunks of 16
+    // consecutive items instead, XCD x taking chunks x, x + 8, ... (ids past
+    // the last whole round of 8 x 16 map to themselves). At 57,960 tokens x
+    // 24 heads the chunks were 3.7 % faster than list order on frame-local
+    // input (0.9 % on i.i.d.), the per-head mapping 1.3 % faster again.
+    unsigned item = static_cast<unsigned>(xcd_item(blockIdx.x, rank_prefix, num_seqs, num_heads));
+    if (BSA && (rank_prefix == nullptr || (num_heads & 7) != 0)) {
         constexpr unsigned kChunk = 16;
         const unsigned full = gridDim.x / (8 * kChunk) * (8 * kChunk);
         if (blockIdx.x < full) {
@@ -563,7 +563,7 @@ hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* cu_host, const int32_t* items, int64_t num_items,
                            int num_seqs, int total_tokens, int num_heads, float softmax_scale,
                            int sp_permille, int64_t list_stride, int32_t* lists_out, void* scratch,
-                           hipStream_t stream) {
+                           const int32_t* rank_prefix, hipStream_t stream) {
     if (num_items <= 0 || num_seqs <= 0) return hipSuccess;
     int64_t tiles = 0;
     int max_blocks = 0;
@@ -595,7 +595,7 @@ hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t*
                        dim3(kThreads), 0, stream, q8, k8, v8t, qsc, ksc, vsc, o, os, cu, tb,
                        reinterpret_cast<const int4*>(items), num_seqs, total_tokens, num_heads,
                        tiles, softmax_scale * kLog2e, 0.f, nullptr, lists, list_stride, sp_permille,
-                       static_cast<const int32_t*>(nullptr));
+                       rank_prefix);
     return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ hipError_t launch_attn_bsa(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int32_t* cu_host, const int32_t* items, int64_t num_items,
                            int num_seqs, int total_tokens, int num_heads, float softmax_scale,
                            int sp_permille, int64_t list_stride, int32_t* lists_out, void* scratch,
-                           hipStream_t stream);
+                           const int32_t* rank_prefix, hipStream_t stream);
 
 // Q/K RMSNorm + 3D RoPE (qk_norm_rope.hip)
 hipError_t launch_qk_norm_rope(uint16_t* q, uint16_t* k, int64_t qs, int64_t ks,

@@ -474,7 +474,8 @@ h3_status run_attention_bsa(const void* q, const void* k, const void* v, void* o
                             static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), qs, ks, vs, os,
                             cu_dev, cu_host, items, n_items, num_seqs, total_tokens, num_heads, scale,
                             permille, bsa_list_stride(cu_host, num_seqs, permille), lists,
-                            ws + plan.total, stream);
+                            ws + plan.total, h3::bookkeeping_rank_prefix(ws + plan.items_bytes, num_seqs),
+                            stream);
     if (e != hipSuccess) return hip_fail(e, "block-sparse attention launch");
     return ok();
 }
