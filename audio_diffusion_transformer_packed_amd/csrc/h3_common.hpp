@@ -101,9 +101,11 @@ __device__ __forceinline__ int64_t xcd_item(unsigned b, const int32_t* __restric
     }
     const int p0 = __builtin_amdgcn_readfirstlane(rank_prefix[lo]);
     const int tiles = __builtin_amdgcn_readfirstlane(rank_prefix[lo + 1]) - p0;
-    const int64_t j = kk - static_cast<int64_t>(p0) * hpx;
-    const int64_t h = 8 * (j / tiles) + x;
-    return static_cast<int64_t>(p0) * num_heads + h * tiles + j % tiles;
+    // j < 2^29 (b is a 32-bit workgroup id): 32-bit division
+    const unsigned j = static_cast<unsigned>(kk - static_cast<int64_t>(p0) * hpx);
+    const unsigned hq = j / static_cast<unsigned>(tiles);
+    const int64_t h = 8 * static_cast<int64_t>(hq) + x;
+    return static_cast<int64_t>(p0) * num_heads + h * tiles + (j - hq * static_cast<unsigned>(tiles));
 }
 
 // Segment of token t: largest s with cu[s] <= t (cu non-decreasing, cu[0] = 0).
