@@ -396,8 +396,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(
         }
         if (__any(m_new > m_run)) {                   // wave-uniform
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            lacc[0] *= __shfl(alpha, lane & 15, 64);
-            lacc[1] *= __shfl(alpha, (lane & 15) + 16, 64);
+            // lacc[0] / lacc[1] of lane l hold queries l % 16 and l % 16 + 16,
+            // whose factors sit in lanes l & ~16 and l | 16: one
+            // v_permlane16_swap of alpha with itself yields both (no LDS)
+            const auto af = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
+            lacc[0] *= __uint_as_float(af[0]);
+            lacc[1] *= __uint_as_float(af[1]);
 #pragma unroll
             for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
         }
